@@ -1,0 +1,258 @@
+"""Plain fp64 CPU oracle of video sparse attention (VSA).
+
+TEST INFRASTRUCTURE ONLY.  Nothing on the product path imports, calls or
+links this file: only tests/, the smoke check in __graft_entry__.py and the
+CPU-baseline leg of bench.py use it.  It shares no code, header, table or
+helper with the HIP library; both sides only share the seeded input
+generator (synth/), which holds none of the method's arithmetic.
+
+What VSA computes, and where the pages state it
+------------------------------------------------
+* VSA is a dynamic sparse attention that finds the important tokens itself
+  and drops in for FlashAttention during training (FastWan/VSA re-post on
+  yumynutrition.com, section "传统零散郑重力，为何会在蒸馏中失效？"; the
+  neican.ai commentary "超越Sora：FastWan如何以“稀疏蒸馏”重塑实时AI视频生成范式",
+  section "技术原理与创新点解析").  So the fine stage is exact softmax
+  attention, scaled by 1/sqrt(d) as the attention it replaces.
+* It has a coarse stage whose output is a block-sparse attention pattern,
+  and a fine block-sparse kernel working on 64x64 blocks (yumynutrition
+  re-post, results section "一张卡，秒生视频": the fine-kernel speed line,
+  the coarse-stage overhead line, the FlexAttention 64x64-block-mask line
+  and Fig. 5).
+* At 87.5% sparsity attention FLOPs drop 8x (same results section, the
+  410M scaling experiment), i.e. sparsity = 1 - K/C over C key blocks.
+
+Readings where the pages are silent (each listed in the design doc):
+* a 64-token block of a video token grid is a 4x4x4 cube; cubes are taken in
+  raster order of the cube grid and slots inside a cube in raster order of
+  (t, y, x); each axis is padded at its high end to a multiple of 4, pad
+  slots are zero and are never attended to;
+* the coarse stage mean-pools q, k, v over the valid slots of each cube,
+  scores every query cube against every key cube with Qc Kc^T / sqrt(d),
+  softmaxes each row over all cubes (O_coarse = Pc Vc), and keeps for each
+  query cube the K key cubes with the largest score, ties to the lower cube
+  index, listed in ascending cube order;
+* O_coarse is returned per token: token r gets the row of its own cube;
+* the backward treats the selection as constant; gradients reach q, k, v
+  through the fine stage and through the coarse stage (the mean-pool spreads
+  a cube's gradient evenly over its valid tokens).
+
+Everything is float64 NumPy.  Loops run over (batch, head, query cube); each
+iteration is a small dense problem written as its definition.
+"""
+from __future__ import annotations
+
+import math
+from typing import Dict, Iterable, Optional, Sequence
+
+import numpy as np
+
+CUBE = 4          # cube edge (tokens per axis)
+SLOTS = 64        # tokens per cube
+
+
+# ----------------------------------------------------------------------------
+# cube geometry and the raster <-> cube permutation
+# ----------------------------------------------------------------------------
+
+def geometry(T: int, Hh: int, Ww: int) -> Dict[str, np.ndarray]:
+    """Cube grid of a (T, Hh, Ww) token grid.
+
+    token[p] is the raster index (t*Hh + y)*Ww + x of the token held by
+    cube-order position p = 64*c + (it*16 + ih*4 + iw), where cube
+    c = (ct*Ch + ch)*Cw + cw holds token (4ct+it, 4ch+ih, 4cw+iw); token[p] is
+    -1 for a pad slot (outside the real grid).  n_valid[c] counts real slots.
+    """
+    Ct, Ch, Cw = -(-T // CUBE), -(-Hh // CUBE), -(-Ww // CUBE)
+    C = Ct * Ch * Cw
+    token = np.full(C * SLOTS, -1, dtype=np.int64)
+    cube_of_token = np.empty(T * Hh * Ww, dtype=np.int64)
+    for ct in range(Ct):
+        for ch in range(Ch):
+            for cw in range(Cw):
+                c = (ct * Ch + ch) * Cw + cw
+                for it in range(CUBE):
+                    for ih in range(CUBE):
+                        for iw in range(CUBE):
+                            t, y, x = CUBE * ct + it, CUBE * ch + ih, CUBE * cw + iw
+                            if t < T and y < Hh and x < Ww:
+                                r = (t * Hh + y) * Ww + x
+                                token[SLOTS * c + it * 16 + ih * 4 + iw] = r
+                                cube_of_token[r] = c
+    valid = token >= 0
+    n_valid = valid.reshape(C, SLOTS).sum(axis=1)
+    return {"T": T, "Hh": Hh, "Ww": Ww, "Ct": Ct, "Ch": Ch, "Cw": Cw, "C": C,
+            "Np": C * SLOTS, "N": T * Hh * Ww, "token": token, "valid": valid,
+            "n_valid": n_valid, "cube_of_token": cube_of_token}
+
+
+def reorder(x: np.ndarray, g) -> np.ndarray:
+    """Raster (..., N, d) -> cube order (..., Np, d); pad slots are zero."""
+    out = np.zeros(x.shape[:-2] + (g["Np"], x.shape[-1]), dtype=np.float64)
+    out[..., g["valid"], :] = x[..., g["token"][g["valid"]], :]
+    return out
+
+
+def inverse_reorder(xc: np.ndarray, g) -> np.ndarray:
+    """Cube order (..., Np, d) -> raster (..., N, d); pad slots are dropped."""
+    out = np.empty(xc.shape[:-2] + (g["N"], xc.shape[-1]), dtype=np.float64)
+    out[..., g["token"][g["valid"]], :] = xc[..., g["valid"], :]
+    return out
+
+
+# ----------------------------------------------------------------------------
+# coarse stage
+# ----------------------------------------------------------------------------
+
+def pool(xc: np.ndarray, g) -> np.ndarray:
+    """Mean over the valid slots of each cube: (..., Np, d) -> (..., C, d)."""
+    C = g["C"]
+    blocks = xc.reshape(xc.shape[:-2] + (C, SLOTS, xc.shape[-1]))
+    mask = g["valid"].reshape(C, SLOTS, 1)
+    return (blocks * mask).sum(axis=-2) / g["n_valid"][:, None]
+
+
+def softmax_rows(s: np.ndarray) -> np.ndarray:
+    m = s.max(axis=-1, keepdims=True)
+    e = np.exp(s - m)
+    return e / e.sum(axis=-1, keepdims=True)
+
+
+def coarse(qc: np.ndarray, kc: np.ndarray, vc: np.ndarray):
+    """Cube-level attention: Sc = Qc Kc^T / sqrt(d), Pc = softmax(Sc), Oc = Pc Vc."""
+    d = qc.shape[-1]
+    sc = qc @ np.swapaxes(kc, -1, -2) / math.sqrt(d)
+    pc = softmax_rows(sc)
+    return sc, pc, pc @ vc
+
+
+def topk(sc: np.ndarray, K: int) -> np.ndarray:
+    """Per row, the K key cubes with the largest score, ties to the lower index,
+    returned in ascending cube order (int32)."""
+    lead = sc.shape[:-1]
+    rows = sc.reshape(-1, sc.shape[-1])
+    out = np.empty((rows.shape[0], K), dtype=np.int32)
+    for i, row in enumerate(rows):
+        # a stable sort on the negated score keeps equal scores in index order
+        order = np.argsort(-row, kind="stable")
+        out[i] = np.sort(order[:K])
+    return out.reshape(lead + (K,))
+
+
+# ----------------------------------------------------------------------------
+# fine stage
+# ----------------------------------------------------------------------------
+
+def _key_positions(sel: Sequence[int], g) -> np.ndarray:
+    """Cube-order positions of the valid slots of the selected cubes."""
+    pos = np.concatenate([np.arange(SLOTS * j, SLOTS * j + SLOTS) for j in sel])
+    return pos[g["valid"][pos]]
+
+
+def fine(qc: np.ndarray, kc: np.ndarray, vc: np.ndarray, idx: np.ndarray, g,
+         qcubes: Optional[Iterable[int]] = None):
+    """Exact softmax attention of each query cube over its selected key cubes.
+
+    qc/kc/vc are cube-order (B, H, Np, d); idx is (B, H, C, K).  Returns
+    o (B, H, Np, d) and lse (B, H, Np) (natural log of the softmax
+    denominator).  Rows that are pad slots, or cubes not in qcubes, are NaN.
+    """
+    B, H, Np, d = qc.shape
+    scale = 1.0 / math.sqrt(d)
+    o = np.full((B, H, Np, d), np.nan)
+    lse = np.full((B, H, Np), np.nan)
+    cubes = range(g["C"]) if qcubes is None else qcubes
+    for b in range(B):
+        for h in range(H):
+            for i in cubes:
+                rows = np.arange(SLOTS * i, SLOTS * i + SLOTS)
+                rows = rows[g["valid"][rows]]
+                keys = _key_positions(idx[b, h, i], g)
+                s = qc[b, h, rows] @ kc[b, h, keys].T * scale
+                m = s.max(axis=1, keepdims=True)
+                e = np.exp(s - m)
+                den = e.sum(axis=1, keepdims=True)
+                o[b, h, rows] = (e / den) @ vc[b, h, keys]
+                lse[b, h, rows] = (m + np.log(den))[:, 0]
+    return o, lse
+
+
+# ----------------------------------------------------------------------------
+# whole forward / backward
+# ----------------------------------------------------------------------------
+
+def forward(q, k, v, T: int, Hh: int, Ww: int, K: int,
+            qcubes: Optional[Iterable[int]] = None, idx: Optional[np.ndarray] = None):
+    """VSA forward on raster q, k, v (B, H, N, d).
+
+    Returns O_fine and O_coarse in raster order (B, H, N, d), the block index
+    list idx (B, H, C, K), the coarse scores Sc and softmax Pc (B, H, C, C),
+    the per-cube coarse output Oc (B, H, C, d) and the fine LSE in cube order.
+    A given idx replaces the coarse selection (to check the fine stage on a
+    mask chosen elsewhere).
+    """
+    g = geometry(T, Hh, Ww)
+    q, k, v = (np.asarray(a, dtype=np.float64) for a in (q, k, v))
+    qcb, kcb, vcb = reorder(q, g), reorder(k, g), reorder(v, g)
+    qp, kp, vp = pool(qcb, g), pool(kcb, g), pool(vcb, g)
+    sc, pc, oc = coarse(qp, kp, vp)
+    if idx is None:
+        idx = topk(sc, K)
+    o_cube, lse = fine(qcb, kcb, vcb, idx, g, qcubes)
+    return {
+        "o_fine": inverse_reorder(o_cube, g),
+        "o_coarse": oc[..., g["cube_of_token"], :],
+        "idx": idx, "scores": sc, "pc": pc, "oc": oc,
+        "o_fine_cube": o_cube, "lse_cube": lse, "geometry": g,
+    }
+
+
+def backward(q, k, v, do_fine, do_coarse, T: int, Hh: int, Ww: int, idx: np.ndarray):
+    """Gradients of sum(O_fine*do_fine) + sum(O_coarse*do_coarse) w.r.t. raster q, k, v.
+
+    The selection idx is held constant.  Fine stage, per query cube with
+    P = softmax(S), S = Q K_sel^T / sqrt(d):
+        dV_sel += P^T dO,  dP = dO V_sel^T,  dS = P * (dP - rowsum(P * dP)),
+        dQ = dS K_sel / sqrt(d),  dK_sel += dS^T Q / sqrt(d).
+    Coarse stage, with O_coarse[r] = Oc[cube(r)]:
+        dOc[c] = sum of do_coarse over the valid tokens of cube c,
+        dVc = Pc^T dOc,  dPc = dOc Vc^T,  dSc = Pc * (dPc - rowsum(Pc * dPc)),
+        dQc = dSc Kc / sqrt(d),  dKc = dSc^T Qc / sqrt(d),
+    and each valid token of cube c receives dQc[c] / n_c (same for k, v).
+    """
+    g = geometry(T, Hh, Ww)
+    q, k, v, dof, doc = (np.asarray(a, dtype=np.float64) for a in (q, k, v, do_fine, do_coarse))
+    B, H, _, d = q.shape
+    scale = 1.0 / math.sqrt(d)
+    qcb, kcb, vcb, docb = reorder(q, g), reorder(k, g), reorder(v, g), reorder(dof, g)
+    dq = np.zeros_like(qcb)
+    dk = np.zeros_like(kcb)
+    dv = np.zeros_like(vcb)
+    for b in range(B):
+        for h in range(H):
+            for i in range(g["C"]):
+                rows = np.arange(SLOTS * i, SLOTS * i + SLOTS)
+                rows = rows[g["valid"][rows]]
+                keys = _key_positions(idx[b, h, i], g)
+                Q, Kk, V, dO = qcb[b, h, rows], kcb[b, h, keys], vcb[b, h, keys], docb[b, h, rows]
+                P = softmax_rows(Q @ Kk.T * scale)
+                dP = dO @ V.T
+                dS = P * (dP - (P * dP).sum(axis=1, keepdims=True))
+                dq[b, h, rows] += dS @ Kk * scale
+                dk[b, h, keys] += dS.T @ Q * scale
+                dv[b, h, keys] += P.T @ dO
+    # coarse stage
+    n = g["n_valid"][:, None]
+    qp, kp, vp = pool(qcb, g), pool(kcb, g), pool(vcb, g)
+    _, pc, _ = coarse(qp, kp, vp)
+    doc_sum = pool(reorder(doc, g), g) * n          # sum (not mean) over valid tokens
+    dvc = np.swapaxes(pc, -1, -2) @ doc_sum
+    dpc = doc_sum @ np.swapaxes(vp, -1, -2)
+    dsc = pc * (dpc - (pc * dpc).sum(axis=-1, keepdims=True))
+    dqc = dsc @ kp * scale
+    dkc = np.swapaxes(dsc, -1, -2) @ qp * scale
+    per_slot = lambda x: np.repeat(x / n, SLOTS, axis=-2) * g["valid"][:, None]
+    dq += per_slot(dqc)
+    dk += per_slot(dkc)
+    dv += per_slot(dvc)
+    return inverse_reorder(dq, g), inverse_reorder(dk, g), inverse_reorder(dv, g)

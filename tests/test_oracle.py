@@ -1,0 +1,329 @@
+"""Pins for the fp64 oracle: each check compares it with something other than
+itself (an independent construction, a closed form, a textbook routine, or a
+finite difference), so a dropped term, a wrong sign, index or operand order
+in the oracle fails at least one of them."""
+import math
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+from oracle import vsa_oracle as vo
+
+RAGGED_GRIDS = [(8, 8, 8), (5, 6, 7), (4, 4, 5), (1, 1, 1), (3, 9, 2), (16, 14, 26)]
+
+
+# --- independent constructions used by the pins -----------------------------
+
+def cube_ids(T, Hh, Ww):
+    """Cube id of every raster token, from its coordinates."""
+    t, y, x = np.meshgrid(np.arange(T), np.arange(Hh), np.arange(Ww), indexing="ij")
+    Ch, Cw = -(-Hh // 4), -(-Ww // 4)
+    return (((t // 4) * Ch + y // 4) * Cw + x // 4).reshape(-1)
+
+
+def pad_reshape_reorder(x, T, Hh, Ww):
+    """Raster -> cube order by zero-padding the grid and permuting axes."""
+    d = x.shape[-1]
+    Tp, Hp, Wp = 4 * -(-T // 4), 4 * -(-Hh // 4), 4 * -(-Ww // 4)
+    g = x.reshape(x.shape[:-2] + (T, Hh, Ww, d))
+    pad = [(0, 0)] * (g.ndim - 4) + [(0, Tp - T), (0, Hp - Hh), (0, Wp - Ww), (0, 0)]
+    g = np.pad(g, pad)
+    lead = g.shape[:-4]
+    g = g.reshape(lead + (Tp // 4, 4, Hp // 4, 4, Wp // 4, 4, d))
+    n = len(lead)
+    perm = list(range(n)) + [n + 0, n + 2, n + 4, n + 1, n + 3, n + 5, n + 6]
+    return g.transpose(perm).reshape(lead + (Tp * Hp * Wp, d))
+
+
+def mean_by_cube(x, ids, C):
+    """Per-cube mean of raster rows via index accumulation."""
+    s = np.zeros(x.shape[:-2] + (C, x.shape[-1]))
+    for c in range(C):
+        s[..., c, :] = x[..., ids == c, :].mean(axis=-2)
+    return s
+
+
+def sdpa(q, k, v, mask=None):
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float64))
+    m = None if mask is None else torch.from_numpy(mask)
+    return F.scaled_dot_product_attention(t(q), t(k), t(v), attn_mask=m).numpy()
+
+
+def block_mask(ids, idx):
+    """Token-level boolean mask: token r may attend r' iff cube(r') in idx[cube(r)]."""
+    H = idx.shape[0]
+    C = idx.shape[1]
+    sel = np.zeros((H, C, C), dtype=bool)
+    for h in range(H):
+        for i in range(C):
+            sel[h, i, idx[h, i]] = True
+    return sel[:, ids][:, :, ids]
+
+
+def random_idx(rng, H, C, K):
+    out = np.empty((H, C, K), np.int32)
+    for h in range(H):
+        for i in range(C):
+            out[h, i] = np.sort(rng.choice(C, size=K, replace=False))
+    return out
+
+
+def rank_topk(row, K):
+    """j is selected iff fewer than K entries beat it (higher score, or equal
+    score at a lower index)."""
+    n = len(row)
+    chosen = [j for j in range(n)
+              if sum(1 for i in range(n) if row[i] > row[j] or (row[i] == row[j] and i < j)) < K]
+    return np.array(chosen, dtype=np.int32)
+
+
+# --- reorder ----------------------------------------------------------------
+
+@pytest.mark.parametrize("grid", RAGGED_GRIDS)
+def test_reorder_matches_pad_and_axis_permutation(grid):
+    T, Hh, Ww = grid
+    rng = np.random.default_rng(1)
+    x = rng.standard_normal((2, T * Hh * Ww, 3))
+    g = vo.geometry(T, Hh, Ww)
+    xc = vo.reorder(x, g)
+    np.testing.assert_array_equal(xc, pad_reshape_reorder(x, T, Hh, Ww))
+    # inverse after forward is the identity; pads are exactly zero
+    np.testing.assert_array_equal(vo.inverse_reorder(xc, g), x)
+    assert np.all(xc[..., ~g["valid"], :] == 0)
+    # the valid slots are a bijection onto the raster tokens
+    assert sorted(g["token"][g["valid"]].tolist()) == list(range(T * Hh * Ww))
+    np.testing.assert_array_equal(g["cube_of_token"], cube_ids(T, Hh, Ww))
+
+
+def test_valid_count_histogram_wan_shape():
+    # 16x14x26 padded to 16x16x28: 4 cubes of 16, 36 of 32, 72 of 64 valid slots
+    g = vo.geometry(16, 14, 26)
+    vals, counts = np.unique(g["n_valid"], return_counts=True)
+    assert dict(zip(vals.tolist(), counts.tolist())) == {16: 4, 32: 36, 64: 72}
+    assert g["C"] == 112 and g["Np"] == 7168
+
+
+# --- pool ---------------------------------------------------------------
+
+@pytest.mark.parametrize("grid", RAGGED_GRIDS)
+def test_pool_cube_constant_input(grid):
+    T, Hh, Ww = grid
+    g = vo.geometry(T, Hh, Ww)
+    rng = np.random.default_rng(2)
+    const = rng.standard_normal((g["C"], 5))
+    x = const[cube_ids(T, Hh, Ww)]
+    np.testing.assert_allclose(vo.pool(vo.reorder(x, g), g), const, rtol=0, atol=1e-13)
+
+
+@pytest.mark.parametrize("grid", RAGGED_GRIDS)
+def test_pool_linear_field_is_value_at_valid_centroid(grid):
+    T, Hh, Ww = grid
+    g = vo.geometry(T, Hh, Ww)
+    coef = np.array([[0.3, -1.2, 2.5, 0.7], [1.1, 0.4, -0.6, -2.0]])  # (a_t, a_y, a_x, e)
+    t, y, x = np.meshgrid(np.arange(T), np.arange(Hh), np.arange(Ww), indexing="ij")
+    pos = np.stack([t.ravel(), y.ravel(), x.ravel(), np.ones(t.size)], axis=1)
+    val = pos @ coef.T
+    got = vo.pool(vo.reorder(val, g), g)
+    for c in range(g["C"]):
+        ct, rem = divmod(c, g["Ch"] * g["Cw"])
+        ch, cw = divmod(rem, g["Cw"])
+        # valid slots of an edge cube form an nt x nh x nw box at its low corner
+        nt, nh, nw = min(4, T - 4 * ct), min(4, Hh - 4 * ch), min(4, Ww - 4 * cw)
+        cen = np.array([4 * ct + (nt - 1) / 2, 4 * ch + (nh - 1) / 2, 4 * cw + (nw - 1) / 2, 1.0])
+        np.testing.assert_allclose(got[c], coef @ cen, rtol=0, atol=1e-12)
+
+
+# --- coarse -------------------------------------------------------------
+
+@pytest.mark.parametrize("grid", [(8, 8, 8), (5, 6, 7), (16, 14, 26)])
+def test_coarse_is_dense_attention_over_cube_means(grid):
+    T, Hh, Ww = grid
+    g = vo.geometry(T, Hh, Ww)
+    rng = np.random.default_rng(3)
+    q, k, v = (rng.standard_normal((2, T * Hh * Ww, 16)) for _ in range(3))
+    ids = cube_ids(T, Hh, Ww)
+    qm, km, vm = (mean_by_cube(a, ids, g["C"]) for a in (q, k, v))
+    qp, kp, vp = (vo.pool(vo.reorder(a, g), g) for a in (q, k, v))
+    np.testing.assert_allclose(qp, qm, atol=1e-13)
+    sc, pc, oc = vo.coarse(qp, kp, vp)
+    np.testing.assert_allclose(pc.sum(-1), 1.0, atol=1e-13)
+    np.testing.assert_allclose(oc, sdpa(qm, km, vm), atol=1e-12)
+    # the scores are the scaled dot products; they rank like the softmax
+    np.testing.assert_allclose(sc, np.einsum("hid,hjd->hij", qm, km) / 4.0, atol=1e-12)
+    assert np.array_equal(np.argsort(-sc, axis=-1, kind="stable"),
+                          np.argsort(-pc, axis=-1, kind="stable"))
+
+
+# --- top-K ----------------------------------------------------------------
+
+def test_topk_matches_rank_definition_with_many_ties():
+    rng = np.random.default_rng(4)
+    for _ in range(200):
+        n = int(rng.integers(1, 24))
+        K = int(rng.integers(1, n + 1))
+        row = rng.integers(-3, 4, size=n).astype(np.float64)   # heavy ties
+        got = vo.topk(row[None], K)[0]
+        np.testing.assert_array_equal(got, rank_topk(row, K))
+        assert np.all(np.diff(got) > 0)
+
+
+def test_topk_crafted_ties_and_signed_zero():
+    np.testing.assert_array_equal(vo.topk(np.zeros((1, 10)), 3)[0], [0, 1, 2])
+    row = np.array([1.0, 5.0, 5.0, 2.0, 5.0, 0.0])
+    np.testing.assert_array_equal(vo.topk(row[None], 2)[0], [1, 2])
+    np.testing.assert_array_equal(vo.topk(row[None], 4)[0], [1, 2, 3, 4])
+    # -0.0 and +0.0 are the same score: the lower index wins
+    row = np.array([-1.0, 0.0, -0.0, -0.0, -2.0])
+    np.testing.assert_array_equal(vo.topk(row[None], 1)[0], [1])
+    row = np.array([-1.0, -0.0, 0.0, -2.0])
+    np.testing.assert_array_equal(vo.topk(row[None], 2)[0], [1, 2])
+    # K = C keeps everything
+    np.testing.assert_array_equal(vo.topk(np.random.default_rng(0).standard_normal((1, 7)), 7)[0],
+                                  np.arange(7))
+
+
+# --- fine ----------------------------------------------------------------
+
+@pytest.mark.parametrize("grid,K", [((8, 8, 8), 2), ((5, 6, 7), 3), ((4, 4, 5), 1), ((3, 9, 2), 2)])
+def test_fine_equals_block_masked_dense_attention(grid, K):
+    T, Hh, Ww = grid
+    g = vo.geometry(T, Hh, Ww)
+    rng = np.random.default_rng(5)
+    H, d = 2, 8
+    q, k, v = (rng.standard_normal((1, H, T * Hh * Ww, d)) for _ in range(3))
+    idx = random_idx(rng, H, g["C"], min(K, g["C"]))[None]
+    out = vo.forward(q, k, v, T, Hh, Ww, K, idx=idx)
+    ids = cube_ids(T, Hh, Ww)
+    mask = block_mask(ids, idx[0])[None]
+    np.testing.assert_allclose(out["o_fine"], sdpa(q, k, v, mask), atol=1e-12)
+    # log-sum-exp of the masked scores
+    s = np.einsum("bhrd,bhsd->bhrs", q, k) / math.sqrt(d)
+    ref_lse = torch.logsumexp(torch.from_numpy(np.where(mask, s, -np.inf)), dim=-1).numpy()
+    np.testing.assert_allclose(vo.inverse_reorder(out["lse_cube"][..., None], g)[..., 0],
+                               ref_lse, atol=1e-12)
+
+
+@pytest.mark.parametrize("grid", [(8, 8, 8), (5, 6, 7)])
+def test_fine_with_all_cubes_is_dense_attention(grid):
+    T, Hh, Ww = grid
+    g = vo.geometry(T, Hh, Ww)
+    rng = np.random.default_rng(6)
+    q, k, v = (rng.standard_normal((1, 2, T * Hh * Ww, 8)) for _ in range(3))
+    out = vo.forward(q, k, v, T, Hh, Ww, g["C"])
+    np.testing.assert_array_equal(out["idx"][0, 0, 0], np.arange(g["C"]))
+    np.testing.assert_allclose(out["o_fine"], sdpa(q, k, v), atol=1e-12)
+
+
+def test_fine_constant_values_give_that_constant():
+    T, Hh, Ww = 5, 6, 7
+    rng = np.random.default_rng(7)
+    q, k = (rng.standard_normal((1, 1, T * Hh * Ww, 8)) for _ in range(2))
+    row = rng.standard_normal(8)
+    v = np.broadcast_to(row, q.shape).copy()
+    out = vo.forward(q, k, v, T, Hh, Ww, 2)
+    np.testing.assert_allclose(out["o_fine"], v, atol=1e-13)   # softmax rows sum to 1
+    np.testing.assert_allclose(out["o_coarse"], v, atol=1e-13)
+
+
+def test_fine_self_cube_only_is_local_attention():
+    T, Hh, Ww = 8, 8, 8
+    g = vo.geometry(T, Hh, Ww)
+    rng = np.random.default_rng(8)
+    q, k, v = (rng.standard_normal((1, 1, T * Hh * Ww, 8)) for _ in range(3))
+    idx = np.arange(g["C"], dtype=np.int32).reshape(1, 1, g["C"], 1)
+    out = vo.forward(q, k, v, T, Hh, Ww, 1, idx=idx)
+    qc, kc, vc = (pad_reshape_reorder(a, T, Hh, Ww) for a in (q, k, v))
+    for c in range(g["C"]):
+        sl = slice(64 * c, 64 * c + 64)
+        ref = sdpa(qc[..., sl, :], kc[..., sl, :], vc[..., sl, :])
+        np.testing.assert_allclose(out["o_fine_cube"][..., sl, :], ref, atol=1e-12)
+
+
+def test_forward_selection_follows_pooled_scores():
+    T, Hh, Ww = 8, 12, 10
+    g = vo.geometry(T, Hh, Ww)
+    rng = np.random.default_rng(9)
+    q, k, v = (rng.standard_normal((1, 2, T * Hh * Ww, 16)) for _ in range(3))
+    K = 3
+    out = vo.forward(q, k, v, T, Hh, Ww, K)
+    ids = cube_ids(T, Hh, Ww)
+    qm, km, vm = (mean_by_cube(a, ids, g["C"]) for a in (q, k, v))
+    sc = np.einsum("bhid,bhjd->bhij", qm, km) / 4.0
+    for h in range(2):
+        for i in range(g["C"]):
+            np.testing.assert_array_equal(out["idx"][0, h, i], rank_topk(sc[0, h, i], K))
+    np.testing.assert_allclose(out["o_coarse"], sdpa(qm, km, vm)[..., ids, :], atol=1e-12)
+
+
+# --- backward -----------------------------------------------------------
+
+def _loss(q, k, v, gf, gc, T, Hh, Ww, idx):
+    out = vo.forward(q, k, v, T, Hh, Ww, idx.shape[-1], idx=idx)
+    return float((out["o_fine"] * gf).sum() + (out["o_coarse"] * gc).sum())
+
+
+def test_backward_matches_central_differences():
+    T, Hh, Ww, d, K = 3, 5, 6, 4, 2
+    g = vo.geometry(T, Hh, Ww)
+    rng = np.random.default_rng(10)
+    shape = (1, 1, T * Hh * Ww, d)
+    q, k, v, gf, gc = (rng.standard_normal(shape) for _ in range(5))
+    idx = random_idx(rng, 1, g["C"], K)[None]
+    dq, dk, dv = vo.backward(q, k, v, gf, gc, T, Hh, Ww, idx)
+    h = 1e-6
+    for name, x, grad in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+        coords = [tuple(c) for c in rng.integers(0, [1, 1, T * Hh * Ww, d], size=(40, 4))]
+        for c in coords:
+            xp, xm = x.copy(), x.copy()
+            xp[c] += h
+            xm[c] -= h
+            args = {"q": q, "k": k, "v": v}
+            lp = _loss(*[xp if n == name else args[n] for n in "qkv"], gf, gc, T, Hh, Ww, idx)
+            lm = _loss(*[xm if n == name else args[n] for n in "qkv"], gf, gc, T, Hh, Ww, idx)
+            fd = (lp - lm) / (2 * h)
+            assert abs(fd - grad[c]) <= 1e-6 * max(1.0, abs(fd)), (name, c, fd, grad[c])
+
+
+def _torch_reference_grads(q, k, v, gf, gc, T, Hh, Ww, idx):
+    """Autograd of block-masked dense attention plus attention over cube means."""
+    C = idx.shape[2]
+    ids = torch.from_numpy(cube_ids(T, Hh, Ww))
+    mask = torch.from_numpy(block_mask(cube_ids(T, Hh, Ww), idx[0]))[None]
+    onehot = torch.nn.functional.one_hot(ids, C).to(torch.float64)      # (N, C)
+    avg = (onehot / onehot.sum(0, keepdim=True)).T                       # (C, N)
+    tq, tk, tv = (torch.from_numpy(a).requires_grad_(True) for a in (q, k, v))
+    of = F.scaled_dot_product_attention(tq, tk, tv, attn_mask=mask)
+    oc = F.scaled_dot_product_attention(avg @ tq, avg @ tk, avg @ tv)
+    loss = (of * torch.from_numpy(gf)).sum() + ((onehot @ oc) * torch.from_numpy(gc)).sum()
+    loss.backward()
+    return tq.grad.numpy(), tk.grad.numpy(), tv.grad.numpy()
+
+
+@pytest.mark.parametrize("grid,K", [((8, 8, 9), 3), ((5, 6, 7), 1), ((4, 8, 8), 4)])
+def test_backward_matches_torch_autograd(grid, K):
+    T, Hh, Ww = grid
+    g = vo.geometry(T, Hh, Ww)
+    rng = np.random.default_rng(11)
+    shape = (1, 2, T * Hh * Ww, 16)
+    q, k, v, gf, gc = (rng.standard_normal(shape) for _ in range(5))
+    idx = random_idx(rng, 2, g["C"], min(K, g["C"]))[None]
+    got = vo.backward(q, k, v, gf, gc, T, Hh, Ww, idx)
+    ref = _torch_reference_grads(q, k, v, gf, gc, T, Hh, Ww, idx)
+    for a, b in zip(got, ref):
+        np.testing.assert_allclose(a, b, atol=1e-11)
+
+
+def test_backward_all_cubes_fine_only_is_dense_attention_backward():
+    T, Hh, Ww = 5, 6, 7
+    g = vo.geometry(T, Hh, Ww)
+    rng = np.random.default_rng(12)
+    shape = (1, 1, T * Hh * Ww, 8)
+    q, k, v, gf = (rng.standard_normal(shape) for _ in range(4))
+    idx = np.tile(np.arange(g["C"], dtype=np.int32), (1, 1, g["C"], 1))
+    got = vo.backward(q, k, v, gf, np.zeros(shape), T, Hh, Ww, idx)
+    tq, tk, tv = (torch.from_numpy(a).requires_grad_(True) for a in (q, k, v))
+    (F.scaled_dot_product_attention(tq, tk, tv) * torch.from_numpy(gf)).sum().backward()
+    for a, b in zip(got, (tq.grad, tk.grad, tv.grad)):
+        np.testing.assert_allclose(a, b.numpy(), atol=1e-12)
