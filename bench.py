@@ -1,0 +1,167 @@
+"""VSA forward benchmark on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+
+Workload: Wan-1.3B 480p shape -- token grid 16x14x26 (5824 tokens) padded to
+16x16x28 (7168 tokens, 112 cubes), 12 heads, d = 128, bf16, top-K = 14 of 112
+cubes (87.5% sparse), synthetic seeded q/k/v.  A step is one vsa_forward call
+(raster q/k/v in HBM -> O_fine, O_coarse, block indices, LSE); inputs rotate
+over 5 independent sets (268 MB) so calls read HBM rather than a warm cache.
+
+Prints one JSON line.  Besides the headline (ms per forward) it reports the
+fine kernel alone (vsa_fine on cube-order inputs), coarse + fine, and the
+in-repo dense flash attention on the same padded sequence (the fine kernel
+with every cube selected), the fine kernel's MFMA roofline, and the fp64 CPU
+oracle timed on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "VSA fwd ms + sparse TFLOPS (% bf16 MFMA peak), 7168 tok, 12 heads, 87.5% sparse"
+N_SETS = 5
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-reps", type=int, default=5)
+    return ap.parse_args()
+
+
+def timed(fn, steps, warmup, rotate):
+    """Average ms per call of fn(i) over `steps` calls, HIP events on the current stream."""
+    import torch
+    for i in range(warmup):
+        fn(i % rotate)
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for i in range(steps):
+        fn(i % rotate)
+    stop.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(stop) / steps
+
+
+def cpu_baseline(w, x, reps):
+    from threadpoolctl import threadpool_info, threadpool_limits
+    from oracle import vsa_oracle as vo
+    cores = os.cpu_count() or 1
+    with threadpool_limits(limits=cores):
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            vo.forward(x["q"], x["k"], x["v"], w.T, w.Hh, w.Ww, w.topk)
+        dt = time.perf_counter() - t0
+    return {"value": round(dt / reps * 1e3, 3), "unit": "ms", "cores": threads, "kind": "oracle",
+            "sample": f"whole {w.name} forward (all {w.H} heads, {w.C} query cubes), fp64 NumPy, "
+                      f"{reps} repetitions, {dt:.1f} s total"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); "
+              "multi-GPU sharding is not part of this library", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import block_sparse_attention_cube_amd as vsa
+    from block_sparse_attention_cube_amd import flops
+    from synth import configs, inputs
+
+    w = configs.WAN_1_3B
+    grid = (w.T, w.Hh, w.Ww)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    host_sets = [inputs.make_inputs(w, seed=s) for s in range(N_SETS)]
+    sets = [{n: inputs.as_torch(h[n], w.dtype, dev) for n in "qkv"} for h in host_sets]
+    cube_sets = [{n: vsa.reorder(s[n], grid) for n in "qkv"} for s in sets]
+
+    plan = vsa.ForwardPlan(w.B, w.H, grid, w.d, w.topk, torch.bfloat16, dev)
+    step = lambda i: plan.run(sets[i]["q"], sets[i]["k"], sets[i]["v"])
+    ms = timed(step, args.steps, args.warmup, N_SETS)
+    warm_ms = timed(lambda i: step(0), args.steps, args.warmup, 1)
+
+    # fine kernel alone and coarse + fine on cube-order inputs
+    idx_sets = []
+    for c in cube_sets:
+        _, idx = vsa.coarse(c["q"], c["k"], c["v"], grid, w.topk)
+        idx_sets.append(idx)
+    o_buf = torch.empty_like(cube_sets[0]["q"])
+    fine_step = lambda i: vsa.fine(cube_sets[i]["q"], cube_sets[i]["k"], cube_sets[i]["v"],
+                                   idx_sets[i], grid, out=o_buf)
+    fine_ms = timed(fine_step, args.steps, args.warmup, N_SETS)
+
+    def coarse_fine(i):
+        c = cube_sets[i]
+        _, idx = vsa.coarse(c["q"], c["k"], c["v"], grid, w.topk)
+        vsa.fine(c["q"], c["k"], c["v"], idx, grid, out=o_buf)
+    cf_ms = timed(coarse_fine, args.steps, args.warmup, N_SETS)
+
+    # dense baseline: every cube selected, pad keys masked, same 7168-token sequence
+    all_idx = torch.arange(w.C, dtype=torch.int32, device=dev).expand(w.B, w.H, w.C, w.C).contiguous()
+    dense_step = lambda i: vsa.fine(cube_sets[i]["q"], cube_sets[i]["k"], cube_sets[i]["v"],
+                                    all_idx, grid, out=o_buf)
+    dense_ms = timed(dense_step, max(10, args.steps // 8), max(2, args.warmup // 4), N_SETS)
+
+    fl = flops.fine_forward_flops(w.B, w.H, w.C, w.topk, w.d)
+    fl_dense = flops.fine_forward_flops(w.B, w.H, w.C, w.C, w.d)
+    fine_tflops = fl / (fine_ms * 1e-3) / 1e12
+    fwd_tflops = fl / (ms * 1e-3) / 1e12
+
+    result = {
+        "metric": METRIC,
+        "value": round(ms, 5),
+        "unit": "ms",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "wan1.3b-480p: grid 16x14x26 -> 16x16x28 (7168 tok, 112 cubes), "
+                               "B=1, H=12, d=128, bf16, top-K 14 (87.5% sparse)",
+                   "global_batch": w.B, "seq_len": w.Np, "heads": w.H, "head_dim": w.d,
+                   "topk": w.topk, "cubes": w.C, "input_sets_rotated": N_SETS},
+        "sparse_tflops": round(fwd_tflops, 2),
+        "pct_bf16_peak": round(100 * fwd_tflops / flops.PEAK_BF16_TFLOPS, 2),
+        "warm_ms": round(warm_ms, 5),
+        "fine_ms": round(fine_ms, 5),
+        "fine_tflops": round(fine_tflops, 2),
+        "coarse_fine_ms": round(cf_ms, 5),
+        "dense_fa_ms": round(dense_ms, 5),
+        "speedup_fine_vs_dense": round(dense_ms / fine_ms, 3),
+        "speedup_coarse_fine_vs_dense": round(dense_ms / cf_ms, 3),
+        "speedup_forward_vs_dense": round(dense_ms / ms, 3),
+        "dense_tflops": round(fl_dense / (dense_ms * 1e-3) / 1e12, 2),
+        "roofline": {"bound": "mfma", "kernel": "fine_fwd_bf16_kernel<128,false> (vsa_fine)",
+                     "achieved": round(fine_tflops, 2), "peak": flops.PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(fine_tflops / flops.PEAK_BF16_TFLOPS, 4),
+                     "traffic": None},
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w, host_sets[0], args.cpu_reps)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,242 @@
+"""PyTorch binding of libvsa.so: the same entry points, tensors in, tensors out.
+
+Only marshalling happens here: shape checks, output/workspace allocation with
+torch (device memory), and the call with the current HIP stream.  Every step
+of the computation runs in the library's HIP kernels; tensors must already
+live on the GPU.
+"""
+from __future__ import annotations
+
+import ctypes
+from typing import Optional, Sequence, Tuple
+
+import torch
+
+from . import _lib as L
+
+Grid = Tuple[int, int, int]
+
+
+def cube_counts(grid: Grid) -> Tuple[int, int]:
+    """(C, Np): number of 4x4x4 cubes and padded token count of a (T, Hh, Ww) grid."""
+    T, Hh, Ww = grid
+    C = (-(-T // 4)) * (-(-Hh // 4)) * (-(-Ww // 4))
+    return C, 64 * C
+
+
+def _code(dtype: torch.dtype) -> int:
+    if dtype == torch.bfloat16:
+        return L.VSA_BF16
+    if dtype == torch.float32:
+        return L.VSA_F32
+    raise TypeError(f"VSA supports bfloat16 and float32 tensors, got {dtype}")
+
+
+def make_problem(B: int, H: int, grid: Grid, d: int, topk: int, dtype: torch.dtype) -> L.VSAProblem:
+    T, Hh, Ww = grid
+    return L.VSAProblem(B, H, T, Hh, Ww, d, 4, 4, 4, topk, _code(dtype))
+
+
+def _device_tensor(t: torch.Tensor, name: str) -> torch.Tensor:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor (got device {t.device})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _expect(t: torch.Tensor, shape: Sequence[int], dtype: torch.dtype, name: str) -> None:
+    _device_tensor(t, name)
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+
+
+def _workspace(prob: L.VSAProblem, op: int, device) -> Tuple[Optional[torch.Tensor], int]:
+    n = int(L.lib().vsa_workspace_bytes(ctypes.byref(prob), op))
+    if n == 0:
+        return None, 0
+    return torch.empty(n, dtype=torch.uint8, device=device), n
+
+
+def workspace_bytes(B: int, H: int, grid: Grid, d: int, topk: int, dtype: torch.dtype,
+                    op: int = L.VSA_OP_FORWARD) -> int:
+    prob = make_problem(B, H, grid, d, topk, dtype)
+    return int(L.lib().vsa_workspace_bytes(ctypes.byref(prob), op))
+
+
+def check_problem(B: int, H: int, grid: Grid, d: int, topk: int, dtype: torch.dtype) -> int:
+    prob = make_problem(B, H, grid, d, topk, dtype)
+    return int(L.lib().vsa_check_problem(ctypes.byref(prob)))
+
+
+def _raster_inputs(q, k, v, grid):
+    _device_tensor(q, "q")
+    B, H, N, d = q.shape
+    if N != grid[0] * grid[1] * grid[2]:
+        raise ValueError(f"q has {N} tokens, grid {grid} has {grid[0] * grid[1] * grid[2]}")
+    _expect(k, q.shape, q.dtype, "k")
+    _expect(v, q.shape, q.dtype, "v")
+    return B, H, N, d
+
+
+def reorder(x: torch.Tensor, grid: Grid, inverse: bool = False) -> torch.Tensor:
+    """Raster [B,H,N,d] -> cube order [B,H,Np,d] (pads zero), or back if inverse."""
+    _device_tensor(x, "x")
+    B, H, n, d = x.shape
+    C, Np = cube_counts(grid)
+    N = grid[0] * grid[1] * grid[2]
+    if n != (Np if inverse else N):
+        raise ValueError(f"x has {n} rows, expected {Np if inverse else N}")
+    y = torch.empty((B, H, N if inverse else Np, d), dtype=x.dtype, device=x.device)
+    prob = make_problem(B, H, grid, d, 1, x.dtype)
+    L.check(L.lib().vsa_reorder(ctypes.byref(prob), _ptr(x), _ptr(y), int(inverse),
+                                _stream(x.device)), "vsa_reorder")
+    return y
+
+
+def coarse(qcube: torch.Tensor, kcube: torch.Tensor, vcube: torch.Tensor, grid: Grid,
+           topk: int, return_scores: bool = False):
+    """Coarse stage on cube-order inputs: (o_coarse [B,H,C,d], idx [B,H,C,K][, scores])."""
+    _device_tensor(qcube, "qcube")
+    B, H, Np_in, d = qcube.shape
+    C, Np = cube_counts(grid)
+    if Np_in != Np:
+        raise ValueError(f"qcube has {Np_in} rows, expected {Np}")
+    _expect(kcube, qcube.shape, qcube.dtype, "kcube")
+    _expect(vcube, qcube.shape, qcube.dtype, "vcube")
+    prob = make_problem(B, H, grid, d, topk, qcube.dtype)
+    L.check(L.lib().vsa_check_problem(ctypes.byref(prob)), "vsa_coarse")
+    dev = qcube.device
+    oc = torch.empty((B, H, C, d), dtype=qcube.dtype, device=dev)
+    idx = torch.empty((B, H, C, topk), dtype=torch.int32, device=dev)
+    sc = torch.empty((B, H, C, C), dtype=torch.float32, device=dev) if return_scores else None
+    ws, nws = _workspace(prob, L.VSA_OP_COARSE, dev)
+    L.check(L.lib().vsa_coarse(ctypes.byref(prob), _ptr(qcube), _ptr(kcube), _ptr(vcube),
+                               _ptr(oc), _ptr(idx), _ptr(sc), _ptr(ws), nws, _stream(dev)),
+            "vsa_coarse")
+    return (oc, idx, sc) if return_scores else (oc, idx)
+
+
+def fine(qcube: torch.Tensor, kcube: torch.Tensor, vcube: torch.Tensor, idx: torch.Tensor,
+         grid: Grid, return_lse: bool = True, out: Optional[torch.Tensor] = None):
+    """Fine stage on cube-order inputs: (o_fine cube order [B,H,Np,d], lse [B,H,Np])."""
+    _device_tensor(qcube, "qcube")
+    B, H, Np_in, d = qcube.shape
+    C, Np = cube_counts(grid)
+    if Np_in != Np:
+        raise ValueError(f"qcube has {Np_in} rows, expected {Np}")
+    _expect(kcube, qcube.shape, qcube.dtype, "kcube")
+    _expect(vcube, qcube.shape, qcube.dtype, "vcube")
+    _device_tensor(idx, "idx")
+    if idx.dtype != torch.int32 or idx.dim() != 4 or tuple(idx.shape[:3]) != (B, H, C):
+        raise ValueError(f"idx must be int32 [B,H,C,K], got {idx.dtype} {tuple(idx.shape)}")
+    topk = idx.shape[3]
+    prob = make_problem(B, H, grid, d, topk, qcube.dtype)
+    dev = qcube.device
+    o = out if out is not None else torch.empty_like(qcube)
+    _expect(o, qcube.shape, qcube.dtype, "out")
+    lse = torch.empty((B, H, Np), dtype=torch.float32, device=dev) if return_lse else None
+    ws, nws = _workspace(prob, L.VSA_OP_FINE, dev)
+    L.check(L.lib().vsa_fine(ctypes.byref(prob), _ptr(qcube), _ptr(kcube), _ptr(vcube),
+                             _ptr(idx), _ptr(o), _ptr(lse), _ptr(ws), nws, _stream(dev)),
+            "vsa_fine")
+    return o, lse
+
+
+class ForwardPlan:
+    """Preallocated outputs and workspace for repeated vsa_forward calls on one shape."""
+
+    def __init__(self, B: int, H: int, grid: Grid, d: int, topk: int, dtype: torch.dtype,
+                 device, return_lse: bool = True):
+        self.prob = make_problem(B, H, grid, d, topk, dtype)
+        L.check(L.lib().vsa_check_problem(ctypes.byref(self.prob)), "vsa_forward")
+        C, Np = cube_counts(grid)
+        N = grid[0] * grid[1] * grid[2]
+        self.shape = (B, H, N, d)
+        self.dtype = dtype
+        self.device = torch.device(device)
+        self.o_fine = torch.empty(self.shape, dtype=dtype, device=device)
+        self.o_coarse = torch.empty(self.shape, dtype=dtype, device=device)
+        self.idx = torch.empty((B, H, C, topk), dtype=torch.int32, device=device)
+        self.lse = torch.empty((B, H, Np), dtype=torch.float32, device=device) if return_lse else None
+        self.ws, self.nws = _workspace(self.prob, L.VSA_OP_FORWARD, device)
+
+    def run(self, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor):
+        for t, n in ((q, "q"), (k, "k"), (v, "v")):
+            _expect(t, self.shape, self.dtype, n)
+        L.check(L.lib().vsa_forward(ctypes.byref(self.prob), _ptr(q), _ptr(k), _ptr(v),
+                                    _ptr(self.o_fine), _ptr(self.o_coarse), _ptr(self.idx),
+                                    _ptr(self.lse), _ptr(self.ws), self.nws,
+                                    _stream(self.device)), "vsa_forward")
+        return self.o_fine, self.o_coarse, self.idx, self.lse
+
+
+def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, grid: Grid, topk: int,
+            return_lse: bool = True):
+    """Whole VSA forward on raster tensors: (o_fine, o_coarse, idx, lse)."""
+    B, H, N, d = _raster_inputs(q, k, v, grid)
+    plan = ForwardPlan(B, H, grid, d, topk, q.dtype, q.device, return_lse)
+    return plan.run(q, k, v)
+
+
+def backward(q, k, v, o_fine, lse, idx, do_fine, do_coarse, grid: Grid):
+    """Gradients (dq, dk, dv) of sum(o_fine*do_fine) + sum(o_coarse*do_coarse)."""
+    B, H, N, d = _raster_inputs(q, k, v, grid)
+    C, Np = cube_counts(grid)
+    _expect(o_fine, q.shape, q.dtype, "o_fine")
+    _expect(do_fine, q.shape, q.dtype, "do_fine")
+    if do_coarse is not None:
+        _expect(do_coarse, q.shape, q.dtype, "do_coarse")
+    _expect(lse, (B, H, Np), torch.float32, "lse")
+    _device_tensor(idx, "idx")
+    if idx.dtype != torch.int32 or tuple(idx.shape[:3]) != (B, H, C):
+        raise ValueError("idx must be int32 [B,H,C,K]")
+    topk = idx.shape[3]
+    prob = make_problem(B, H, grid, d, topk, q.dtype)
+    dev = q.device
+    dq, dk, dv = (torch.empty_like(q) for _ in range(3))
+    ws, nws = _workspace(prob, L.VSA_OP_BACKWARD, dev)
+    L.check(L.lib().vsa_backward(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(o_fine),
+                                 _ptr(lse), _ptr(idx), _ptr(do_fine), _ptr(do_coarse),
+                                 _ptr(dq), _ptr(dk), _ptr(dv), _ptr(ws), nws, _stream(dev)),
+            "vsa_backward")
+    return dq, dk, dv
+
+
+class VSAFunction(torch.autograd.Function):
+    """Trainable VSA: (o_fine, o_coarse) = VSA(q, k, v); the selection is constant."""
+
+    @staticmethod
+    def forward(ctx, q, k, v, grid, topk):
+        q, k, v = q.contiguous(), k.contiguous(), v.contiguous()
+        o_fine, o_coarse, idx, lse = forward(q, k, v, grid, topk, return_lse=True)
+        o_fine, o_coarse = o_fine.clone(), o_coarse.clone()
+        ctx.save_for_backward(q, k, v, o_fine, lse, idx)
+        ctx.grid = grid
+        ctx.mark_non_differentiable(idx)
+        return o_fine, o_coarse, idx.clone()
+
+    @staticmethod
+    def backward(ctx, do_fine, do_coarse, _didx):
+        q, k, v, o_fine, lse, idx = ctx.saved_tensors
+        do_fine = torch.zeros_like(o_fine) if do_fine is None else do_fine.contiguous()
+        do_coarse = None if do_coarse is None else do_coarse.contiguous()
+        dq, dk, dv = backward(q, k, v, o_fine, lse, idx, do_fine, do_coarse, ctx.grid)
+        return dq, dk, dv, None, None
+
+
+def vsa_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, grid: Grid, topk: int):
+    """Autograd entry: returns (o_fine, o_coarse, idx)."""
+    return VSAFunction.apply(q, k, v, grid, topk)

@@ -1,0 +1,228 @@
+// Coarse stage of VSA: cube-level attention and the top-K block selection.
+//
+// Input: fp32 means of q, k, v per cube, [B,H,C,D] (written by the reorder).
+// One workgroup (4 waves) owns 16 query-cube rows of one head:
+//   1. Sc[16, C] = Qc Kc^T / sqrt(D) on fp32 MFMA (v_mfma_f32_16x16x4_f32),
+//      kept in LDS (16 x C fp32, C <= 2048) and optionally written out;
+//   2. row max and 1/sum(exp) per row (one wave per row, wave reductions);
+//   3. O_coarse[16, D] = softmax(Sc) Vc on fp32 MFMA, probabilities formed on
+//      the fly from the LDS scores;
+//   4. top-K per row: the K-th largest score is found exactly by a 32-step
+//      bitwise search over order-preserving uint32 keys of the fp32 scores,
+//      then one ordered pass with wave ballots emits every index above it
+//      plus the lowest-index ties, already in ascending order.
+// Everything is fp32 (no bf16 rounding of means or scores), so the selection
+// differs from an exact one only where two scores are within fp32 rounding.
+#include "vsa_internal.h"
+
+namespace vsa {
+namespace {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ inline float wave_max(float x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
+  return x;
+}
+__device__ inline float wave_sum(float x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
+  return x;
+}
+__device__ inline int wave_sum_int(int x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
+  return x;
+}
+
+// Order-preserving key of an fp32 score: a > b  <=>  key(a) > key(b); -0 == +0.
+__device__ inline uint32_t score_key(float f) {
+  uint32_t u = __float_as_uint(f);
+  if (u == 0x80000000u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ inline void store_out(float* p, float x) { *p = x; }
+__device__ inline void store_out(uint16_t* p, float x) { *p = f32_to_bf16_rne(x); }
+
+constexpr int kRows = 16;
+constexpr int kMaxKeysPerLane = kMaxCubes / 64;
+
+template <typename TOut, int D>
+__global__ __launch_bounds__(256) void coarse_kernel(const float* __restrict__ qm,
+                                                     const float* __restrict__ km,
+                                                     const float* __restrict__ vm,
+                                                     TOut* __restrict__ oc,
+                                                     int32_t* __restrict__ idx,
+                                                     float* __restrict__ scores, Geo g,
+                                                     int ldc) {
+  extern __shared__ float lds[];
+  float* sc = lds;                       // [kRows][ldc]
+  float* rowmax = lds + kRows * ldc;     // [kRows]
+  float* rowinv = rowmax + kRows;        // [kRows]
+
+  constexpr float kScale = (D == 64) ? 0.125f : 0.08838834764831845f;  // 1/sqrt(D)
+  const int C = g.C;
+  const int64_t bh = blockIdx.y;
+  const int row0 = blockIdx.x * kRows;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int li = lane & 15, lg = lane >> 4;
+  const float* qh = qm + bh * C * D;
+  const float* kh = km + bh * C * D;
+  const float* vh = vm + bh * C * D;
+
+  // -- 1. scores.  Lane (li, lg) feeds A[m=li][k=lg] and B[k=lg][n=li]; the
+  // t-th of four MFMAs per 16-wide slice of D uses d = 16*kk + 4*lg + t for
+  // both operands, so their products pair up on the same d.
+  float4 qf[D / 16];
+  {
+    const int r = row0 + li;
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk)
+      qf[kk] = (r < C) ? *reinterpret_cast<const float4*>(qh + (int64_t)r * D + 16 * kk + 4 * lg)
+                       : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  const int ntile = (C + 15) / 16;
+  for (int ct = wave; ct < ntile; ct += 4) {
+    const int col = ct * 16 + li;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) {
+      const float4 kf = (col < C)
+          ? *reinterpret_cast<const float4*>(kh + (int64_t)col * D + 16 * kk + 4 * lg)
+          : make_float4(0.f, 0.f, 0.f, 0.f);
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(qf[kk].x, kf.x, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(qf[kk].y, kf.y, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(qf[kk].z, kf.z, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(qf[kk].w, kf.w, acc, 0, 0, 0);
+    }
+    // acc[r] is the dot product of query row 4*lg + r with key column col
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int rr = 4 * lg + r;
+      const float s = acc[r] * kScale;
+      sc[rr * ldc + col] = s;
+      if (scores != nullptr && row0 + rr < C && col < C)
+        scores[(bh * C + row0 + rr) * C + col] = s;
+    }
+  }
+  __syncthreads();
+
+  // -- 2. softmax statistics per row
+  for (int rr = wave; rr < kRows; rr += 4) {
+    const float* srow = sc + rr * ldc;
+    float m = -INFINITY;
+    for (int j = lane; j < C; j += 64) m = fmaxf(m, srow[j]);
+    m = wave_max(m);
+    float s = 0.f;
+    for (int j = lane; j < C; j += 64) s += __expf(srow[j] - m);
+    s = wave_sum(s);
+    if (lane == 0) {
+      rowmax[rr] = m;
+      rowinv[rr] = 1.f / s;
+    }
+  }
+  __syncthreads();
+
+  // -- 3. O_coarse = P Vc: A[m=li][k=lg] = P[row li][j], B[k=lg][n=li] = Vc[j][col]
+  {
+    const float mrow = rowmax[li], irow = rowinv[li];
+    const float* prow = sc + li * ldc;
+    for (int dt = wave; dt < D / 16; dt += 4) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      for (int j0 = 0; j0 < C; j0 += 16) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const int j = j0 + 4 * lg + t;
+          const float a = (j < C) ? __expf(prow[j] - mrow) * irow : 0.f;
+          const float b = (j < C) ? vh[(int64_t)j * D + dt * 16 + li] : 0.f;
+          acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc, 0, 0, 0);
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = row0 + 4 * lg + r;
+        if (row < C) store_out(oc + (bh * C + row) * D + dt * 16 + li, acc[r]);
+      }
+    }
+  }
+
+  // -- 4. top-K per row (one wave per row)
+  const int K = g.K;
+  const int nk = (C + 63) / 64;
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  for (int rr = wave; rr < kRows; rr += 4) {
+    if (row0 + rr >= C) break;
+    const float* srow = sc + rr * ldc;
+    uint32_t key[kMaxKeysPerLane];
+#pragma unroll
+    for (int e = 0; e < kMaxKeysPerLane; ++e) {
+      const int j = e * 64 + lane;
+      key[e] = (e < nk && j < C) ? score_key(srow[j]) : 0u;  // 0 is below every score key
+    }
+    // largest threshold t with #{key >= t} >= K, i.e. the K-th largest key
+    uint32_t thr = 0u;
+    for (int bit = 31; bit >= 0; --bit) {
+      const uint32_t cand = thr | (1u << bit);
+      int cnt = 0;
+#pragma unroll
+      for (int e = 0; e < kMaxKeysPerLane; ++e)
+        if (e < nk) cnt += (key[e] >= cand) ? 1 : 0;
+      if (wave_sum_int(cnt) >= K) thr = cand;
+    }
+    int gt = 0;
+#pragma unroll
+    for (int e = 0; e < kMaxKeysPerLane; ++e)
+      if (e < nk) gt += (key[e] > thr) ? 1 : 0;
+    const int need = K - wave_sum_int(gt);  // ties at the threshold to keep, lowest index first
+    int ties_before = 0, sel_before = 0;
+    int32_t* out = idx + (bh * C + row0 + rr) * K;
+#pragma unroll
+    for (int e = 0; e < kMaxKeysPerLane; ++e) {
+      if (e < nk) {  // uniform across the wave
+        const int j = e * 64 + lane;
+        const bool is_gt = (j < C) && key[e] > thr;
+        const bool is_eq = (j < C) && key[e] == thr;
+        const uint64_t eqm = __ballot(is_eq);
+        const int eq_rank = ties_before + __popcll(eqm & lt_mask);
+        const bool take = is_gt || (is_eq && eq_rank < need);
+        const uint64_t takem = __ballot(take);
+        if (take) out[sel_before + __popcll(takem & lt_mask)] = j;
+        ties_before += __popcll(eqm);
+        sel_before += __popcll(takem);
+      }
+    }
+  }
+}
+
+template <typename TOut, int D>
+hipError_t launch_typed(const Geo& g, const float* qm, const float* km, const float* vm,
+                        void* oc, int32_t* idx, float* scores, hipStream_t s) {
+  const int ntile = (g.C + 15) / 16;
+  const int ldc = ntile * 16 + 1;  // odd stride spreads a column over the LDS banks
+  const size_t lds = (size_t)(kRows * ldc + 2 * kRows) * sizeof(float);
+  auto* kern = coarse_kernel<TOut, D>;
+  if (lds > 65536) {
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize,
+                                             static_cast<int>(lds));
+    if (e != hipSuccess) return e;
+  }
+  return launch_kernel(kern, dim3(ntile, g.B * g.H), dim3(256), lds, s, qm, km, vm,
+                       static_cast<TOut*>(oc), idx, scores, g, ldc);
+}
+
+}  // namespace
+
+hipError_t launch_coarse(const Geo& g, int dtype, const float* qm, const float* km,
+                         const float* vm, void* oc, int32_t* idx, float* scores,
+                         hipStream_t s) {
+  if (dtype == 1)
+    return g.D == 128 ? launch_typed<uint16_t, 128>(g, qm, km, vm, oc, idx, scores, s)
+                      : launch_typed<uint16_t, 64>(g, qm, km, vm, oc, idx, scores, s);
+  return g.D == 128 ? launch_typed<float, 128>(g, qm, km, vm, oc, idx, scores, s)
+                    : launch_typed<float, 64>(g, qm, km, vm, oc, idx, scores, s);
+}
+
+}  // namespace vsa

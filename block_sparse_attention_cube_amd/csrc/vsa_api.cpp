@@ -1,0 +1,229 @@
+// C ABI of the VSA library: argument validation, workspace layout and the
+// launch sequence of every entry point.  No device memory is allocated here;
+// nothing is enqueued until every argument has been checked.
+#include "../../include/vsa.h"
+#include "vsa_internal.h"
+
+#include <initializer_list>
+
+namespace {
+
+using vsa::Geo;
+
+constexpr size_t kAlign = 256;
+size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+vsa_status check(const vsa_problem* p) {
+  if (p == nullptr) return VSA_ERR_NULL;
+  if (p->B < 1 || p->H < 1 || p->T < 1 || p->Hh < 1 || p->Ww < 1) return VSA_ERR_SHAPE;
+  if (p->cube_t != vsa::kCube || p->cube_h != vsa::kCube || p->cube_w != vsa::kCube)
+    return VSA_ERR_UNSUPPORTED;
+  if (p->d != 64 && p->d != 128) return VSA_ERR_UNSUPPORTED;
+  if (p->dtype != VSA_F32 && p->dtype != VSA_BF16) return VSA_ERR_UNSUPPORTED;
+  const int64_t C = int64_t((p->T + 3) / 4) * ((p->Hh + 3) / 4) * ((p->Ww + 3) / 4);
+  if (C > vsa::kMaxCubes) return VSA_ERR_UNSUPPORTED;
+  if (p->topk < 1 || p->topk > C) return VSA_ERR_SHAPE;
+  const int64_t bh = int64_t(p->B) * p->H;
+  if (bh > 65535) return VSA_ERR_UNSUPPORTED;                 // grid y extent
+  if (bh * C > (int64_t(1) << 30)) return VSA_ERR_UNSUPPORTED; // 1-D tile grid
+  // B*H*Np*d elements must stay far from int64 overflow
+  if (bh * C * 64 * p->d > (int64_t(1) << 58)) return VSA_ERR_UNSUPPORTED;
+  return VSA_OK;
+}
+
+Geo geometry(const vsa_problem* p) {
+  Geo g;
+  g.B = p->B; g.H = p->H; g.T = p->T; g.Hh = p->Hh; g.Ww = p->Ww; g.D = p->d;
+  g.Ct = (p->T + 3) / 4; g.Ch = (p->Hh + 3) / 4; g.Cw = (p->Ww + 3) / 4;
+  g.C = g.Ct * g.Ch * g.Cw;
+  g.K = p->topk;
+  g.N = int64_t(p->T) * p->Hh * p->Ww;
+  g.Np = int64_t(g.C) * vsa::kSlots;
+  return g;
+}
+
+size_t elem_bytes(const vsa_problem* p) { return p->dtype == VSA_BF16 ? 2 : 4; }
+
+// Sub-buffers of one workspace, each 256-byte aligned.
+struct Carver {
+  char* base;
+  size_t off = 0;
+  explicit Carver(void* b) : base(static_cast<char*>(b)) {}
+  void* take(size_t bytes) {
+    void* r = base ? base + off : nullptr;
+    off += round_up(bytes);
+    return r;
+  }
+};
+
+struct FwdWs {
+  void* qc; void* kc; void* vc;
+  float* qm; float* km; float* vm;
+  void* oc;
+};
+FwdWs carve_forward(const vsa_problem* p, void* ws, size_t* total) {
+  const Geo g = geometry(p);
+  const size_t e = elem_bytes(p);
+  const size_t cube = size_t(g.B) * g.H * g.Np * g.D * e;
+  const size_t mean = size_t(g.B) * g.H * g.C * g.D * sizeof(float);
+  Carver c(ws);
+  FwdWs w;
+  w.qc = c.take(cube); w.kc = c.take(cube); w.vc = c.take(cube);
+  w.qm = static_cast<float*>(c.take(mean));
+  w.km = static_cast<float*>(c.take(mean));
+  w.vm = static_cast<float*>(c.take(mean));
+  w.oc = c.take(size_t(g.B) * g.H * g.C * g.D * e);
+  if (total) *total = c.off;
+  return w;
+}
+
+struct CoarseWs { float* qm; float* km; float* vm; };
+CoarseWs carve_coarse(const vsa_problem* p, void* ws, size_t* total) {
+  const Geo g = geometry(p);
+  const size_t mean = size_t(g.B) * g.H * g.C * g.D * sizeof(float);
+  Carver c(ws);
+  CoarseWs w;
+  w.qm = static_cast<float*>(c.take(mean));
+  w.km = static_cast<float*>(c.take(mean));
+  w.vm = static_cast<float*>(c.take(mean));
+  if (total) *total = c.off;
+  return w;
+}
+
+bool misaligned(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) != 0; }
+
+vsa_status pointers(std::initializer_list<const void*> required,
+                    std::initializer_list<const void*> optional) {
+  for (const void* q : required)
+    if (q == nullptr) return VSA_ERR_NULL;
+  for (const void* q : required)
+    if (misaligned(q)) return VSA_ERR_ALIGN;
+  for (const void* q : optional)
+    if (q != nullptr && misaligned(q)) return VSA_ERR_ALIGN;
+  return VSA_OK;
+}
+
+vsa_status workspace(const vsa_problem* p, int op, const void* ws, size_t ws_bytes) {
+  const size_t need = vsa_workspace_bytes(p, op);
+  if (need == 0) return VSA_OK;
+  if (ws == nullptr) return VSA_ERR_NULL;
+  if (misaligned(ws)) return VSA_ERR_ALIGN;
+  if (ws_bytes < need) return VSA_ERR_WORKSPACE;
+  return VSA_OK;
+}
+
+vsa_status launched(hipError_t e) { return e == hipSuccess ? VSA_OK : VSA_ERR_LAUNCH; }
+
+}  // namespace
+
+extern "C" {
+
+vsa_status vsa_check_problem(const vsa_problem* p) { return check(p); }
+
+size_t vsa_workspace_bytes(const vsa_problem* p, int op) {
+  if (check(p) != VSA_OK) return 0;
+  size_t total = 0;
+  switch (op) {
+    case VSA_OP_FORWARD: carve_forward(p, nullptr, &total); return total;
+    case VSA_OP_COARSE: carve_coarse(p, nullptr, &total); return total;
+    case VSA_OP_FINE: return 0;
+    case VSA_OP_BACKWARD: return 0;
+    default: return 0;
+  }
+}
+
+const char* vsa_status_string(vsa_status s) {
+  switch (s) {
+    case VSA_OK: return "VSA_OK";
+    case VSA_ERR_NULL: return "VSA_ERR_NULL: a required pointer is NULL";
+    case VSA_ERR_SHAPE: return "VSA_ERR_SHAPE: a dimension is < 1 or topk is outside [1, C]";
+    case VSA_ERR_UNSUPPORTED:
+      return "VSA_ERR_UNSUPPORTED: head dim, cube size, dtype or problem size not supported";
+    case VSA_ERR_ALIGN: return "VSA_ERR_ALIGN: a device pointer is not 16-byte aligned";
+    case VSA_ERR_WORKSPACE: return "VSA_ERR_WORKSPACE: workspace smaller than required";
+    case VSA_ERR_LAUNCH: return "VSA_ERR_LAUNCH: the HIP runtime rejected a kernel launch";
+  }
+  return "VSA: unknown status";
+}
+
+vsa_status vsa_reorder(const vsa_problem* p, const void* x, void* y, int inverse,
+                       hipStream_t stream) {
+  vsa_status st = check(p);
+  if (st != VSA_OK) return st;
+  if ((st = pointers({x, y}, {})) != VSA_OK) return st;
+  const Geo g = geometry(p);
+  vsa::ReorderBatch b = {};
+  b.x[0] = x;
+  b.y[0] = y;
+  b.count = 1;
+  return launched(vsa::launch_reorder(g, p->dtype, inverse ? 1 : 0, b, stream));
+}
+
+vsa_status vsa_coarse(const vsa_problem* p, const void* qcube, const void* kcube,
+                      const void* vcube, void* o_coarse, int32_t* idx, float* scores,
+                      void* ws, size_t ws_bytes, hipStream_t stream) {
+  vsa_status st = check(p);
+  if (st != VSA_OK) return st;
+  if ((st = pointers({qcube, kcube, vcube, o_coarse, idx}, {scores})) != VSA_OK) return st;
+  if ((st = workspace(p, VSA_OP_COARSE, ws, ws_bytes)) != VSA_OK) return st;
+  const Geo g = geometry(p);
+  const CoarseWs w = carve_coarse(p, ws, nullptr);
+  vsa::ReorderBatch b = {};
+  b.x[0] = qcube; b.x[1] = kcube; b.x[2] = vcube;
+  b.mean[0] = w.qm; b.mean[1] = w.km; b.mean[2] = w.vm;
+  b.count = 3;
+  hipError_t e = vsa::launch_reorder(g, p->dtype, 2, b, stream);
+  if (e == hipSuccess)
+    e = vsa::launch_coarse(g, p->dtype, w.qm, w.km, w.vm, o_coarse, idx, scores, stream);
+  return launched(e);
+}
+
+vsa_status vsa_fine(const vsa_problem* p, const void* qcube, const void* kcube,
+                    const void* vcube, const int32_t* idx, void* o_fine, float* lse,
+                    void* ws, size_t ws_bytes, hipStream_t stream) {
+  vsa_status st = check(p);
+  if (st != VSA_OK) return st;
+  if ((st = pointers({qcube, kcube, vcube, idx, o_fine}, {lse})) != VSA_OK) return st;
+  if ((st = workspace(p, VSA_OP_FINE, ws, ws_bytes)) != VSA_OK) return st;
+  const Geo g = geometry(p);
+  return launched(vsa::launch_fine(g, p->dtype, qcube, kcube, vcube, idx, o_fine, lse,
+                                   /*raster_out=*/false, nullptr, nullptr, stream));
+}
+
+vsa_status vsa_forward(const vsa_problem* p, const void* q, const void* k, const void* v,
+                       void* o_fine, void* o_coarse, int32_t* idx, float* lse, void* ws,
+                       size_t ws_bytes, hipStream_t stream) {
+  vsa_status st = check(p);
+  if (st != VSA_OK) return st;
+  if ((st = pointers({q, k, v, o_fine, o_coarse, idx}, {lse})) != VSA_OK) return st;
+  if ((st = workspace(p, VSA_OP_FORWARD, ws, ws_bytes)) != VSA_OK) return st;
+  const Geo g = geometry(p);
+  const FwdWs w = carve_forward(p, ws, nullptr);
+  vsa::ReorderBatch b = {};
+  b.x[0] = q; b.x[1] = k; b.x[2] = v;
+  b.y[0] = w.qc; b.y[1] = w.kc; b.y[2] = w.vc;
+  b.mean[0] = w.qm; b.mean[1] = w.km; b.mean[2] = w.vm;
+  b.count = 3;
+  hipError_t e = vsa::launch_reorder(g, p->dtype, 0, b, stream);
+  if (e == hipSuccess)
+    e = vsa::launch_coarse(g, p->dtype, w.qm, w.km, w.vm, w.oc, idx, nullptr, stream);
+  if (e == hipSuccess)
+    e = vsa::launch_fine(g, p->dtype, w.qc, w.kc, w.vc, idx, o_fine, lse,
+                         /*raster_out=*/true, w.oc, o_coarse, stream);
+  return launched(e);
+}
+
+vsa_status vsa_backward(const vsa_problem* p, const void* q, const void* k, const void* v,
+                        const void* o_fine, const float* lse, const int32_t* idx,
+                        const void* do_fine, const void* do_coarse, void* dq, void* dk,
+                        void* dv, void* ws, size_t ws_bytes, hipStream_t stream) {
+  vsa_status st = check(p);
+  if (st != VSA_OK) return st;
+  if ((st = pointers({q, k, v, o_fine, lse, idx, do_fine, dq, dk, dv}, {do_coarse})) != VSA_OK)
+    return st;
+  if ((st = workspace(p, VSA_OP_BACKWARD, ws, ws_bytes)) != VSA_OK) return st;
+  (void)stream;
+  return VSA_ERR_UNSUPPORTED;
+}
+
+}  // extern "C"

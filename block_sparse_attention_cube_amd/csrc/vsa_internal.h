@@ -1,0 +1,109 @@
+// Internal declarations shared by the HIP kernels and the C-ABI layer.
+// Not installed; the public interface is include/vsa.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <tuple>
+
+namespace vsa {
+
+constexpr int kCube = 4;     // cube edge along each of (t, y, x)
+constexpr int kSlots = 64;   // tokens per cube
+constexpr int kMaxCubes = 2048;  // coarse score rows are staged in LDS: 16 x C fp32
+
+// Geometry of one problem, passed by value to every kernel.
+struct Geo {
+  int B, H, T, Hh, Ww, D;
+  int Ct, Ch, Cw, C;
+  int K;
+  int64_t N, Np;
+};
+
+// Cube grid position of cube c and its valid extent per axis (1..4).
+struct CubeExt {
+  int ct, ch, cw;
+  int nt, nh, nw;
+};
+
+__host__ __device__ inline CubeExt cube_extent(const Geo& g, int c) {
+  CubeExt e;
+  e.cw = c % g.Cw;
+  e.ch = (c / g.Cw) % g.Ch;
+  e.ct = c / (g.Cw * g.Ch);
+  e.nt = min(kCube, g.T - kCube * e.ct);
+  e.nh = min(kCube, g.Hh - kCube * e.ch);
+  e.nw = min(kCube, g.Ww - kCube * e.cw);
+  return e;
+}
+
+// Raster index of slot s (it*16 + ih*4 + iw) of a cube, or -1 for a pad slot.
+__host__ __device__ inline int64_t slot_token(const Geo& g, const CubeExt& e, int s) {
+  const int it = s >> 4, ih = (s >> 2) & 3, iw = s & 3;
+  if (it >= e.nt || ih >= e.nh || iw >= e.nw) return -1;
+  const int64_t t = kCube * e.ct + it, y = kCube * e.ch + ih, x = kCube * e.cw + iw;
+  return (t * g.Hh + y) * g.Ww + x;
+}
+
+// fp32 -> bfloat16 bits, round to nearest even (finite inputs).
+__device__ inline uint16_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+// Workgroups are dealt to the 8 XCDs round-robin (hardware id w runs on XCD
+// w % 8).  Remap so that each XCD receives one contiguous range of logical
+// tiles: tiles of one head then share that XCD's L2.
+__device__ inline int xcd_remap(int w, int n) {
+  constexpr int kXcd = 8;
+  const int q = n / kXcd, rem = n % kXcd;
+  const int x = w % kXcd, j = w / kXcd;
+  return (x < rem) ? x * (q + 1) + j : rem * (q + 1) + (x - rem) * q + j;
+}
+
+// Launches kernel k and returns the runtime's verdict on this launch alone
+// (unlike hipGetLastError, it neither reads nor clears errors of unrelated
+// earlier calls on this thread).
+template <typename... P, typename... A>
+hipError_t launch_kernel(void (*k)(P...), dim3 grid, dim3 block, size_t lds_bytes,
+                         hipStream_t s, A... a) {
+  static_assert(sizeof...(P) == sizeof...(A), "argument count");
+  std::tuple<P...> args(static_cast<P>(a)...);
+  return std::apply(
+      [&](auto&... e) {
+        void* ptrs[] = {static_cast<void*>(&e)...};
+        return hipLaunchKernel(reinterpret_cast<const void*>(k), grid, block, ptrs,
+                               lds_bytes, s);
+      },
+      args);
+}
+
+// ---- launchers (each returns the first HIP launch error, or hipSuccess) ----
+
+// mode 0: raster -> cube order (+ optional fp32 means), mode 1: cube -> raster,
+// mode 2: cube order -> fp32 means only.  Up to 3 tensors per launch.
+struct ReorderBatch {
+  const void* x[3];
+  void* y[3];
+  float* mean[3];
+  int count;
+};
+hipError_t launch_reorder(const Geo& g, int dtype, int mode, const ReorderBatch& b,
+                          hipStream_t s);
+
+// Coarse stage from fp32 cube means [B,H,C,D]: scores (optional), softmax,
+// O_coarse [B,H,C,D] in dtype, and the top-K index list [B,H,C,K].
+hipError_t launch_coarse(const Geo& g, int dtype, const float* qm, const float* km,
+                         const float* vm, void* oc, int32_t* idx, float* scores,
+                         hipStream_t s);
+
+// Fine stage.  raster_out = false: o is cube order [B,H,Np,D];
+// raster_out = true: o is raster [B,H,N,D] and, if oc != nullptr, o_coarse
+// (raster) receives the per-cube coarse row of every valid token.
+hipError_t launch_fine(const Geo& g, int dtype, const void* q, const void* k, const void* v,
+                       const int32_t* idx, void* o, float* lse, bool raster_out,
+                       const void* oc, void* o_coarse, hipStream_t s);
+
+}  // namespace vsa

@@ -1,0 +1,177 @@
+/*
+ * vsa.h -- C ABI of the MI355X (gfx950) video sparse attention library.
+ *
+ * Video sparse attention (VSA) is a trainable, dynamic block-sparse attention
+ * that drops in for FlashAttention inside a video diffusion transformer
+ * (FastWan/VSA re-post on yumynutrition.com, section
+ * "传统零散郑重力，为何会在蒸馏中失效？").  A coarse stage decides a
+ * block-sparse pattern of 64x64 blocks and a fine block-sparse kernel runs
+ * exact attention over it (same page, results section "一张卡，秒生视频": the
+ * fine-kernel, coarse-overhead and 64x64 FlexAttention lines, Fig. 5).
+ *
+ * Geometry.  q/k/v come in raster token order [B, H, N, d] with
+ * N = T*Hh*Ww and token r = (t*Hh + y)*Ww + x.  A 64-token block is a 4x4x4
+ * cube.  Each axis is padded at its high end to a multiple of 4, giving a
+ * cube grid (Ct, Ch, Cw) = (ceil(T/4), ceil(Hh/4), ceil(Ww/4)), C = Ct*Ch*Cw
+ * cubes and Np = 64*C padded tokens.  In "cube order" position
+ * p = 64*c + it*16 + ih*4 + iw, with c = (ct*Ch + ch)*Cw + cw, holds token
+ * (4ct+it, 4ch+ih, 4cw+iw); a position outside the real grid is a pad slot.
+ * Pad slots are zero in reorder outputs and are never attended to.
+ *
+ * Method (each stage restated in the entry point that runs it):
+ *   coarse:  Qc, Kc, Vc = mean over the valid slots of each cube (fp32);
+ *            Sc = Qc Kc^T / sqrt(d); O_coarse per cube = softmax_row(Sc) Vc;
+ *            idx[i] = the K key cubes with the largest Sc[i, :], ties to the
+ *            lower cube index, listed in ascending cube order.
+ *   fine:    for every query slot of cube i, exact softmax attention with
+ *            scale 1/sqrt(d) over the valid key slots of the cubes idx[i].
+ * Sparsity is 1 - K/C (8x fewer attention FLOPs at 87.5%, results section,
+ * 410M scaling experiment).
+ *
+ * Conventions shared by every entry point.
+ *   - All tensors are contiguous, d innermost, in the problem's dtype unless
+ *     stated: VSA_BF16 (bfloat16) or VSA_F32.  idx is int32, lse is fp32
+ *     natural-log log-sum-exp.
+ *   - The caller owns every buffer.  The library never allocates or frees
+ *     device memory, keeps no pointer after returning and holds no mutable
+ *     global state; calls are re-entrant.  Device pointers must point to
+ *     memory of the current HIP device.
+ *   - All work is enqueued asynchronously on `stream` (0 = null stream); the
+ *     library never synchronises with the host.  Buffers must stay alive
+ *     until the stream has executed the work.
+ *   - Every argument is validated before anything is enqueued.  On any error
+ *     nothing is enqueued and outputs are untouched.  Device pointers must be
+ *     16-byte aligned (VSA_ERR_ALIGN).  Limits: B, H, T, Hh, Ww >= 1;
+ *     cube = 4x4x4 (else VSA_ERR_UNSUPPORTED); d in {64, 128}
+ *     (else VSA_ERR_UNSUPPORTED); 1 <= topk <= C (else VSA_ERR_SHAPE);
+ *     C <= 8192 and B*H*Np*d < 2^62 (else VSA_ERR_UNSUPPORTED).
+ *   - A kernel launch failure is reported as VSA_ERR_LAUNCH.
+ *   - Offsets are 64-bit throughout.
+ */
+#ifndef VSA_H_
+#define VSA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  VSA_OK = 0,
+  VSA_ERR_NULL = 1,         /* a required pointer is NULL                       */
+  VSA_ERR_SHAPE = 2,        /* a dimension is < 1 or topk is outside [1, C]      */
+  VSA_ERR_UNSUPPORTED = 3,  /* valid but not implemented: d, cube size, dtype    */
+  VSA_ERR_ALIGN = 4,        /* a device pointer is not 16-byte aligned           */
+  VSA_ERR_WORKSPACE = 5,    /* workspace smaller than vsa_workspace_bytes()      */
+  VSA_ERR_LAUNCH = 6        /* the HIP runtime rejected a kernel launch          */
+} vsa_status;
+
+typedef enum { VSA_F32 = 0, VSA_BF16 = 1 } vsa_dtype;
+
+typedef struct {
+  int32_t B, H;              /* batch, heads                                     */
+  int32_t T, Hh, Ww;         /* token grid; N = T*Hh*Ww                          */
+  int32_t d;                 /* head dimension: 64 or 128                        */
+  int32_t cube_t, cube_h, cube_w;  /* cube edge per axis; must be 4, 4, 4      */
+  int32_t topk;              /* key cubes kept per query cube, 1 <= topk <= C    */
+  int32_t dtype;             /* vsa_dtype of q, k, v and of every output tensor  */
+} vsa_problem;
+
+enum { VSA_OP_FORWARD = 0, VSA_OP_BACKWARD = 1, VSA_OP_COARSE = 2, VSA_OP_FINE = 3 };
+
+/* Bytes of device workspace the entry point `op` needs for problem `p`
+ * (VSA_OP_FORWARD: vsa_forward, VSA_OP_BACKWARD: vsa_backward,
+ * VSA_OP_COARSE: vsa_coarse, VSA_OP_FINE: vsa_fine).  Returns 0 if `p` is
+ * invalid (see vsa_check_problem) or `op` unknown; a valid problem may also
+ * need 0 bytes (then ws may be NULL).  Host-only, never touches the GPU. */
+size_t vsa_workspace_bytes(const vsa_problem* p, int op);
+
+/* Validates `p` alone (host-only).  Returns the status every entry point
+ * would return for this problem with valid pointers. */
+vsa_status vsa_check_problem(const vsa_problem* p);
+
+/* Cube reorder (the 64-token blocks of the results section, laid out as 4x4x4
+ * cubes).
+ *   inverse = 0: x raster [B,H,N,d] -> y cube order [B,H,Np,d]; pad slots of
+ *                y are written as zero.
+ *   inverse = 1: x cube order [B,H,Np,d] -> y raster [B,H,N,d]; pad slots of
+ *                x are ignored.
+ * A pure permutation: bit-exact.  x and y must not overlap. */
+vsa_status vsa_reorder(const vsa_problem* p, const void* x, void* y, int inverse,
+                       hipStream_t stream);
+
+/* Coarse stage on cube-order inputs (block pattern producer of the results
+ * section, Fig. 5).
+ *   qcube, kcube, vcube : [B,H,Np,d] cube order, pad slots ignored.
+ *   o_coarse            : [B,H,C,d] out, softmax_row(Sc) Vc per query cube.
+ *   idx                 : [B,H,C,topk] int32 out, ascending cube indices.
+ *   scores              : [B,H,C,C] fp32 out (Sc), or NULL to skip.
+ *   ws, ws_bytes        : workspace of vsa_workspace_bytes(p, VSA_OP_COARSE).
+ * Means, scores, softmax and O_coarse are computed in fp32; the selection
+ * compares fp32 scores exactly (-0 equals +0). */
+vsa_status vsa_coarse(const vsa_problem* p, const void* qcube, const void* kcube,
+                      const void* vcube, void* o_coarse, int32_t* idx, float* scores,
+                      void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Fine stage on cube-order inputs (the fine block-sparse kernel of the
+ * results section).
+ *   qcube, kcube, vcube : [B,H,Np,d] cube order; pad slots of kcube/vcube are
+ *                         never attended to.
+ *   idx                 : [B,H,C,topk] int32, each in [0, C), distinct per row
+ *                         (any order; the result does not depend on it).
+ *   o_fine              : [B,H,Np,d] out, cube order.  Rows of pad slots are
+ *                         written with unspecified values.
+ *   lse                 : [B,H,Np] fp32 out (natural log), or NULL.
+ *   ws, ws_bytes        : workspace of vsa_workspace_bytes(p, VSA_OP_FINE).
+ * bf16 inputs use bf16 MFMA with fp32 accumulation and fp32 softmax; fp32
+ * inputs are computed in fp32 throughout.  Entries of idx outside [0, C) are
+ * not checked on the device; they are the caller's error. */
+vsa_status vsa_fine(const vsa_problem* p, const void* qcube, const void* kcube,
+                    const void* vcube, const int32_t* idx, void* o_fine, float* lse,
+                    void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Whole forward on raster tensors: reorder + coarse + fine + inverse reorder
+ * (the drop-in for FlashAttention of the section on why sparse attention
+ * fails under distillation).
+ *   q, k, v   : [B,H,N,d] raster.
+ *   o_fine    : [B,H,N,d] out, raster.
+ *   o_coarse  : [B,H,N,d] out, raster; token r holds its cube's coarse row.
+ *   idx       : [B,H,C,topk] int32 out, ascending (as vsa_coarse).
+ *   lse       : [B,H,Np] fp32 out in cube order (for vsa_backward), or NULL.
+ *   ws        : vsa_workspace_bytes(p, VSA_OP_FORWARD) bytes. */
+vsa_status vsa_forward(const vsa_problem* p, const void* q, const void* k, const void* v,
+                       void* o_fine, void* o_coarse, int32_t* idx, float* lse,
+                       void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Backward of vsa_forward, the trainable path (VSA trains in place of
+ * FlashAttention, section on why sparse attention fails under
+ * distillation).  Gradients of  sum(o_fine*do_fine) + sum(o_coarse*do_coarse)
+ * w.r.t. q, k, v with the selection idx held constant:
+ *   fine:   P = exp(S - lse), D = rowsum(do_fine * o_fine),
+ *           dS = P * (do_fine V^T - D), dQ = dS K / sqrt(d),
+ *           dK = sum over query cubes selecting the key cube of dS^T Q / sqrt(d),
+ *           dV = the same sum of P^T do_fine;
+ *   coarse: dOc = sum of do_coarse over each cube's valid tokens,
+ *           dVc = Pc^T dOc, dSc = Pc * (dOc Vc^T - rowsum(.)),
+ *           dQc = dSc Kc / sqrt(d), dKc = dSc^T Qc / sqrt(d); every valid token
+ *           of a cube receives that cube's gradient divided by its valid count.
+ *   q, k, v, o_fine, do_fine, do_coarse : [B,H,N,d] raster (do_coarse may be
+ *           NULL, meaning zero); lse [B,H,Np] and idx as written by vsa_forward.
+ *   dq, dk, dv : [B,H,N,d] raster out (overwritten).
+ * Deterministic: no floating-point atomics; repeated calls give the same bits. */
+vsa_status vsa_backward(const vsa_problem* p, const void* q, const void* k, const void* v,
+                        const void* o_fine, const float* lse, const int32_t* idx,
+                        const void* do_fine, const void* do_coarse,
+                        void* dq, void* dk, void* dv,
+                        void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Static string naming a status. */
+const char* vsa_status_string(vsa_status s);
+
+#ifdef __cplusplus
+}  /* extern "C" */
+#endif
+#endif  /* VSA_H_ */

@@ -1,0 +1,165 @@
+"""GPU parity of the forward path (reorder, coarse, fine, whole forward) against
+the fp64 oracle, through the C ABI (ctypes binding)."""
+from dataclasses import replace
+
+import numpy as np
+import pytest
+import torch
+
+import block_sparse_attention_cube_amd as vsa
+from oracle import vsa_oracle as vo
+from parity import assert_close, check_idx
+from synth import configs, inputs
+from synth.configs import Workload
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+EDGE = [
+    Workload("ragged-bf16-d128", B=2, H=3, T=5, Hh=6, Ww=7, d=128, dtype="bf16", topk=3,
+             structure="offset", alpha=0.5),
+    Workload("ragged-f32-d128", B=1, H=2, T=6, Hh=5, Ww=9, d=128, dtype="f32", topk=4,
+             structure="offset", alpha=1.0),
+    Workload("ragged-bf16-d64", B=1, H=2, T=9, Hh=3, Ww=10, d=64, dtype="bf16", topk=2,
+             structure="field", alpha=0.5),
+    Workload("ragged-f32-d64", B=2, H=1, T=3, Hh=7, Ww=5, d=64, dtype="f32", topk=2,
+             structure="field", alpha=0.5),
+    Workload("one-token", B=1, H=2, T=1, Hh=1, Ww=1, d=128, dtype="bf16", topk=1,
+             structure="offset", alpha=0.5),
+    Workload("all-cubes", B=1, H=2, T=8, Hh=12, Ww=10, d=128, dtype="bf16", topk=18,
+             structure="field", alpha=0.5),
+    Workload("one-cube-each", B=1, H=2, T=8, Hh=12, Ww=10, d=64, dtype="bf16", topk=1,
+             structure="field", alpha=0.5),
+]
+SMALL = [configs.TINY_F32, configs.DIT_410M, configs.WAN_1_3B]
+CASES = SMALL + EDGE
+ids = lambda ws: [w.name for w in ws]
+
+
+def dev(x, w):
+    return inputs.as_torch(x, w.dtype, DEV)
+
+
+def host(t):
+    return t.float().cpu().numpy()
+
+
+def grid(w):
+    return (w.T, w.Hh, w.Ww)
+
+
+@pytest.fixture(scope="module")
+def cache():
+    return {}
+
+
+def case_data(w, cache):
+    """Inputs, GPU cube-order copies and the oracle forward, computed once per workload."""
+    if w.name not in cache:
+        x = inputs.make_inputs(w, seed=0)
+        q, k, v = (dev(x[n], w) for n in "qkv")
+        cube = tuple(vsa.reorder(t, grid(w)) for t in (q, k, v))
+        ref = vo.forward(x["q"], x["k"], x["v"], w.T, w.Hh, w.Ww, w.topk)
+        cache[w.name] = (x, (q, k, v), cube, ref)
+    return cache[w.name]
+
+
+@pytest.mark.parametrize("w", CASES, ids=ids(CASES))
+def test_reorder_is_bit_exact(w, cache):
+    x, (q, _, _), (qc, _, _), ref = case_data(w, cache)
+    g = ref["geometry"]
+    got = host(qc)
+    np.testing.assert_array_equal(got, vo.reorder(x["q"], g))
+    back = vsa.reorder(qc, grid(w), inverse=True)
+    assert torch.equal(back, q)
+
+
+@pytest.mark.parametrize("w", CASES, ids=ids(CASES))
+def test_coarse_scores_selection_and_output(w, cache):
+    x, _, (qc, kc, vc), ref = case_data(w, cache)
+    oc, idx, sc = vsa.coarse(qc, kc, vc, grid(w), w.topk, return_scores=True)
+    torch.cuda.synchronize()
+    sc = sc.cpu().numpy().astype(np.float64)
+    scale = max(1.0, float(np.abs(ref["scores"]).max()))
+    np.testing.assert_allclose(sc, ref["scores"], rtol=0, atol=2e-5 * scale)
+    check_idx(idx.cpu().numpy(), ref["idx"], ref["scores"], w.topk)
+    assert_close(host(oc), ref["oc"], w.dtype, "O_coarse per cube")
+
+
+@pytest.mark.parametrize("w", CASES, ids=ids(CASES))
+def test_fine_with_oracle_selection(w, cache):
+    x, _, (qc, kc, vc), ref = case_data(w, cache)
+    g = ref["geometry"]
+    idx = torch.from_numpy(ref["idx"]).to(DEV)
+    o, lse = vsa.fine(qc, kc, vc, idx, grid(w))
+    torch.cuda.synchronize()
+    assert_close(host(o), ref["o_fine_cube"], w.dtype, "O_fine (oracle idx)", rows=g["valid"])
+    lse_tol = 1e-4 if w.dtype == "f32" else 1e-3
+    got = lse.cpu().numpy()[..., g["valid"]]
+    np.testing.assert_allclose(got, ref["lse_cube"][..., g["valid"]], rtol=0, atol=lse_tol)
+
+
+@pytest.mark.parametrize("w", CASES, ids=ids(CASES))
+def test_fine_selection_order_does_not_matter(w, cache):
+    x, _, (qc, kc, vc), ref = case_data(w, cache)
+    g = ref["geometry"]
+    rng = np.random.default_rng(3)
+    perm = np.array([[[rng.permutation(r) for r in hh] for hh in bb] for bb in ref["idx"]])
+    o, _ = vsa.fine(qc, kc, vc, torch.from_numpy(perm.astype(np.int32)).to(DEV), grid(w))
+    assert_close(host(o), ref["o_fine_cube"], w.dtype, "O_fine (permuted idx)", rows=g["valid"])
+
+
+@pytest.mark.parametrize("w", CASES, ids=ids(CASES))
+def test_forward_end_to_end(w, cache):
+    x, (q, k, v), _, ref = case_data(w, cache)
+    o_fine, o_coarse, idx, lse = vsa.forward(q, k, v, grid(w), w.topk)
+    torch.cuda.synchronize()
+    gidx = idx.cpu().numpy()
+    near = check_idx(gidx, ref["idx"], ref["scores"], w.topk)
+    # judge the fine stage on the mask the GPU chose (identical unless near ties)
+    ref_g = ref if near == 0 else vo.forward(x["q"], x["k"], x["v"], w.T, w.Hh, w.Ww, w.topk,
+                                             idx=gidx)
+    assert_close(host(o_fine), ref_g["o_fine"], w.dtype, "O_fine raster")
+    assert_close(host(o_coarse), ref["o_coarse"], w.dtype, "O_coarse raster")
+    g = ref["geometry"]
+    lse_tol = 1e-4 if w.dtype == "f32" else 1e-3
+    np.testing.assert_allclose(lse.cpu().numpy()[..., g["valid"]],
+                               ref_g["lse_cube"][..., g["valid"]], rtol=0, atol=lse_tol)
+
+
+@pytest.mark.parametrize("w", [configs.WAN_1_3B, EDGE[0]], ids=ids([configs.WAN_1_3B, EDGE[0]]))
+def test_forward_is_deterministic(w, cache):
+    _, (q, k, v), _, _ = case_data(w, cache)
+    a = [t.clone() for t in vsa.forward(q, k, v, grid(w), w.topk)]
+    b = vsa.forward(q, k, v, grid(w), w.topk)
+    for s, t in zip(a, b):
+        assert torch.equal(s, t)
+
+
+def test_forward_wan14b_sampled():
+    """Wan-14B 720p shape at full size on the GPU; the oracle checks 4 sampled
+    heads (full coarse stage) and 16 query cubes of each of them."""
+    w = configs.WAN_14B
+    x = inputs.make_inputs(w, seed=0)
+    q, k, v = (dev(x[n], w) for n in "qkv")
+    o_fine, o_coarse, idx, lse = vsa.forward(q, k, v, grid(w), w.topk)
+    torch.cuda.synchronize()
+    heads, qcubes = inputs.sample_plan(w)
+    hs = torch.tensor(heads, device=DEV)
+    sub = {n: x[n][:, heads] for n in "qkv"}
+    del x
+    gidx = idx[:, hs].cpu().numpy()
+    ref = vo.forward(sub["q"], sub["k"], sub["v"], w.T, w.Hh, w.Ww, w.topk, qcubes=qcubes,
+                     idx=None)
+    check_idx(gidx, ref["idx"], ref["scores"], w.topk)
+    ref_g = vo.forward(sub["q"], sub["k"], sub["v"], w.T, w.Hh, w.Ww, w.topk, qcubes=qcubes,
+                       idx=gidx)
+    g = ref_g["geometry"]
+    pos = np.concatenate([np.arange(64 * c, 64 * c + 64) for c in qcubes])
+    pos = pos[g["valid"][pos]]
+    toks = g["token"][pos]
+    assert_close(host(o_fine[:, hs])[:, :, toks], ref_g["o_fine"][:, :, toks], w.dtype,
+                 "O_fine sampled")
+    assert_close(host(o_coarse[:, hs]), ref["o_coarse"], w.dtype, "O_coarse sampled heads")
+    np.testing.assert_allclose(lse[:, hs].cpu().numpy()[..., pos], ref_g["lse_cube"][..., pos],
+                               rtol=0, atol=1e-3)
