@@ -36,6 +36,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-reps", type=int, default=5)
+    ap.add_argument("--stage", choices=["all", "forward", "fine", "coarse", "reorder"],
+                    default="all",
+                    help="time one stage only (for profiler runs); prints a short JSON line")
     return ap.parse_args()
 
 
@@ -70,6 +73,27 @@ def cpu_baseline(w, x, reps):
                       f"{reps} repetitions, {dt:.1f} s total"}
 
 
+def stage_only(args, w, grid, sets, cube_sets, step):
+    import torch
+    import block_sparse_attention_cube_amd as vsa
+    n = len(sets)
+    if args.stage == "forward":
+        fn = step
+    elif args.stage == "reorder":
+        fn = lambda i: [vsa.reorder(sets[i][t], grid) for t in "qkv"]
+    else:
+        idx = [vsa.coarse(c["q"], c["k"], c["v"], grid, w.topk)[1] for c in cube_sets]
+        out = torch.empty_like(cube_sets[0]["q"])
+        if args.stage == "fine":
+            fn = lambda i: vsa.fine(cube_sets[i]["q"], cube_sets[i]["k"], cube_sets[i]["v"],
+                                    idx[i], grid, out=out)
+        else:
+            fn = lambda i: vsa.coarse(cube_sets[i]["q"], cube_sets[i]["k"], cube_sets[i]["v"],
+                                      grid, w.topk)
+    ms = timed(fn, args.steps, args.warmup, n)
+    print(json.dumps({"stage": args.stage, "ms": round(ms, 5), "steps": args.steps}), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -95,6 +119,9 @@ def main():
 
     plan = vsa.ForwardPlan(w.B, w.H, grid, w.d, w.topk, torch.bfloat16, dev)
     step = lambda i: plan.run(sets[i]["q"], sets[i]["k"], sets[i]["v"])
+    if args.stage != "all":
+        stage_only(args, w, grid, sets, cube_sets, step)
+        return
     ms = timed(step, args.steps, args.warmup, N_SETS)
     warm_ms = timed(lambda i: step(0), args.steps, args.warmup, 1)
 

@@ -9,8 +9,9 @@
 //      the fly from the LDS scores;
 //   4. top-K per row: the K-th largest score is found exactly by a 32-step
 //      bitwise search over order-preserving uint32 keys of the fp32 scores,
-//      then one ordered pass with wave ballots emits every index above it
-//      plus the lowest-index ties, already in ascending order.
+//      each step counting with 64-bit wave ballots (no shuffles); then one
+//      ordered pass with ballots emits every index above it plus the
+//      lowest-index ties, already in ascending order.
 // Everything is fp32 (no bf16 rounding of means or scores), so the selection
 // differs from an exact one only where two scores are within fp32 rounding.
 #include "vsa_internal.h"
@@ -30,11 +31,6 @@ __device__ inline float wave_sum(float x) {
   for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
   return x;
 }
-__device__ inline int wave_sum_int(int x) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
-  return x;
-}
 
 // Order-preserving key of an fp32 score: a > b  <=>  key(a) > key(b); -0 == +0.
 __device__ inline uint32_t score_key(float f) {
@@ -47,9 +43,9 @@ __device__ inline void store_out(float* p, float x) { *p = x; }
 __device__ inline void store_out(uint16_t* p, float x) { *p = f32_to_bf16_rne(x); }
 
 constexpr int kRows = 16;
-constexpr int kMaxKeysPerLane = kMaxCubes / 64;
 
-template <typename TOut, int D>
+// KPL: keys per lane in the top-K, ceil(C / 64) rounded up to a power of two.
+template <typename TOut, int D, int KPL>
 __global__ __launch_bounds__(256) void coarse_kernel(const float* __restrict__ qm,
                                                      const float* __restrict__ km,
                                                      const float* __restrict__ vm,
@@ -125,20 +121,28 @@ __global__ __launch_bounds__(256) void coarse_kernel(const float* __restrict__ q
   }
   __syncthreads();
 
-  // -- 3. O_coarse = P Vc: A[m=li][k=lg] = P[row li][j], B[k=lg][n=li] = Vc[j][col]
+  // -- 3. O_coarse = P Vc: A[m=li][k=lg] = P[row li][j], B[k=lg][n=li] = Vc[j][col].
+  // 16 loads of Vc are issued together before their 16 MFMAs.
   {
     const float mrow = rowmax[li], irow = rowinv[li];
     const float* prow = sc + li * ldc;
     for (int dt = wave; dt < D / 16; dt += 4) {
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      for (int j0 = 0; j0 < C; j0 += 16) {
+      for (int j0 = 0; j0 < C; j0 += 64) {
+        float a[16], b[16];
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const int j = j0 + 4 * lg + t;
-          const float a = (j < C) ? __expf(prow[j] - mrow) * irow : 0.f;
-          const float b = (j < C) ? vh[(int64_t)j * D + dt * 16 + li] : 0.f;
-          acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc, 0, 0, 0);
+        for (int u = 0; u < 16; ++u) {
+          const int j = j0 + 16 * (u >> 2) + 4 * lg + (u & 3);
+          b[u] = (j < C) ? vh[(int64_t)j * D + dt * 16 + li] : 0.f;
         }
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+          const int j = j0 + 16 * (u >> 2) + 4 * lg + (u & 3);
+          a[u] = (j < C) ? __expf(prow[j] - mrow) * irow : 0.f;
+        }
+#pragma unroll
+        for (int u = 0; u < 16; ++u)
+          acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[u], b[u], acc, 0, 0, 0);
       }
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
@@ -148,18 +152,18 @@ __global__ __launch_bounds__(256) void coarse_kernel(const float* __restrict__ q
     }
   }
 
-  // -- 4. top-K per row (one wave per row)
+  // -- 4. top-K per row (one wave per row).  Counting a predicate over the
+  // row is one 64-bit ballot plus a scalar popcount per 64 keys.
   const int K = g.K;
-  const int nk = (C + 63) / 64;
   const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   for (int rr = wave; rr < kRows; rr += 4) {
     if (row0 + rr >= C) break;
     const float* srow = sc + rr * ldc;
-    uint32_t key[kMaxKeysPerLane];
+    uint32_t key[KPL];
 #pragma unroll
-    for (int e = 0; e < kMaxKeysPerLane; ++e) {
+    for (int e = 0; e < KPL; ++e) {
       const int j = e * 64 + lane;
-      key[e] = (e < nk && j < C) ? score_key(srow[j]) : 0u;  // 0 is below every score key
+      key[e] = (j < C) ? score_key(srow[j]) : 0u;  // 0 is below every score key
     }
     // largest threshold t with #{key >= t} >= K, i.e. the K-th largest key
     uint32_t thr = 0u;
@@ -167,42 +171,38 @@ __global__ __launch_bounds__(256) void coarse_kernel(const float* __restrict__ q
       const uint32_t cand = thr | (1u << bit);
       int cnt = 0;
 #pragma unroll
-      for (int e = 0; e < kMaxKeysPerLane; ++e)
-        if (e < nk) cnt += (key[e] >= cand) ? 1 : 0;
-      if (wave_sum_int(cnt) >= K) thr = cand;
+      for (int e = 0; e < KPL; ++e) cnt += __popcll(__ballot(key[e] >= cand));
+      if (cnt >= K) thr = cand;
     }
     int gt = 0;
 #pragma unroll
-    for (int e = 0; e < kMaxKeysPerLane; ++e)
-      if (e < nk) gt += (key[e] > thr) ? 1 : 0;
-    const int need = K - wave_sum_int(gt);  // ties at the threshold to keep, lowest index first
+    for (int e = 0; e < KPL; ++e) gt += __popcll(__ballot(key[e] > thr));
+    const int need = K - gt;  // ties at the threshold to keep, lowest index first
     int ties_before = 0, sel_before = 0;
     int32_t* out = idx + (bh * C + row0 + rr) * K;
 #pragma unroll
-    for (int e = 0; e < kMaxKeysPerLane; ++e) {
-      if (e < nk) {  // uniform across the wave
-        const int j = e * 64 + lane;
-        const bool is_gt = (j < C) && key[e] > thr;
-        const bool is_eq = (j < C) && key[e] == thr;
-        const uint64_t eqm = __ballot(is_eq);
-        const int eq_rank = ties_before + __popcll(eqm & lt_mask);
-        const bool take = is_gt || (is_eq && eq_rank < need);
-        const uint64_t takem = __ballot(take);
-        if (take) out[sel_before + __popcll(takem & lt_mask)] = j;
-        ties_before += __popcll(eqm);
-        sel_before += __popcll(takem);
-      }
+    for (int e = 0; e < KPL; ++e) {
+      const int j = e * 64 + lane;
+      const bool is_gt = (j < C) && key[e] > thr;
+      const bool is_eq = (j < C) && key[e] == thr;
+      const uint64_t eqm = __ballot(is_eq);
+      const int eq_rank = ties_before + __popcll(eqm & lt_mask);
+      const bool take = is_gt || (is_eq && eq_rank < need);
+      const uint64_t takem = __ballot(take);
+      if (take) out[sel_before + __popcll(takem & lt_mask)] = j;
+      ties_before += __popcll(eqm);
+      sel_before += __popcll(takem);
     }
   }
 }
 
-template <typename TOut, int D>
-hipError_t launch_typed(const Geo& g, const float* qm, const float* km, const float* vm,
-                        void* oc, int32_t* idx, float* scores, hipStream_t s) {
+template <typename TOut, int D, int KPL>
+hipError_t launch_kpl(const Geo& g, const float* qm, const float* km, const float* vm, void* oc,
+                      int32_t* idx, float* scores, hipStream_t s) {
   const int ntile = (g.C + 15) / 16;
   const int ldc = ntile * 16 + 1;  // odd stride spreads a column over the LDS banks
   const size_t lds = (size_t)(kRows * ldc + 2 * kRows) * sizeof(float);
-  auto* kern = coarse_kernel<TOut, D>;
+  auto* kern = coarse_kernel<TOut, D, KPL>;
   if (lds > 65536) {
     const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                              hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -211,6 +211,19 @@ hipError_t launch_typed(const Geo& g, const float* qm, const float* km, const fl
   }
   return launch_kernel(kern, dim3(ntile, g.B * g.H), dim3(256), lds, s, qm, km, vm,
                        static_cast<TOut*>(oc), idx, scores, g, ldc);
+}
+
+template <typename TOut, int D>
+hipError_t launch_typed(const Geo& g, const float* qm, const float* km, const float* vm,
+                        void* oc, int32_t* idx, float* scores, hipStream_t s) {
+  static_assert(kMaxCubes <= 32 * 64, "top-K holds at most 32 keys per lane");
+  const int per_lane = (g.C + 63) / 64;
+  if (per_lane <= 1) return launch_kpl<TOut, D, 1>(g, qm, km, vm, oc, idx, scores, s);
+  if (per_lane <= 2) return launch_kpl<TOut, D, 2>(g, qm, km, vm, oc, idx, scores, s);
+  if (per_lane <= 4) return launch_kpl<TOut, D, 4>(g, qm, km, vm, oc, idx, scores, s);
+  if (per_lane <= 8) return launch_kpl<TOut, D, 8>(g, qm, km, vm, oc, idx, scores, s);
+  if (per_lane <= 16) return launch_kpl<TOut, D, 16>(g, qm, km, vm, oc, idx, scores, s);
+  return launch_kpl<TOut, D, 32>(g, qm, km, vm, oc, idx, scores, s);
 }
 
 }  // namespace

@@ -50,13 +50,29 @@ __device__ inline uint32_t pack_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2));  // RNE
 }
 
-// Lo/hi 16-bit halves of two words -> one word (a's half in the low bits).
-__device__ inline uint32_t lo_lo(uint32_t a, uint32_t b) { return (a & 0xffffu) | (b << 16); }
-__device__ inline uint32_t hi_hi(uint32_t a, uint32_t b) { return (a >> 16) | (b & 0xffff0000u); }
+// Halves of two words packed into one with v_perm_b32 (a's half in the low bits).
+__device__ inline uint32_t lo_lo(uint32_t a, uint32_t b) { return __builtin_amdgcn_perm(b, a, 0x05040100u); }
+__device__ inline uint32_t hi_hi(uint32_t a, uint32_t b) { return __builtin_amdgcn_perm(b, a, 0x07060302u); }
 
-// Register staging of one key cube: K rows copied as 16-byte chunks, V
-// transposed on the way into LDS (Vt[d][key]) so that PV can read 4
-// consecutive keys of one dim as a single 8-byte operand piece.
+// Column of key kappa inside a transposed V row.  Keys 32s + 16h + 4g + r go
+// to 32s + 8g + 4h + r, so the 8 keys one lane feeds to a PV MFMA k-step
+// ({32s + 4g + r} and {32s + 16 + 4g + r}, r = 0..3) sit in one 16-byte run.
+__device__ __host__ constexpr int vt_col(int kappa) {
+  return (kappa & ~31) | (((kappa >> 2) & 3) << 3) | (((kappa >> 4) & 1) << 2) | (kappa & 3);
+}
+
+// Shared-memory tile of one key cube: K [64][D] with 16-byte chunks XOR
+// swizzled by row, and V^T [D][64 (+8 pad)] with keys in vt_col order.
+template <int D>
+struct Tile {
+  static constexpr int kKElems = 64 * D;
+  static constexpr int kVtStride = 72;                 // 144 bytes: rows spread over banks
+  static constexpr int kElems = kKElems + D * kVtStride;
+};
+
+// Register staging of one key cube on its way from HBM/L2 into LDS.  K rows
+// are copied as 16-byte chunks; V is transposed: a thread holds 4 keys x 8
+// dims and writes 8 runs of 4 keys (one per dim).
 template <int D>
 struct KVStage {
   static constexpr int kKC = D / 8;             // 16-byte chunks per K row
@@ -68,8 +84,8 @@ struct KVStage {
 
   __device__ __forceinline__ void init(int t) {
     tid = t;
-    v_kg = t / (D / 8);   // 4-key group
-    v_dc = t % (D / 8);   // 8-dim chunk
+    v_kg = t % 16;   // 4-key group (consecutive lanes: consecutive groups)
+    v_dc = t / 16;   // 8-dim chunk
   }
   __device__ __forceinline__ void load(const uint16_t* __restrict__ k,
                                        const uint16_t* __restrict__ v, int64_t base) {
@@ -82,21 +98,24 @@ struct KVStage {
       for (int u = 0; u < 4; ++u) vreg[u] = *reinterpret_cast<const u32x4*>(vb + u * D);
     }
   }
-  __device__ __forceinline__ void store(uint16_t* k_lds, uint16_t* vt_lds) const {
+  __device__ __forceinline__ void store(uint16_t* tile) const {
+    uint16_t* k_lds = tile;
+    uint16_t* vt_lds = tile + Tile<D>::kKElems;
 #pragma unroll
     for (int u = 0; u < kKReg; ++u) {
       const int ch = tid + 256 * u, row = ch / kKC, c = ch % kKC;
       *reinterpret_cast<u32x4*>(k_lds + row * D + ((c ^ (row & (kKC - 1))) * 8)) = kreg[u];
     }
     if (tid < kVThreads) {
-      // vreg[u] = V[key 4kg+u][8dc .. 8dc+7]  ->  Vt[8dc+i][4kg .. 4kg+3]
+      // vreg[u] = V[key 4kg+u][8dc .. 8dc+7]  ->  Vt[8dc+i][vt_col(4kg) .. +3]
+      const int col = vt_col(4 * v_kg);
 #pragma unroll
       for (int h = 0; h < 4; ++h) {
-        const int d0 = 8 * v_dc + 2 * h, d1 = d0 + 1;
+        const int d0 = 8 * v_dc + 2 * h;
         const u32x2 lo = {lo_lo(vreg[0][h], vreg[1][h]), lo_lo(vreg[2][h], vreg[3][h])};
         const u32x2 hi = {hi_hi(vreg[0][h], vreg[1][h]), hi_hi(vreg[2][h], vreg[3][h])};
-        *reinterpret_cast<u32x2*>(vt_lds + d0 * 64 + ((v_kg ^ (d0 & 15)) * 4)) = lo;
-        *reinterpret_cast<u32x2*>(vt_lds + d1 * 64 + ((v_kg ^ (d1 & 15)) * 4)) = hi;
+        *reinterpret_cast<u32x2*>(vt_lds + d0 * Tile<D>::kVtStride + col) = lo;
+        *reinterpret_cast<u32x2*>(vt_lds + (d0 + 1) * Tile<D>::kVtStride + col) = hi;
       }
     }
   }
@@ -111,11 +130,13 @@ __global__ __launch_bounds__(256, 2) void fine_fwd_bf16_kernel(
   constexpr int kKC = D / 8;              // 16-byte chunks per K row
   constexpr int kKS = D / 32;             // k-steps of S^T = K Q^T
   constexpr int kDT = D / 16;             // 16-row tiles of O^T
-  constexpr int kKReg = 64 * kKC / 256;   // 16-byte output chunks per thread
+  constexpr int kOutReg = 64 * kKC / 256; // 16-byte output chunks per thread
   constexpr int kOS = D + 8;              // padded row stride of the O staging tile
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * 64 * D];
-  uint16_t* const k_lds = smem;           // [64 keys][D], 16-byte chunks swizzled
-  uint16_t* const vt_lds = smem + 64 * D; // [D][64 keys], 8-byte chunks swizzled
+  constexpr int kVS = Tile<D>::kVtStride;
+  // rescale the running output only when a row max grows by more than 2^8
+  // (in exp2 units): probabilities stay <= 256, exact after normalisation
+  constexpr float kTau = 8.0f;
+  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * Tile<D>::kElems];
 
   const int tile = xcd_remap(blockIdx.x, gridDim.x);
   const int64_t bh = tile / g.C;
@@ -125,6 +146,7 @@ __global__ __launch_bounds__(256, 2) void fine_fwd_bf16_kernel(
   const int K = g.K;
   const int32_t* __restrict__ sel = idx + static_cast<int64_t>(tile) * K;
   const float c2 = inv_sqrt_d<D>() * kLog2e;
+  const float tau_raw = kTau / c2;
 
   // Q fragment: B operand of S^T, lane holds Q[slot 16w+li][32ks + 8lg .. +7]
   u32x4 qf[kKS];
@@ -141,13 +163,18 @@ __global__ __launch_bounds__(256, 2) void fine_fwd_bf16_kernel(
   f32x4 oacc[kDT];
 #pragma unroll
   for (int dt = 0; dt < kDT; ++dt) oacc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY, l_run = 0.f;
+  f32x4 lacc = {0.f, 0.f, 0.f, 0.f};   // row sums of P, by MFMA against ones
+  const u32x4 ones = {0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u};  // bf16 1.0 x 8
+  float m_run = -INFINITY;
 
   st.load(k, v, (bh * g.Np + static_cast<int64_t>(sel[0]) * 64) * D);
-  st.store(k_lds, vt_lds);
+  st.store(smem);
   __syncthreads();
 
   for (int n = 0; n < K; ++n) {
+    const uint16_t* const cur = smem + (n & 1) * Tile<D>::kElems;
+    const uint16_t* const k_lds = cur;
+    const uint16_t* const vt_lds = cur + Tile<D>::kKElems;
     const int j = sel[n];
     const bool has_next = n + 1 < K;
     if (has_next) st.load(k, v, (bh * g.Np + static_cast<int64_t>(sel[n + 1]) * 64) * D);
@@ -156,15 +183,15 @@ __global__ __launch_bounds__(256, 2) void fine_fwd_bf16_kernel(
     f32x4 sacc[4];
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
-      sacc[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
       const int row = 16 * kb + li;
 #pragma unroll
       for (int ks = 0; ks < kKS; ++ks) {
         const int c = 4 * ks + lg;
         const u32x4 kf =
             *reinterpret_cast<const u32x4*>(k_lds + row * D + ((c ^ (row & (kKC - 1))) * 8));
-        sacc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kf), as_bf16x8(qf[ks]),
-                                                           sacc[kb], 0, 0, 0);
+        sacc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            as_bf16x8(kf), as_bf16x8(qf[ks]),
+            ks == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : sacc[kb], 0, 0, 0);
       }
     }
 
@@ -178,65 +205,55 @@ __global__ __launch_bounds__(256, 2) void fine_fwd_bf16_kernel(
           if (kb >= e.nt || lg >= e.nh || r >= e.nw) sacc[kb][r] = -INFINITY;
     }
 
-    // online softmax (row q = li; the 4 lanes li, li+16, li+32, li+48 share it)
-    float mloc = -INFINITY;
+    // online softmax for row q = li (lanes li, li+16, li+32, li+48 share it)
+    float mloc = fmaxf(fmaxf(sacc[0][0], sacc[0][1]), fmaxf(sacc[0][2], sacc[0][3]));
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) mloc = fmaxf(mloc, sacc[kb][r]);
+    for (int kb = 1; kb < 4; ++kb)
+      mloc = fmaxf(mloc, fmaxf(fmaxf(sacc[kb][0], sacc[kb][1]), fmaxf(sacc[kb][2], sacc[kb][3])));
     mloc = fmaxf(mloc, __shfl_xor(mloc, 16));
     mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
-    const float m_new = fmaxf(m_run, mloc);
-    const float alpha = exp2f((m_run - m_new) * c2);
-    const float mb = m_new * c2;
-    float p[4][4];
-    float psum = 0.f;
+    const bool grow = mloc > m_run + tau_raw;
+    if (__ballot(grow) != 0ull) {   // wave-uniform: rare after the first block
+      const float m_new = grow ? mloc : m_run;
+      const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c2);
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        p[kb][r] = exp2f(fmaf(sacc[kb][r], c2, -mb));
-        psum += p[kb][r];
-      }
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
-#pragma unroll
-    for (int dt = 0; dt < kDT; ++dt) oacc[dt] *= alpha;
+      for (int dt = 0; dt < kDT; ++dt) oacc[dt] *= alpha;
+      lacc *= alpha;
+      m_run = m_new;
+    }
+    const float mb = m_run * c2;
 
     // P^T as B operand: k-step s covers keys 32s + 16(i/4) + 4lg + (i%4)
-    bf16x8 pf[2];
+    u32x4 pf[2];
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
-      const u32x4 u = {pack_bf16x2(p[2 * s][0], p[2 * s][1]),
-                       pack_bf16x2(p[2 * s][2], p[2 * s][3]),
-                       pack_bf16x2(p[2 * s + 1][0], p[2 * s + 1][1]),
-                       pack_bf16x2(p[2 * s + 1][2], p[2 * s + 1][3])};
-      pf[s] = as_bf16x8(u);
+      float p[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        p[i] = __builtin_amdgcn_exp2f(fmaf(sacc[2 * s + (i >> 2)][i & 3], c2, -mb));
+      pf[s] = u32x4{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
+                    pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7])};
     }
     // O^T[d][q] += V^T[d][keys] P^T[keys][q]; A lane holds Vt[16dt+li][same keys]
 #pragma unroll
-    for (int dt = 0; dt < kDT; ++dt) {
-      const int d = 16 * dt + li;
+    for (int s = 0; s < 2; ++s) {
+      lacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ones), as_bf16x8(pf[s]), lacc,
+                                                     0, 0, 0);
 #pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        const u32x2 a0 = *reinterpret_cast<const u32x2*>(vt_lds + d * 64 + (((8 * s + lg) ^ li) * 4));
-        const u32x2 a1 =
-            *reinterpret_cast<const u32x2*>(vt_lds + d * 64 + (((8 * s + 4 + lg) ^ li) * 4));
-        const u32x4 a = {a0.x, a0.y, a1.x, a1.y};
-        oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), pf[s], oacc[dt], 0, 0, 0);
+      for (int dt = 0; dt < kDT; ++dt) {
+        const u32x4 a =
+            *reinterpret_cast<const u32x4*>(vt_lds + (16 * dt + li) * kVS + 32 * s + 8 * lg);
+        oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(pf[s]),
+                                                           oacc[dt], 0, 0, 0);
       }
     }
 
+    if (has_next) st.store(smem + ((n + 1) & 1) * Tile<D>::kElems);
     __syncthreads();
-    if (has_next) {
-      st.store(k_lds, vt_lds);
-      __syncthreads();
-    }
   }
 
-  // ---- epilogue
-  float l = l_run + __shfl_xor(l_run, 16);
-  l += __shfl_xor(l, 32);
+  // ---- epilogue: l is the same in every accumulator row of lacc
+  const float l = lacc[0];
   const float inv = 1.f / l;
   if (lse != nullptr && lg == 0)
     lse[bh * g.Np + static_cast<int64_t>(qc) * 64 + wave * 16 + li] = (m_run * c2 + log2f(l)) * kLn2;
@@ -252,7 +269,7 @@ __global__ __launch_bounds__(256, 2) void fine_fwd_bf16_kernel(
   __syncthreads();
   const CubeExt eq = cube_extent(g, qc);
 #pragma unroll
-  for (int u = 0; u < kKReg; ++u) {
+  for (int u = 0; u < kOutReg; ++u) {
     const int ch = tid + 256 * u, row = ch / kKC, c = ch % kKC;
     const u32x4 val = *reinterpret_cast<const u32x4*>(o_lds + row * kOS + 8 * c);
     if (RASTER) {
