@@ -15,6 +15,7 @@
 // Everything is fp32 (no bf16 rounding of means or scores), so the selection
 // differs from an exact one only where two scores are within fp32 rounding.
 #include "vsa_internal.h"
+#include "vsa_bwd.h"
 
 namespace vsa {
 namespace {
@@ -226,6 +227,179 @@ hipError_t launch_typed(const Geo& g, const float* qm, const float* km, const fl
   return launch_kpl<TOut, D, 32>(g, qm, km, vm, oc, idx, scores, s);
 }
 
+// ---------------------------------------------------------------------------
+// Backward of the coarse stage.  With Pc = softmax(Sc), Sc = Qc Kc^T / sqrt(D)
+// and dOc the per-cube sums of dO_coarse:
+//   dPc = dOc Vc^T,  dSc = Pc * (dPc - rowsum(Pc * dPc)),
+//   dQc = dSc Kc / sqrt(D),  dKc = dSc^T Qc / sqrt(D),  dVc = Pc^T dOc.
+// Row pass (16 query cubes per workgroup): dQc and the per-row statistics.
+// Column pass (16 key cubes per workgroup): dKc and dVc, recomputing Pc and
+// dSc column-wise from those statistics.  Both are deterministic.
+
+// out[r][j] = scale * dot(A[r], B[j]) for the 16 rows r of A starting at a0
+// (rows >= C read as zero) and every j < C, into LDS with row stride ldc.
+template <int D>
+__device__ __forceinline__ void rows_dot(const float* __restrict__ A, int a0,
+                                         const float* __restrict__ B, int C, float scale,
+                                         float* out, int ldc, int wave, int lane) {
+  const int li = lane & 15, lg = lane >> 4;
+  float4 af[D / 16];
+  const int r = a0 + li;
+#pragma unroll
+  for (int kk = 0; kk < D / 16; ++kk)
+    af[kk] = (r < C) ? *reinterpret_cast<const float4*>(A + (int64_t)r * D + 16 * kk + 4 * lg)
+                     : make_float4(0.f, 0.f, 0.f, 0.f);
+  const int ntile = (C + 15) / 16;
+  for (int ct = wave; ct < ntile; ct += 4) {
+    const int col = ct * 16 + li;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) {
+      const float4 bf = (col < C)
+          ? *reinterpret_cast<const float4*>(B + (int64_t)col * D + 16 * kk + 4 * lg)
+          : make_float4(0.f, 0.f, 0.f, 0.f);
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(af[kk].x, bf.x, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(af[kk].y, bf.y, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(af[kk].z, bf.z, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(af[kk].w, bf.w, acc, 0, 0, 0);
+    }
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) out[(4 * lg + rr) * ldc + col] = acc[rr] * scale;
+  }
+}
+
+// y[r][:] = scale * sum_j T[r][j] Y[j][:] for the 16 LDS rows of T, stored to
+// out rows o0 + r (< C) of an fp32 [C][D] matrix.
+template <int D>
+__device__ __forceinline__ void lds_times(const float* T, int ldc, const float* __restrict__ Y,
+                                          int C, float scale, float* __restrict__ out, int o0,
+                                          int wave, int lane) {
+  const int li = lane & 15, lg = lane >> 4;
+  const float* trow = T + li * ldc;
+  for (int dt = wave; dt < D / 16; dt += 4) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int j0 = 0; j0 < C; j0 += 64) {
+      float a[16], b[16];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        const int j = j0 + 16 * (u >> 2) + 4 * lg + (u & 3);
+        b[u] = (j < C) ? Y[(int64_t)j * D + dt * 16 + li] : 0.f;
+        a[u] = (j < C) ? trow[j] : 0.f;
+      }
+#pragma unroll
+      for (int u = 0; u < 16; ++u)
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[u], b[u], acc, 0, 0, 0);
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int row = o0 + 4 * lg + r;
+      if (row < C) out[(int64_t)row * D + dt * 16 + li] = acc[r] * scale;
+    }
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void coarse_bwd_rows_kernel(
+    const float* __restrict__ qm, const float* __restrict__ km, const float* __restrict__ vm,
+    const float* __restrict__ docs, float* __restrict__ stats, float* __restrict__ dqc, Geo g,
+    int ldc) {
+  extern __shared__ float lds[];
+  float* s1 = lds;                 // scores, then probabilities
+  float* s2 = lds + kRows * ldc;   // dPc, then dSc
+  constexpr float kScale = (D == 64) ? 0.125f : 0.08838834764831845f;
+  const int C = g.C;
+  const int64_t bh = blockIdx.y;
+  const int row0 = blockIdx.x * kRows;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t hoff = bh * C * D;
+  rows_dot<D>(qm + hoff, row0, km + hoff, C, kScale, s1, ldc, wave, lane);
+  rows_dot<D>(docs + hoff, row0, vm + hoff, C, 1.f, s2, ldc, wave, lane);
+  __syncthreads();
+  for (int rr = wave; rr < kRows; rr += 4) {
+    float* p = s1 + rr * ldc;
+    float* dp = s2 + rr * ldc;
+    float m = -INFINITY;
+    for (int j = lane; j < C; j += 64) m = fmaxf(m, p[j]);
+    m = wave_max(m);
+    float l = 0.f;
+    for (int j = lane; j < C; j += 64) l += __expf(p[j] - m);
+    l = wave_sum(l);
+    const float inv = 1.f / l;
+    float r = 0.f;
+    for (int j = lane; j < C; j += 64) {
+      const float pj = __expf(p[j] - m) * inv;
+      p[j] = pj;
+      r += pj * dp[j];
+    }
+    r = wave_sum(r);
+    for (int j = lane; j < C; j += 64) dp[j] = p[j] * (dp[j] - r);
+    if (lane == 0 && row0 + rr < C) {
+      const int64_t at = bh * C + row0 + rr;
+      stats[at] = m;
+      stats[(int64_t)g.B * g.H * C + at] = l;
+      stats[2 * (int64_t)g.B * g.H * C + at] = r;
+    }
+  }
+  __syncthreads();
+  lds_times<D>(s2, ldc, km + hoff, C, kScale, dqc + hoff, row0, wave, lane);
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void coarse_bwd_cols_kernel(
+    const float* __restrict__ qm, const float* __restrict__ km, const float* __restrict__ vm,
+    const float* __restrict__ docs, const float* __restrict__ stats, float* __restrict__ dkc,
+    float* __restrict__ dvc, Geo g, int ldc) {
+  extern __shared__ float lds[];
+  float* t1 = lds;                 // Sc^T rows (16 key cubes x C query cubes), then Pc^T
+  float* t2 = lds + kRows * ldc;   // dPc^T, then dSc^T
+  constexpr float kScale = (D == 64) ? 0.125f : 0.08838834764831845f;
+  const int C = g.C;
+  const int64_t bh = blockIdx.y;
+  const int col0 = blockIdx.x * kRows;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t hoff = bh * C * D;
+  rows_dot<D>(km + hoff, col0, qm + hoff, C, kScale, t1, ldc, wave, lane);
+  rows_dot<D>(vm + hoff, col0, docs + hoff, C, 1.f, t2, ldc, wave, lane);
+  __syncthreads();
+  const int64_t plane = (int64_t)g.B * g.H * C;
+  const float* sm = stats + bh * C;
+  const float* sl = sm + plane;
+  const float* sr = sm + 2 * plane;
+  for (int e = threadIdx.x; e < kRows * C; e += 256) {
+    const int jj = e / C, i = e % C;
+    const float p = __expf(t1[jj * ldc + i] - sm[i]) / sl[i];
+    t1[jj * ldc + i] = p;
+    t2[jj * ldc + i] = p * (t2[jj * ldc + i] - sr[i]);
+  }
+  __syncthreads();
+  lds_times<D>(t2, ldc, qm + hoff, C, kScale, dkc + hoff, col0, wave, lane);
+  lds_times<D>(t1, ldc, docs + hoff, C, 1.f, dvc + hoff, col0, wave, lane);
+}
+
+template <int D>
+hipError_t launch_coarse_bwd_typed(const Geo& g, const float* qm, const float* km,
+                                   const float* vm, const float* docs, float* stats,
+                                   float* dqc, float* dkc, float* dvc, hipStream_t s) {
+  const int ntile = (g.C + 15) / 16;
+  const int ldc = ntile * 16 + 1;
+  const size_t lds = (size_t)(2 * kRows * ldc) * sizeof(float);
+  auto* rows = coarse_bwd_rows_kernel<D>;
+  auto* cols = coarse_bwd_cols_kernel<D>;
+  if (lds > 65536) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(rows),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e == hipSuccess)
+      e = hipFuncSetAttribute(reinterpret_cast<const void*>(cols),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+  }
+  const dim3 grid(ntile, g.B * g.H), block(256);
+  hipError_t e = launch_kernel(rows, grid, block, lds, s, qm, km, vm, docs, stats, dqc, g, ldc);
+  if (e != hipSuccess) return e;
+  return launch_kernel(cols, grid, block, lds, s, qm, km, vm, docs,
+                       static_cast<const float*>(stats), dkc, dvc, g, ldc);
+}
+
 }  // namespace
 
 hipError_t launch_coarse(const Geo& g, int dtype, const float* qm, const float* km,
@@ -236,6 +410,18 @@ hipError_t launch_coarse(const Geo& g, int dtype, const float* qm, const float* 
                       : launch_typed<uint16_t, 64>(g, qm, km, vm, oc, idx, scores, s);
   return g.D == 128 ? launch_typed<float, 128>(g, qm, km, vm, oc, idx, scores, s)
                     : launch_typed<float, 64>(g, qm, km, vm, oc, idx, scores, s);
+}
+
+}  // namespace vsa
+
+namespace vsa {
+
+hipError_t launch_coarse_bwd(const Geo& g, const float* qm, const float* km, const float* vm,
+                             const float* docs, float* stats, float* dqc, float* dkc,
+                             float* dvc, hipStream_t s) {
+  return g.D == 128
+             ? launch_coarse_bwd_typed<128>(g, qm, km, vm, docs, stats, dqc, dkc, dvc, s)
+             : launch_coarse_bwd_typed<64>(g, qm, km, vm, docs, stats, dqc, dkc, dvc, s);
 }
 
 }  // namespace vsa

@@ -3,6 +3,7 @@
 // nothing is enqueued until every argument has been checked.
 #include "../../include/vsa.h"
 #include "vsa_internal.h"
+#include "vsa_bwd.h"
 
 #include <initializer_list>
 
@@ -77,6 +78,49 @@ FwdWs carve_forward(const vsa_problem* p, void* ws, size_t* total) {
   return w;
 }
 
+struct BwdWs {
+  uint16_t* qc; uint16_t* kc; uint16_t* vc; uint16_t* dofc;
+  float* delta;
+  float* qm; float* km; float* vm; float* docs;
+  float* stats;
+  float* dqc; float* dkc; float* dvc;
+  int32_t* offsets; int32_t* list;
+};
+BwdWs carve_backward(const vsa_problem* p, void* ws, size_t* total) {
+  const Geo g = geometry(p);
+  const size_t bh = size_t(g.B) * g.H;
+  const size_t cube = bh * g.Np * g.D * sizeof(uint16_t);
+  const size_t mean = bh * g.C * g.D * sizeof(float);
+  Carver c(ws);
+  BwdWs w;
+  w.qc = static_cast<uint16_t*>(c.take(cube));
+  w.kc = static_cast<uint16_t*>(c.take(cube));
+  w.vc = static_cast<uint16_t*>(c.take(cube));
+  w.dofc = static_cast<uint16_t*>(c.take(cube));
+  w.delta = static_cast<float*>(c.take(bh * g.Np * sizeof(float)));
+  w.qm = static_cast<float*>(c.take(mean));
+  w.km = static_cast<float*>(c.take(mean));
+  w.vm = static_cast<float*>(c.take(mean));
+  w.docs = static_cast<float*>(c.take(mean));
+  w.stats = static_cast<float*>(c.take(3 * bh * g.C * sizeof(float)));
+  w.dqc = static_cast<float*>(c.take(mean));
+  w.dkc = static_cast<float*>(c.take(mean));
+  w.dvc = static_cast<float*>(c.take(mean));
+  w.offsets = static_cast<int32_t*>(c.take(bh * (g.C + 1) * sizeof(int32_t)));
+  w.list = static_cast<int32_t*>(c.take(bh * size_t(g.C) * g.K * sizeof(int32_t)));
+  if (total) *total = c.off;
+  return w;
+}
+
+// The backward keeps two 16 x C fp32 score tiles of the coarse stage in LDS.
+vsa_status check_backward(const vsa_problem* p) {
+  const vsa_status st = check(p);
+  if (st != VSA_OK) return st;
+  if (p->dtype != VSA_BF16) return VSA_ERR_UNSUPPORTED;
+  if (geometry(p).C > vsa::kMaxCubesBackward) return VSA_ERR_UNSUPPORTED;
+  return VSA_OK;
+}
+
 struct CoarseWs { float* qm; float* km; float* vm; };
 CoarseWs carve_coarse(const vsa_problem* p, void* ws, size_t* total) {
   const Geo g = geometry(p);
@@ -127,7 +171,10 @@ size_t vsa_workspace_bytes(const vsa_problem* p, int op) {
     case VSA_OP_FORWARD: carve_forward(p, nullptr, &total); return total;
     case VSA_OP_COARSE: carve_coarse(p, nullptr, &total); return total;
     case VSA_OP_FINE: return 0;
-    case VSA_OP_BACKWARD: return 0;
+    case VSA_OP_BACKWARD:
+      if (check_backward(p) != VSA_OK) return 0;
+      carve_backward(p, nullptr, &total);
+      return total;
     default: return 0;
   }
 }
@@ -221,9 +268,37 @@ vsa_status vsa_backward(const vsa_problem* p, const void* q, const void* k, cons
   if (st != VSA_OK) return st;
   if ((st = pointers({q, k, v, o_fine, lse, idx, do_fine, dq, dk, dv}, {do_coarse})) != VSA_OK)
     return st;
+  if ((st = check_backward(p)) != VSA_OK) return st;
   if ((st = workspace(p, VSA_OP_BACKWARD, ws, ws_bytes)) != VSA_OK) return st;
-  (void)stream;
-  return VSA_ERR_UNSUPPORTED;
+  const Geo g = geometry(p);
+  const BwdWs w = carve_backward(p, ws, nullptr);
+  auto b16 = [](const void* x) { return static_cast<const uint16_t*>(x); };
+  vsa::BwdPrepArgs pa;
+  pa.q = b16(q); pa.k = b16(k); pa.v = b16(v);
+  pa.dof = b16(do_fine); pa.o = b16(o_fine); pa.doc = b16(do_coarse);
+  pa.qc = w.qc; pa.kc = w.kc; pa.vc = w.vc; pa.dofc = w.dofc;
+  pa.delta = w.delta;
+  pa.qm = w.qm; pa.km = w.km; pa.vm = w.vm; pa.docs = w.docs;
+  hipError_t e = vsa::launch_bwd_prep(g, pa, stream);
+  const bool coarse = do_coarse != nullptr;
+  if (e == hipSuccess && coarse)
+    e = vsa::launch_coarse_bwd(g, w.qm, w.km, w.vm, w.docs, w.stats, w.dqc, w.dkc, w.dvc,
+                               stream);
+  if (e == hipSuccess) e = vsa::launch_idx_transpose(g, idx, w.offsets, w.list, stream);
+  if (e == hipSuccess) {
+    vsa::BwdFineArgs fa;
+    fa.qc = w.qc; fa.kc = w.kc; fa.vc = w.vc; fa.dofc = w.dofc;
+    fa.lse = lse; fa.delta = w.delta; fa.idx = idx;
+    fa.offsets = w.offsets; fa.list = w.list;
+    fa.dqc = coarse ? w.dqc : nullptr;
+    fa.dkc = coarse ? w.dkc : nullptr;
+    fa.dvc = coarse ? w.dvc : nullptr;
+    fa.dq = static_cast<uint16_t*>(dq);
+    fa.dk = static_cast<uint16_t*>(dk);
+    fa.dv = static_cast<uint16_t*>(dv);
+    e = vsa::launch_bwd_fine(g, fa, stream);
+  }
+  return launched(e);
 }
 
 }  // extern "C"

@@ -1,0 +1,42 @@
+// Internal declarations of the backward kernels (not installed).
+#pragma once
+
+#include "vsa_internal.h"
+
+namespace vsa {
+
+// Preparation pass over raster tensors (bf16).
+struct BwdPrepArgs {
+  const uint16_t* q; const uint16_t* k; const uint16_t* v;
+  const uint16_t* dof;   // upstream gradient of O_fine
+  const uint16_t* o;     // O_fine
+  const uint16_t* doc;   // upstream gradient of O_coarse, or nullptr (zero)
+  uint16_t* qc; uint16_t* kc; uint16_t* vc; uint16_t* dofc;   // cube order out
+  float* delta;          // [B,H,Np] rowsum(dO * O), 0 on pad slots
+  float* qm; float* km; float* vm;   // [B,H,C,D] means over valid slots
+  float* docs;           // [B,H,C,D] sums of dO_coarse over valid slots
+};
+hipError_t launch_bwd_prep(const Geo& g, const BwdPrepArgs& a, hipStream_t s);
+
+// Coarse-stage gradients from the means (fp32): dqc/dkc/dvc [B,H,C,D] and row
+// statistics stats [3][B,H,C] (row max, row sum of exp, rowsum(P * dP)).
+hipError_t launch_coarse_bwd(const Geo& g, const float* qm, const float* km, const float* vm,
+                             const float* docs, float* stats, float* dqc, float* dkc,
+                             float* dvc, hipStream_t s);
+
+// offsets [B,H,C+1], list [B,H,C*K]: query cubes selecting each key cube.
+hipError_t launch_idx_transpose(const Geo& g, const int32_t* idx, int32_t* offsets,
+                                int32_t* list, hipStream_t s);
+
+struct BwdFineArgs {
+  const uint16_t* qc; const uint16_t* kc; const uint16_t* vc; const uint16_t* dofc;
+  const float* lse;      // [B,H,Np] natural log
+  const float* delta;    // [B,H,Np]
+  const int32_t* idx;    // [B,H,C,K]
+  const int32_t* offsets; const int32_t* list;
+  const float* dqc; const float* dkc; const float* dvc;   // coarse gradients or nullptr
+  uint16_t* dq; uint16_t* dk; uint16_t* dv;               // raster out
+};
+hipError_t launch_bwd_fine(const Geo& g, const BwdFineArgs& a, hipStream_t s);
+
+}  // namespace vsa

@@ -12,6 +12,7 @@ namespace vsa {
 constexpr int kCube = 4;     // cube edge along each of (t, y, x)
 constexpr int kSlots = 64;   // tokens per cube
 constexpr int kMaxCubes = 2048;  // coarse score rows are staged in LDS: 16 x C fp32
+constexpr int kMaxCubesBackward = 1216;  // backward keeps two such tiles in LDS
 
 // Geometry of one problem, passed by value to every kernel.
 struct Geo {

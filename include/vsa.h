@@ -44,7 +44,8 @@
  *     16-byte aligned (VSA_ERR_ALIGN).  Limits: B, H, T, Hh, Ww >= 1;
  *     cube = 4x4x4 (else VSA_ERR_UNSUPPORTED); d in {64, 128}
  *     (else VSA_ERR_UNSUPPORTED); 1 <= topk <= C (else VSA_ERR_SHAPE);
- *     C <= 8192 and B*H*Np*d < 2^62 (else VSA_ERR_UNSUPPORTED).
+ *     C <= 2048 cubes, B*H <= 65535 and B*H*Np*d < 2^58 (else
+ *     VSA_ERR_UNSUPPORTED).
  *   - A kernel launch failure is reported as VSA_ERR_LAUNCH.
  *   - Offsets are 64-bit throughout.
  */
@@ -161,7 +162,9 @@ vsa_status vsa_forward(const vsa_problem* p, const void* q, const void* k, const
  *   q, k, v, o_fine, do_fine, do_coarse : [B,H,N,d] raster (do_coarse may be
  *           NULL, meaning zero); lse [B,H,Np] and idx as written by vsa_forward.
  *   dq, dk, dv : [B,H,N,d] raster out (overwritten).
- * Deterministic: no floating-point atomics; repeated calls give the same bits. */
+ * Deterministic: no floating-point atomics; repeated calls give the same bits.
+ * Implemented for VSA_BF16 with C <= 1216 cubes; other problems return
+ * VSA_ERR_UNSUPPORTED before anything is enqueued. */
 vsa_status vsa_backward(const vsa_problem* p, const void* q, const void* k, const void* v,
                         const void* o_fine, const float* lse, const int32_t* idx,
                         const void* do_fine, const void* do_coarse,
