@@ -36,7 +36,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-reps", type=int, default=5)
-    ap.add_argument("--stage", choices=["all", "forward", "fine", "coarse", "reorder"],
+    ap.add_argument("--stage", choices=["all", "forward", "fine", "coarse", "reorder", "backward"],
                     default="all",
                     help="time one stage only (for profiler runs); prints a short JSON line")
     return ap.parse_args()
@@ -58,6 +58,38 @@ def timed(fn, steps, warmup, rotate):
     return start.elapsed_time(stop) / steps
 
 
+def per_launch(fn, launches, warmup, rotate):
+    """Average duration of single launches, each bracketed by its own HIP events
+    on the current stream (launches do not overlap, as under a profiler)."""
+    import torch
+    for i in range(warmup):
+        fn(i % rotate)
+    pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+             for _ in range(launches)]
+    torch.cuda.synchronize()
+    for i, (a, b) in enumerate(pairs):
+        a.record()
+        fn(i % rotate)
+        b.record()
+    torch.cuda.synchronize()
+    return sum(a.elapsed_time(b) for a, b in pairs) / launches
+
+
+def traffic_record(kernel_source):
+    """HBM bytes per launch from the committed counter record, if it was taken
+    on the current kernel source (else None)."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "fine_fwd_wan1.3b_traffic.json")
+    try:
+        rec = json.load(open(path))
+        src = open(os.path.join(ROOT, kernel_source), "rb").read()
+    except OSError:
+        return None
+    if rec.get("source_sha256") != hashlib.sha256(src).hexdigest():
+        return None
+    return rec["traffic_bytes"]
+
+
 def cpu_baseline(w, x, reps):
     from threadpoolctl import threadpool_info, threadpool_limits
     from oracle import vsa_oracle as vo
@@ -73,12 +105,59 @@ def cpu_baseline(w, x, reps):
                       f"{reps} repetitions, {dt:.1f} s total"}
 
 
+def sparsity_sweep(args, dev):
+    """Forward and backward at top-K ratios 0.2 / 0.1 / 0.03 of the Wan-1.3B shape."""
+    import torch
+    import block_sparse_attention_cube_amd as vsa
+    from block_sparse_attention_cube_amd import flops
+    from synth import configs, inputs
+    out = []
+    steps = max(10, args.steps // 4)
+    warm = max(2, args.warmup // 4)
+    for w in configs.SWEEP:
+        grid = (w.T, w.Hh, w.Ww)
+        host = [inputs.make_inputs(w, seed=s, grads=True) for s in range(2)]
+        sets = [{n: inputs.as_torch(h[n], w.dtype, dev) for n in h} for h in host]
+        fwd = vsa.ForwardPlan(w.B, w.H, grid, w.d, w.topk, torch.bfloat16, dev)
+        bwd = vsa.BackwardPlan(w.B, w.H, grid, w.d, w.topk, torch.bfloat16, dev)
+        outs = []
+        for s in sets:
+            of, oc, idx, lse = fwd.run(s["q"], s["k"], s["v"])
+            outs.append((of.clone(), idx.clone(), lse.clone()))
+        f_ms = timed(lambda i: fwd.run(sets[i]["q"], sets[i]["k"], sets[i]["v"]), steps, warm, 2)
+        b_ms = timed(lambda i: bwd.run(sets[i]["q"], sets[i]["k"], sets[i]["v"], outs[i][0],
+                                       outs[i][2], outs[i][1], sets[i]["do_fine"],
+                                       sets[i]["do_coarse"]), steps, warm, 2)
+        ff = flops.fine_forward_flops(w.B, w.H, w.C, w.topk, w.d)
+        fb = flops.fine_backward_flops(w.B, w.H, w.C, w.topk, w.d)
+        out.append({"topk": w.topk, "sparsity": round(1 - w.topk / w.C, 4),
+                    "fwd_ms": round(f_ms, 5), "bwd_ms": round(b_ms, 5),
+                    "fwd_tflops": round(ff / (f_ms * 1e-3) / 1e12, 2),
+                    "bwd_tflops": round(fb / (b_ms * 1e-3) / 1e12, 2)})
+    return out
+
+
+CAL_BYTES = 256 << 20
+
+
 def stage_only(args, w, grid, sets, cube_sets, step):
     import torch
     import block_sparse_attention_cube_amd as vsa
     n = len(sets)
+    # one plain device copy of known size, so HBM byte counters can be scaled
+    src = torch.empty(CAL_BYTES, dtype=torch.uint8, device=sets[0]["q"].device)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
     if args.stage == "forward":
         fn = step
+    elif args.stage == "backward":
+        from synth import configs
+        w = configs.SWEEP[0]
+        print(json.dumps({"stage": "backward", "sweep": sparsity_sweep(args, sets[0]["q"].device)}),
+              flush=True)
+        return
     elif args.stage == "reorder":
         fn = lambda i: [vsa.reorder(sets[i][t], grid) for t in "qkv"]
     else:
@@ -134,6 +213,7 @@ def main():
     fine_step = lambda i: vsa.fine(cube_sets[i]["q"], cube_sets[i]["k"], cube_sets[i]["v"],
                                    idx_sets[i], grid, out=o_buf)
     fine_ms = timed(fine_step, args.steps, args.warmup, N_SETS)
+    fine_launch_ms = per_launch(fine_step, args.steps, args.warmup, N_SETS)
 
     def coarse_fine(i):
         c = cube_sets[i]
@@ -147,9 +227,13 @@ def main():
                                     all_idx, grid, out=o_buf)
     dense_ms = timed(dense_step, max(10, args.steps // 8), max(2, args.warmup // 4), N_SETS)
 
+    sweep = sparsity_sweep(args, dev)
+
     fl = flops.fine_forward_flops(w.B, w.H, w.C, w.topk, w.d)
     fl_dense = flops.fine_forward_flops(w.B, w.H, w.C, w.C, w.d)
     fine_tflops = fl / (fine_ms * 1e-3) / 1e12
+    launch_tflops = fl / (fine_launch_ms * 1e-3) / 1e12
+    traffic = traffic_record("block_sparse_attention_cube_amd/csrc/fine_fwd.hip")
     fwd_tflops = fl / (ms * 1e-3) / 1e12
 
     result = {
@@ -180,10 +264,13 @@ def main():
         "speedup_coarse_fine_vs_dense": round(dense_ms / cf_ms, 3),
         "speedup_forward_vs_dense": round(dense_ms / ms, 3),
         "dense_tflops": round(fl_dense / (dense_ms * 1e-3) / 1e12, 2),
+        "sweep": sweep,
+        "fine_launch_ms": round(fine_launch_ms, 5),
         "roofline": {"bound": "mfma", "kernel": "fine_fwd_bf16_kernel<128,false> (vsa_fine)",
-                     "achieved": round(fine_tflops, 2), "peak": flops.PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(fine_tflops / flops.PEAK_BF16_TFLOPS, 4),
-                     "traffic": None},
+                     "achieved": round(launch_tflops, 2), "peak": flops.PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(launch_tflops / flops.PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic,
+                     "flops_per_launch": fl, "launch_ms": round(fine_launch_ms, 5)},
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, host_sets[0], args.cpu_reps)

@@ -4,10 +4,10 @@ The computation lives in libvsa.so (include/vsa.h); this package is its
 PyTorch binding.  Importing it does not load the library; the first call does,
 and fails loudly if the library is missing.
 """
-from .binding import (ForwardPlan, VSAFunction, backward, check_problem, coarse, cube_counts,
+from .binding import (BackwardPlan, ForwardPlan, VSAFunction, backward, check_problem, coarse, cube_counts,
                       fine, forward, make_problem, reorder, vsa_attention, workspace_bytes)
 from ._lib import VSAError, LIB_PATH
 
-__all__ = ["ForwardPlan", "VSAFunction", "VSAError", "LIB_PATH", "backward", "check_problem",
+__all__ = ["BackwardPlan", "ForwardPlan", "VSAFunction", "VSAError", "LIB_PATH", "backward", "check_problem",
            "coarse", "cube_counts", "fine", "forward", "make_problem", "reorder",
            "vsa_attention", "workspace_bytes"]

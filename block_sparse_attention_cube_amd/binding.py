@@ -183,6 +183,39 @@ class ForwardPlan:
         return self.o_fine, self.o_coarse, self.idx, self.lse
 
 
+class BackwardPlan:
+    """Preallocated gradients and workspace for repeated vsa_backward calls on one shape."""
+
+    def __init__(self, B: int, H: int, grid: Grid, d: int, topk: int, dtype: torch.dtype,
+                 device):
+        self.prob = make_problem(B, H, grid, d, topk, dtype)
+        L.check(L.lib().vsa_check_problem(ctypes.byref(self.prob)), "vsa_backward")
+        C, Np = cube_counts(grid)
+        N = grid[0] * grid[1] * grid[2]
+        self.shape = (B, H, N, d)
+        self.lse_shape = (B, H, Np)
+        self.idx_shape = (B, H, C, topk)
+        self.dtype = dtype
+        self.device = torch.device(device)
+        self.dq, self.dk, self.dv = (torch.empty(self.shape, dtype=dtype, device=device)
+                                     for _ in range(3))
+        self.ws, self.nws = _workspace(self.prob, L.VSA_OP_BACKWARD, device)
+
+    def run(self, q, k, v, o_fine, lse, idx, do_fine, do_coarse=None):
+        for t, n in ((q, "q"), (k, "k"), (v, "v"), (o_fine, "o_fine"), (do_fine, "do_fine")):
+            _expect(t, self.shape, self.dtype, n)
+        if do_coarse is not None:
+            _expect(do_coarse, self.shape, self.dtype, "do_coarse")
+        _expect(lse, self.lse_shape, torch.float32, "lse")
+        _expect(idx, self.idx_shape, torch.int32, "idx")
+        L.check(L.lib().vsa_backward(ctypes.byref(self.prob), _ptr(q), _ptr(k), _ptr(v),
+                                     _ptr(o_fine), _ptr(lse), _ptr(idx), _ptr(do_fine),
+                                     _ptr(do_coarse), _ptr(self.dq), _ptr(self.dk), _ptr(self.dv),
+                                     _ptr(self.ws), self.nws, _stream(self.device)),
+                "vsa_backward")
+        return self.dq, self.dk, self.dv
+
+
 def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, grid: Grid, topk: int,
             return_lse: bool = True):
     """Whole VSA forward on raster tensors: (o_fine, o_coarse, idx, lse)."""

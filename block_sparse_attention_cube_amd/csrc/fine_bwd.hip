@@ -303,10 +303,10 @@ __global__ __launch_bounds__(256, 2) void fine_bwd_dq_kernel(BwdFineArgs a, Geo 
     // S^T and dP^T: lane holds (q = li, key = 16kb + 4lg + r)
     f32x4 sacc[4], pacc[4];
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      const int row = 16 * kb + li;
+    for (int ks = 0; ks < kKS; ++ks) {
 #pragma unroll
-      for (int ks = 0; ks < kKS; ++ks) {
+      for (int kb = 0; kb < 4; ++kb) {
+        const int row = 16 * kb + li;
         const u32x4 kf = read_row<D>(k_rows, row, 4 * ks + lg);
         const u32x4 vf = read_row<D>(v_rows, row, 4 * ks + lg);
         sacc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
@@ -435,10 +435,10 @@ __global__ __launch_bounds__(256, 2) void fine_bwd_dkdv_kernel(BwdFineArgs a, Ge
     // S and dP: lane holds (q = 16qb + 4lg + r, key = 16w + li)
     f32x4 sacc[4], pacc[4];
 #pragma unroll
-    for (int qb = 0; qb < 4; ++qb) {
-      const int row = 16 * qb + li;
+    for (int ks = 0; ks < kKS; ++ks) {
 #pragma unroll
-      for (int ks = 0; ks < kKS; ++ks) {
+      for (int qb = 0; qb < 4; ++qb) {
+        const int row = 16 * qb + li;
         const u32x4 qa = read_row<D>(q_rows, row, 4 * ks + lg);
         const u32x4 oa = read_row<D>(o_rows, row, 4 * ks + lg);
         sacc[qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(

@@ -121,6 +121,17 @@ struct KVStage {
   }
 };
 
+// Max over the 4 lanes l, l^16, l^32, l^48 that hold one query row, with the
+// gfx950 cross-row swaps (VALU ops, no LDS round trip).
+__device__ __forceinline__ float row_max4(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const uint32_t w = __float_as_uint(x);
+  const auto b = __builtin_amdgcn_permlane32_swap(w, w, false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
 template <int D, bool RASTER>
 __global__ __launch_bounds__(256, 2) void fine_fwd_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
@@ -180,12 +191,14 @@ __global__ __launch_bounds__(256, 2) void fine_fwd_bf16_kernel(
     if (has_next) st.load(k, v, (bh * g.Np + static_cast<int64_t>(sel[n + 1]) * 64) * D);
 
     // S^T[key][q] for the 4 key tiles: lane holds S[q=li][key=16kb+4lg+r]
+    // k-step outer, key tile inner: 4 independent accumulations between
+    // dependent MFMAs
     f32x4 sacc[4];
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      const int row = 16 * kb + li;
+    for (int ks = 0; ks < kKS; ++ks) {
 #pragma unroll
-      for (int ks = 0; ks < kKS; ++ks) {
+      for (int kb = 0; kb < 4; ++kb) {
+        const int row = 16 * kb + li;
         const int c = 4 * ks + lg;
         const u32x4 kf =
             *reinterpret_cast<const u32x4*>(k_lds + row * D + ((c ^ (row & (kKC - 1))) * 8));
@@ -210,8 +223,7 @@ __global__ __launch_bounds__(256, 2) void fine_fwd_bf16_kernel(
 #pragma unroll
     for (int kb = 1; kb < 4; ++kb)
       mloc = fmaxf(mloc, fmaxf(fmaxf(sacc[kb][0], sacc[kb][1]), fmaxf(sacc[kb][2], sacc[kb][3])));
-    mloc = fmaxf(mloc, __shfl_xor(mloc, 16));
-    mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
+    mloc = row_max4(mloc);
     const bool grow = mloc > m_run + tau_raw;
     if (__ballot(grow) != 0ull) {   // wave-uniform: rare after the first block
       const float m_new = grow ? mloc : m_run;
