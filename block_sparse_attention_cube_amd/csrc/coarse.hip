@@ -17,20 +17,37 @@
 #include "vsa_internal.h"
 #include "vsa_bwd.h"
 
+#include <type_traits>
+
 namespace vsa {
 namespace {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
+// Wave-wide reductions without LDS: DPP within 16-lane rows (xor 1, xor 2,
+// half-row mirror, row mirror), then the gfx950 cross-row swaps.
+template <typename Op>
+__device__ inline float wave_reduce(float x, Op op) {
+  auto dpp = [](float v, auto ctrl) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), decltype(ctrl)::value,
+                                                      0xf, 0xf, false));
+  };
+  x = op(x, dpp(x, std::integral_constant<int, 0xB1>{}));   // quad_perm [1,0,3,2]
+  x = op(x, dpp(x, std::integral_constant<int, 0x4E>{}));   // quad_perm [2,3,0,1]
+  x = op(x, dpp(x, std::integral_constant<int, 0x141>{}));  // row_half_mirror
+  x = op(x, dpp(x, std::integral_constant<int, 0x140>{}));  // row_mirror
+  const uint32_t u = __float_as_uint(x);
+  const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  x = op(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const uint32_t w = __float_as_uint(x);
+  const auto b = __builtin_amdgcn_permlane32_swap(w, w, false, false);
+  return op(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
 __device__ inline float wave_max(float x) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
-  return x;
+  return wave_reduce(x, [](float a, float b) { return fmaxf(a, b); });
 }
 __device__ inline float wave_sum(float x) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
-  return x;
+  return wave_reduce(x, [](float a, float b) { return a + b; });
 }
 
 // Order-preserving key of an fp32 score: a > b  <=>  key(a) > key(b); -0 == +0.
@@ -45,15 +62,39 @@ __device__ inline void store_out(uint16_t* p, float x) { *p = f32_to_bf16_rne(x)
 
 constexpr int kRows = 16;
 
+constexpr int kWaves = 8;   // 512 threads: 2 rows of statistics / top-K per wave
+
+// 16x16 fp32 tile out[r][j] = dot(A row r, B row j) over D, with the D/4
+// MFMA steps spread over 4 independent accumulators (short dependency chains).
+template <int D>
+__device__ __forceinline__ f32x4 dot_tile(const float4 (&af)[D / 16],
+                                          const float* __restrict__ brow, bool valid, int lg) {
+  f32x4 acc[4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f},
+                  {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+  float4 bf[D / 16];
+#pragma unroll
+  for (int kk = 0; kk < D / 16; ++kk)
+    bf[kk] = valid ? *reinterpret_cast<const float4*>(brow + 16 * kk + 4 * lg)
+                   : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+  for (int kk = 0; kk < D / 16; ++kk) {
+    acc[0] = __builtin_amdgcn_mfma_f32_16x16x4f32(af[kk].x, bf[kk].x, acc[0], 0, 0, 0);
+    acc[1] = __builtin_amdgcn_mfma_f32_16x16x4f32(af[kk].y, bf[kk].y, acc[1], 0, 0, 0);
+    acc[2] = __builtin_amdgcn_mfma_f32_16x16x4f32(af[kk].z, bf[kk].z, acc[2], 0, 0, 0);
+    acc[3] = __builtin_amdgcn_mfma_f32_16x16x4f32(af[kk].w, bf[kk].w, acc[3], 0, 0, 0);
+  }
+  return (acc[0] + acc[1]) + (acc[2] + acc[3]);
+}
+
 // KPL: keys per lane in the top-K, ceil(C / 64) rounded up to a power of two.
 template <typename TOut, int D, int KPL>
-__global__ __launch_bounds__(256) void coarse_kernel(const float* __restrict__ qm,
-                                                     const float* __restrict__ km,
-                                                     const float* __restrict__ vm,
-                                                     TOut* __restrict__ oc,
-                                                     int32_t* __restrict__ idx,
-                                                     float* __restrict__ scores, Geo g,
-                                                     int ldc) {
+__global__ __launch_bounds__(64 * kWaves) void coarse_kernel(const float* __restrict__ qm,
+                                                            const float* __restrict__ km,
+                                                            const float* __restrict__ vm,
+                                                            TOut* __restrict__ oc,
+                                                            int32_t* __restrict__ idx,
+                                                            float* __restrict__ scores, Geo g,
+                                                            int ldc) {
   extern __shared__ float lds[];
   float* sc = lds;                       // [kRows][ldc]
   float* rowmax = lds + kRows * ldc;     // [kRows]
@@ -81,19 +122,9 @@ __global__ __launch_bounds__(256) void coarse_kernel(const float* __restrict__ q
                        : make_float4(0.f, 0.f, 0.f, 0.f);
   }
   const int ntile = (C + 15) / 16;
-  for (int ct = wave; ct < ntile; ct += 4) {
+  for (int ct = wave; ct < ntile; ct += kWaves) {
     const int col = ct * 16 + li;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) {
-      const float4 kf = (col < C)
-          ? *reinterpret_cast<const float4*>(kh + (int64_t)col * D + 16 * kk + 4 * lg)
-          : make_float4(0.f, 0.f, 0.f, 0.f);
-      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(qf[kk].x, kf.x, acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(qf[kk].y, kf.y, acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(qf[kk].z, kf.z, acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(qf[kk].w, kf.w, acc, 0, 0, 0);
-    }
+    const f32x4 acc = dot_tile<D>(qf, kh + (int64_t)col * D, col < C, lg);
     // acc[r] is the dot product of query row 4*lg + r with key column col
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -107,7 +138,7 @@ __global__ __launch_bounds__(256) void coarse_kernel(const float* __restrict__ q
   __syncthreads();
 
   // -- 2. softmax statistics per row
-  for (int rr = wave; rr < kRows; rr += 4) {
+  for (int rr = wave; rr < kRows; rr += kWaves) {
     const float* srow = sc + rr * ldc;
     float m = -INFINITY;
     for (int j = lane; j < C; j += 64) m = fmaxf(m, srow[j]);
@@ -123,19 +154,28 @@ __global__ __launch_bounds__(256) void coarse_kernel(const float* __restrict__ q
   __syncthreads();
 
   // -- 3. O_coarse = P Vc: A[m=li][k=lg] = P[row li][j], B[k=lg][n=li] = Vc[j][col].
-  // 16 loads of Vc are issued together before their 16 MFMAs.
+  // Each batch of 16 Vc loads is issued one batch ahead of its MFMAs; the 16
+  // MFMAs of a batch alternate between 4 accumulators.
   {
     const float mrow = rowmax[li], irow = rowinv[li];
     const float* prow = sc + li * ldc;
-    for (int dt = wave; dt < D / 16; dt += 4) {
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      for (int j0 = 0; j0 < C; j0 += 64) {
-        float a[16], b[16];
+    for (int dt = wave; dt < D / 16; dt += kWaves) {
+      f32x4 acc[4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f},
+                      {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+      float b[16];
+      auto load_batch = [&](int j0) {
 #pragma unroll
         for (int u = 0; u < 16; ++u) {
           const int j = j0 + 16 * (u >> 2) + 4 * lg + (u & 3);
           b[u] = (j < C) ? vh[(int64_t)j * D + dt * 16 + li] : 0.f;
         }
+      };
+      load_batch(0);
+      for (int j0 = 0; j0 < C; j0 += 64) {
+        float bc[16], a[16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) bc[u] = b[u];
+        if (j0 + 64 < C) load_batch(j0 + 64);
 #pragma unroll
         for (int u = 0; u < 16; ++u) {
           const int j = j0 + 16 * (u >> 2) + 4 * lg + (u & 3);
@@ -143,12 +183,13 @@ __global__ __launch_bounds__(256) void coarse_kernel(const float* __restrict__ q
         }
 #pragma unroll
         for (int u = 0; u < 16; ++u)
-          acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[u], b[u], acc, 0, 0, 0);
+          acc[u & 3] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[u], bc[u], acc[u & 3], 0, 0, 0);
       }
+      const f32x4 tot = (acc[0] + acc[1]) + (acc[2] + acc[3]);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int row = row0 + 4 * lg + r;
-        if (row < C) store_out(oc + (bh * C + row) * D + dt * 16 + li, acc[r]);
+        if (row < C) store_out(oc + (bh * C + row) * D + dt * 16 + li, tot[r]);
       }
     }
   }
@@ -157,7 +198,7 @@ __global__ __launch_bounds__(256) void coarse_kernel(const float* __restrict__ q
   // row is one 64-bit ballot plus a scalar popcount per 64 keys.
   const int K = g.K;
   const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  for (int rr = wave; rr < kRows; rr += 4) {
+  for (int rr = wave; rr < kRows; rr += kWaves) {
     if (row0 + rr >= C) break;
     const float* srow = sc + rr * ldc;
     uint32_t key[KPL];
@@ -210,7 +251,7 @@ hipError_t launch_kpl(const Geo& g, const float* qm, const float* km, const floa
                                              static_cast<int>(lds));
     if (e != hipSuccess) return e;
   }
-  return launch_kernel(kern, dim3(ntile, g.B * g.H), dim3(256), lds, s, qm, km, vm,
+  return launch_kernel(kern, dim3(ntile, g.B * g.H), dim3(64 * kWaves), lds, s, qm, km, vm,
                        static_cast<TOut*>(oc), idx, scores, g, ldc);
 }
 
@@ -252,17 +293,7 @@ __device__ __forceinline__ void rows_dot(const float* __restrict__ A, int a0,
   const int ntile = (C + 15) / 16;
   for (int ct = wave; ct < ntile; ct += 4) {
     const int col = ct * 16 + li;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) {
-      const float4 bf = (col < C)
-          ? *reinterpret_cast<const float4*>(B + (int64_t)col * D + 16 * kk + 4 * lg)
-          : make_float4(0.f, 0.f, 0.f, 0.f);
-      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(af[kk].x, bf.x, acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(af[kk].y, bf.y, acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(af[kk].z, bf.z, acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(af[kk].w, bf.w, acc, 0, 0, 0);
-    }
+    const f32x4 acc = dot_tile<D>(af, B + (int64_t)col * D, col < C, lg);
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr) out[(4 * lg + rr) * ldc + col] = acc[rr] * scale;
   }
@@ -277,7 +308,8 @@ __device__ __forceinline__ void lds_times(const float* T, int ldc, const float* 
   const int li = lane & 15, lg = lane >> 4;
   const float* trow = T + li * ldc;
   for (int dt = wave; dt < D / 16; dt += 4) {
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    f32x4 acc[4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f},
+                    {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
     for (int j0 = 0; j0 < C; j0 += 64) {
       float a[16], b[16];
 #pragma unroll
@@ -288,12 +320,13 @@ __device__ __forceinline__ void lds_times(const float* T, int ldc, const float* 
       }
 #pragma unroll
       for (int u = 0; u < 16; ++u)
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[u], b[u], acc, 0, 0, 0);
+        acc[u & 3] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[u], b[u], acc[u & 3], 0, 0, 0);
     }
+    const f32x4 tot = (acc[0] + acc[1]) + (acc[2] + acc[3]);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int row = o0 + 4 * lg + r;
-      if (row < C) out[(int64_t)row * D + dt * 16 + li] = acc[r] * scale;
+      if (row < C) out[(int64_t)row * D + dt * 16 + li] = tot[r] * scale;
     }
   }
 }
