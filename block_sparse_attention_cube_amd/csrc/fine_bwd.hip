@@ -199,26 +199,33 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdPrepArgs a, Geo g) {
 // ---------------------------------------------------------------------------
 // Transposed block lists: for each key cube j of head (b, h), the query cubes
 // whose selection contains j, in ascending order.  One workgroup per head:
-// count, exclusive scan, then rows in ascending order fill the lists (the K
-// entries of one row are distinct, so a row's threads never share a cursor).
+// count, exclusive scan, then rows are placed R at a time (R <= 32): every
+// entry sets its row's bit in a per-key mask (atomicOr, order-free), and its
+// position is the key's cursor plus the number of earlier rows of the step
+// that hold the same key -- deterministic, no ordering by atomics.
 __global__ __launch_bounds__(256) void idx_transpose_kernel(const int32_t* __restrict__ idx,
                                                             int32_t* __restrict__ offsets,
                                                             int32_t* __restrict__ list, Geo g) {
-  extern __shared__ int32_t cursor[];     // [C] counts, then write cursors
+  extern __shared__ int32_t shared[];
+  int32_t* cursor = shared;                                   // [C] counts, then cursors
+  uint32_t* mask = reinterpret_cast<uint32_t*>(shared + g.C);  // [C] rows of this step
   __shared__ int32_t part[256];
   const int64_t bh = blockIdx.x;
   const int C = g.C, K = g.K, tid = threadIdx.x;
   const int32_t* rows = idx + bh * C * K;
-  for (int j = tid; j < C; j += 256) cursor[j] = 0;
+  for (int j = tid; j < C; j += 256) {
+    cursor[j] = 0;
+    mask[j] = 0u;
+  }
   __syncthreads();
   for (int e = tid; e < C * K; e += 256) atomicAdd(&cursor[rows[e]], 1);
   __syncthreads();
   // exclusive scan of the C counts: per-thread chunk sums, serial scan of 256 partials
   const int per = (C + 255) / 256;
   const int lo = min(C, tid * per), hi = min(C, lo + per);
-  int s = 0;
-  for (int j = lo; j < hi; ++j) s += cursor[j];
-  part[tid] = s;
+  int sum = 0;
+  for (int j = lo; j < hi; ++j) sum += cursor[j];
+  part[tid] = sum;
   __syncthreads();
   if (tid == 0) {
     int run = 0;
@@ -240,10 +247,19 @@ __global__ __launch_bounds__(256) void idx_transpose_kernel(const int32_t* __res
   if (tid == 0) off[C] = C * K;
   __syncthreads();
   int32_t* out = list + bh * C * K;
-  for (int i = 0; i < C; ++i) {
-    for (int k = tid; k < K; k += 256) {
-      const int j = rows[i * K + k];
-      out[cursor[j]++] = i;
+  const int R = max(1, min(32, 256 / K));
+  for (int i0 = 0; i0 < C; i0 += R) {
+    const int n = min(R, C - i0) * K;
+    for (int e = tid; e < n; e += 256) atomicOr(&mask[rows[i0 * K + e]], 1u << (e / K));
+    __syncthreads();
+    for (int e = tid; e < n; e += 256) {
+      const int r = e / K, j = rows[i0 * K + e];
+      out[cursor[j] + __popc(mask[j] & ((1u << r) - 1u))] = i0 + r;
+    }
+    __syncthreads();
+    for (int j = tid; j < C; j += 256) {
+      cursor[j] += __popc(mask[j]);
+      mask[j] = 0u;
     }
     __syncthreads();
   }
@@ -518,7 +534,7 @@ hipError_t launch_bwd_prep(const Geo& g, const BwdPrepArgs& a, hipStream_t s) {
 hipError_t launch_idx_transpose(const Geo& g, const int32_t* idx, int32_t* offsets,
                                 int32_t* list, hipStream_t s) {
   return launch_kernel(idx_transpose_kernel, dim3(g.B * g.H), dim3(256),
-                       static_cast<size_t>(g.C) * sizeof(int32_t), s, idx, offsets, list, g);
+                       2 * static_cast<size_t>(g.C) * sizeof(int32_t), s, idx, offsets, list, g);
 }
 
 hipError_t launch_bwd_fine(const Geo& g, const BwdFineArgs& a, hipStream_t s) {
