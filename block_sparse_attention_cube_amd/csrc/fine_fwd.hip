@@ -1,30 +1,31 @@
 // Fine stage of VSA: exact softmax attention of each 64-token query cube over
 // its K selected 64-token key cubes (64x64 blocks).
 //
-// bf16 path (the hot loop), one workgroup = 4 waves = one query cube:
-//   * wave w owns query slots 16w..16w+15; its Q fragment stays in VGPRs for
-//     the whole loop;
-//   * per selected key cube the K rows and the transposed V rows are staged
-//     in LDS (32 KB at d=128), XOR-swizzled so the MFMA operand reads hit
-//     distinct banks; the next cube's global loads are issued before the
-//     current cube is multiplied, so HBM/L2 latency hides behind the MFMAs;
-//   * S^T = K Q^T is computed with v_mfma_f32_16x16x32_bf16: the accumulator
-//     then holds, per lane, 16 scores of ONE query row, which is exactly the
-//     B-operand layout of the next product O^T += V^T P^T -- the
-//     probabilities go from the softmax straight into the PV MFMAs without an
-//     LDS round trip, and the O^T accumulator rows line up with the softmax
-//     statistics of the same lane;
-//   * online softmax in fp32 with exp2 (scale folded into one FMA); the row
-//     sum is kept per lane and reduced once at the end;
-//   * pad key slots of edge cubes get -inf before the max;
-//   * the epilogue stages O through LDS and writes whole 16-byte chunks,
+// bf16 path (the hot loop), one workgroup = 4 waves = one query cube; wave w
+// owns query slots 16w..16w+15 and keeps its Q fragment in VGPRs.
+//   * Staging: K cubes (row major, [64][D]) and V^T cubes ([D][64], keys in
+//     vt_col order, written that way by the reorder) go from HBM/L2 straight
+//     into LDS with global_load_lds_dwordx4; no VGPRs, no VALU.  Each lane's
+//     source chunk is chosen so that LDS holds the tiles XOR-swizzled and
+//     the MFMA operand reads below hit 16 distinct bank groups.  K runs one
+//     key cube ahead of V in a 2-slot ring each (64 KB at D = 128).
+//   * S^T = K Q^T with v_mfma_f32_16x16x32_bf16: the accumulator then holds,
+//     per lane, 16 scores of ONE query row, which is the B-operand layout of
+//     O^T += V^T P^T, so probabilities go from the softmax straight into the
+//     PV MFMAs.  Pad key slots of an edge cube enter the first MFMA of each
+//     chain as a -inf accumulator, so no masking pass follows the product.
+//   * Software pipeline per wave: while the MFMAs of S(n+1) run, the VALU
+//     evaluates exp2 of block n; while PV(n) runs, it scales S(n+1) into exp2
+//     units (t = s log2(e)/sqrt(d) - m) and takes its row max.  The running
+//     max m is raised lazily (only when a row exceeds it by 2^8), so
+//     probabilities stay <= 256 and the common step has no rescale.
+//   * Row sums come from one extra MFMA per k-step against a ones operand.
+//   * The epilogue stages O through LDS and writes whole 16-byte chunks,
 //     either in cube order or straight to raster order (fusing the inverse
 //     reorder), optionally also broadcasting the coarse row of the cube to
 //     every valid token (O_coarse in raster order).
 // Workgroups are remapped so each XCD walks one contiguous range of
 // (head, query cube) tiles, keeping that head's K/V in its own L2.
-//
-// fp32 path: a plain kernel, 4 threads per query row, fp32 FMA throughout.
 #include "vsa_internal.h"
 
 namespace vsa {
@@ -50,80 +51,60 @@ __device__ inline uint32_t pack_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2));  // RNE
 }
 
-// Halves of two words packed into one with v_perm_b32 (a's half in the low bits).
-__device__ inline uint32_t lo_lo(uint32_t a, uint32_t b) { return __builtin_amdgcn_perm(b, a, 0x05040100u); }
-__device__ inline uint32_t hi_hi(uint32_t a, uint32_t b) { return __builtin_amdgcn_perm(b, a, 0x07060302u); }
+// LDS geometry of one key cube.  A K row is D/8 16-byte chunks; chunk c of
+// row r is stored at chunk position c ^ ksw(r).  A V^T row (one head dim,
+// 64 keys) is 8 chunks stored at c ^ vsw(r).  With 256-byte K rows the
+// 16 rows an MFMA operand read touches land on 16 distinct chunk positions;
+// with 128-byte rows (V^T, and K at D = 64) two rows share a bank line and
+// the row pair index spreads them.
+template <int D>
+struct FineTile {
+  static constexpr int kElems = 64 * D;            // elements of a K or V^T tile
+  static constexpr int kKC = D / 8;                // chunks per K row
+  static constexpr int kDma = kElems / (256 * 8);  // 16-byte DMA loads per thread per tile
+  __device__ static constexpr int ksw(int r) { return kKC == 16 ? (r & 15) : ((r >> 1) & 7); }
+  __device__ static constexpr int vsw(int r) { return (r >> 1) & 7; }
+};
 
-// Column of key kappa inside a transposed V row.  Keys 32s + 16h + 4g + r go
-// to 32s + 8g + 4h + r, so the 8 keys one lane feeds to a PV MFMA k-step
-// ({32s + 4g + r} and {32s + 16 + 4g + r}, r = 0..3) sit in one 16-byte run.
-__device__ __host__ constexpr int vt_col(int kappa) {
-  return (kappa & ~31) | (((kappa >> 2) & 3) << 3) | (((kappa >> 4) & 1) << 2) | (kappa & 3);
+// Issues the DMA loads of one tile: thread t moves physical chunks
+// u*256 + t, whose source offsets (elements) were precomputed in off[].
+// The LDS destination of a load is wave-uniform; lane l lands at +16*l bytes.
+template <int D>
+__device__ __forceinline__ void dma_tile(const uint16_t* __restrict__ src, const int* off,
+                                         uint16_t* slot, int wave) {
+#pragma unroll
+  for (int u = 0; u < FineTile<D>::kDma; ++u)
+    __builtin_amdgcn_global_load_lds(
+        src + off[u], (__attribute__((address_space(3))) void*)(slot + (u * 256 + wave * 64) * 8),
+        16, 0, 0);
 }
 
-// Shared-memory tile of one key cube: K [64][D] with 16-byte chunks XOR
-// swizzled by row, and V^T [D][64 (+8 pad)] with keys in vt_col order.
-template <int D>
-struct Tile {
-  static constexpr int kKElems = 64 * D;
-  static constexpr int kVtStride = 72;                 // 144 bytes: rows spread over banks
-  static constexpr int kElems = kKElems + D * kVtStride;
-};
+// Accumulator init of S^T for key cube j: 0 for valid key slots, -inf for
+// pad slots.  Lane (li, lg) element r of tile kb is key slot 16kb + 4lg + r,
+// i.e. (it, ih, iw) = (kb, lg, r).
+__device__ __forceinline__ void edge_bias(const Geo& g, int j, int lg, f32x4* bias) {
+  const CubeExt e = cube_extent(g, j);
+  const float vl = lg < e.nh ? 0.f : -INFINITY;
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) bias[kb][r] = (kb < e.nt && r < e.nw) ? vl : -INFINITY;
+}
 
-// Register staging of one key cube on its way from HBM/L2 into LDS.  K rows
-// are copied as 16-byte chunks; V is transposed: a thread holds 4 keys x 8
-// dims and writes 8 runs of 4 keys (one per dim).
-template <int D>
-struct KVStage {
-  static constexpr int kKC = D / 8;             // 16-byte chunks per K row
-  static constexpr int kKReg = 64 * kKC / 256;  // K chunks per thread
-  static constexpr int kVThreads = 2 * D;       // threads moving 4 keys x 8 dims of V
-  u32x4 kreg[kKReg];
-  u32x4 vreg[4];
-  int tid, v_kg, v_dc;
+__device__ __forceinline__ bool is_edge(const Geo& g, int j) {
+  const CubeExt e = cube_extent(g, j);
+  return e.nt < 4 || e.nh < 4 || e.nw < 4;
+}
 
-  __device__ __forceinline__ void init(int t) {
-    tid = t;
-    v_kg = t % 16;   // 4-key group (consecutive lanes: consecutive groups)
-    v_dc = t / 16;   // 8-dim chunk
-  }
-  __device__ __forceinline__ void load(const uint16_t* __restrict__ k,
-                                       const uint16_t* __restrict__ v, int64_t base) {
-#pragma unroll
-    for (int u = 0; u < kKReg; ++u)
-      kreg[u] = *reinterpret_cast<const u32x4*>(k + base + (tid + 256 * u) * 8);
-    if (tid < kVThreads) {
-      const uint16_t* vb = v + base + (4 * v_kg) * D + 8 * v_dc;
-#pragma unroll
-      for (int u = 0; u < 4; ++u) vreg[u] = *reinterpret_cast<const u32x4*>(vb + u * D);
-    }
-  }
-  __device__ __forceinline__ void store(uint16_t* tile) const {
-    uint16_t* k_lds = tile;
-    uint16_t* vt_lds = tile + Tile<D>::kKElems;
-#pragma unroll
-    for (int u = 0; u < kKReg; ++u) {
-      const int ch = tid + 256 * u, row = ch / kKC, c = ch % kKC;
-      *reinterpret_cast<u32x4*>(k_lds + row * D + ((c ^ (row & (kKC - 1))) * 8)) = kreg[u];
-    }
-    if (tid < kVThreads) {
-      // vreg[u] = V[key 4kg+u][8dc .. 8dc+7]  ->  Vt[8dc+i][vt_col(4kg) .. +3]
-      const int col = vt_col(4 * v_kg);
-#pragma unroll
-      for (int h = 0; h < 4; ++h) {
-        const int d0 = 8 * v_dc + 2 * h;
-        const u32x2 lo = {lo_lo(vreg[0][h], vreg[1][h]), lo_lo(vreg[2][h], vreg[3][h])};
-        const u32x2 hi = {hi_hi(vreg[0][h], vreg[1][h]), hi_hi(vreg[2][h], vreg[3][h])};
-        *reinterpret_cast<u32x2*>(vt_lds + d0 * Tile<D>::kVtStride + col) = lo;
-        *reinterpret_cast<u32x2*>(vt_lds + (d0 + 1) * Tile<D>::kVtStride + col) = hi;
-      }
-    }
-  }
-};
-
-// Max over the 4 lanes l, l^16, l^32, l^48 that hold one query row, with the
-// gfx950 cross-row swaps (VALU ops, no LDS round trip).
-__device__ __forceinline__ float row_max4(float x) {
+// Max over one lane's 16 values and then over the 4 lanes l, l^16, l^32,
+// l^48 that hold the same query row (gfx950 cross-row swaps, no LDS).  The
+// inputs come out of VALU arithmetic, so the compiler needs no canonicalising
+// maxes on them.
+__device__ __forceinline__ float row_max(const f32x4* t) {
+  float x = fmaxf(fmaxf(fmaxf(fmaxf(t[0][0], t[0][1]), fmaxf(t[0][2], t[0][3])),
+                        fmaxf(fmaxf(t[1][0], t[1][1]), fmaxf(t[1][2], t[1][3]))),
+                  fmaxf(fmaxf(fmaxf(t[2][0], t[2][1]), fmaxf(t[2][2], t[2][3])),
+                        fmaxf(fmaxf(t[3][0], t[3][1]), fmaxf(t[3][2], t[3][3]))));
   const uint32_t u = __float_as_uint(x);
   const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
   x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
@@ -132,145 +113,192 @@ __device__ __forceinline__ float row_max4(float x) {
   return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
+// S^T tile of one key cube: sacc[kb] for keys 16kb..16kb+15.  k-step outer,
+// key tile inner: 4 independent accumulations between dependent MFMAs.
+template <int D>
+__device__ __forceinline__ void score_tile(const uint16_t* k_lds, const int* kro, const u32x4* qf,
+                                           const f32x4* bias, f32x4* sacc) {
+#pragma unroll
+  for (int ks = 0; ks < D / 32; ++ks)
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      const u32x4 kf = *reinterpret_cast<const u32x4*>(k_lds + kro[ks] + kb * 16 * D);
+      sacc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kf), as_bf16x8(qf[ks]),
+                                                         ks == 0 ? bias[kb] : sacc[kb], 0, 0, 0);
+    }
+}
+
+// P^T as the B operand of the PV product: k-step s covers keys
+// 32s + 16(i/4) + 4lg + (i%4), i = 0..7 (t already in exp2 units).
+__device__ __forceinline__ void probabilities(const f32x4* t, u32x4* pf) {
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    float p[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) p[i] = __builtin_amdgcn_exp2f(t[2 * s + (i >> 2)][i & 3]);
+    pf[s] = u32x4{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
+                  pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7])};
+  }
+}
+
+// O^T[d][q] += V^T[d][keys] P^T[keys][q] and the row sums of P (MFMA
+// against ones).  A lane holds V^T[16dt + li][the same 8 keys as pf].
+template <int D>
+__device__ __forceinline__ void pv_tile(const uint16_t* vt_lds, const int* vro, const u32x4* pf,
+                                        f32x4* oacc, f32x4& lacc) {
+  const u32x4 ones = {0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u};  // bf16 1.0 x 8
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    lacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ones), as_bf16x8(pf[s]), lacc, 0, 0, 0);
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) {
+      const u32x4 a = *reinterpret_cast<const u32x4*>(vt_lds + vro[s] + dt * 16 * 64);
+      oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(pf[s]),
+                                                         oacc[dt], 0, 0, 0);
+    }
+  }
+}
+
 template <int D, bool RASTER>
 __global__ __launch_bounds__(256, 2) void fine_fwd_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
-    const uint16_t* __restrict__ v, const int32_t* __restrict__ idx,
+    const uint16_t* __restrict__ vt, const int32_t* __restrict__ idx,
     uint16_t* __restrict__ o, float* __restrict__ lse, const uint16_t* __restrict__ oc,
     uint16_t* __restrict__ o_coarse, Geo g) {
-  constexpr int kKC = D / 8;              // 16-byte chunks per K row
-  constexpr int kKS = D / 32;             // k-steps of S^T = K Q^T
-  constexpr int kDT = D / 16;             // 16-row tiles of O^T
-  constexpr int kOutReg = 64 * kKC / 256; // 16-byte output chunks per thread
-  constexpr int kOS = D + 8;              // padded row stride of the O staging tile
-  constexpr int kVS = Tile<D>::kVtStride;
-  // rescale the running output only when a row max grows by more than 2^8
-  // (in exp2 units): probabilities stay <= 256, exact after normalisation
-  constexpr float kTau = 8.0f;
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * Tile<D>::kElems];
+  using Tl = FineTile<D>;
+  constexpr int kKC = Tl::kKC;
+  constexpr int kKS = D / 32;              // k-steps of S^T = K Q^T
+  constexpr int kDT = D / 16;              // 16-row tiles of O^T
+  constexpr int kT = Tl::kElems;
+  constexpr int kOutReg = 64 * kKC / 256;  // 16-byte output chunks per thread
+  constexpr int kOS = D + 8;               // padded row stride of the O staging tile
+  constexpr float kTau = 8.0f;             // lazy rescale threshold (exp2 units)
+  __shared__ __attribute__((aligned(16))) uint16_t smem[4 * kT];   // K ring (2), V^T ring (2)
+  uint16_t* const kring = smem;
+  uint16_t* const vring = smem + 2 * kT;
 
   const int tile = xcd_remap(blockIdx.x, gridDim.x);
   const int64_t bh = tile / g.C;
   const int qc = tile % g.C;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int li = lane & 15, lg = lane >> 4;
   const int K = g.K;
   const int32_t* __restrict__ sel = idx + static_cast<int64_t>(tile) * K;
   const float c2 = inv_sqrt_d<D>() * kLog2e;
-  const float tau_raw = kTau / c2;
+  const int64_t kv0 = bh * g.Np * D;
+  auto cube = [&](int n) { return kv0 + static_cast<int64_t>(sel[n]) * 64 * D; };
 
+  // DMA source offsets of this thread's chunks (loop invariant)
+  int koff[Tl::kDma], voff[Tl::kDma];
+#pragma unroll
+  for (int u = 0; u < Tl::kDma; ++u) {
+    const int P = u * 256 + tid;
+    const int kr = P / kKC, vr = P / 8;
+    koff[u] = kr * D + (((P % kKC) ^ Tl::ksw(kr)) * 8);
+    voff[u] = vr * 64 + (((P % 8) ^ Tl::vsw(vr)) * 8);
+  }
   // Q fragment: B operand of S^T, lane holds Q[slot 16w+li][32ks + 8lg .. +7]
   u32x4 qf[kKS];
   {
     const uint16_t* qrow = q + (bh * g.Np + static_cast<int64_t>(qc) * 64 + wave * 16 + li) * D;
 #pragma unroll
-    for (int ks = 0; ks < kKS; ++ks)
-      qf[ks] = *reinterpret_cast<const u32x4*>(qrow + 32 * ks + 8 * lg);
+    for (int ks = 0; ks < kKS; ++ks) qf[ks] = *reinterpret_cast<const u32x4*>(qrow + 32 * ks + 8 * lg);
   }
-
-  KVStage<D> st;
-  st.init(tid);
+  // per-lane LDS element offsets of the MFMA operand reads (loop invariant)
+  int kro[kKS], vro[2];
+#pragma unroll
+  for (int ks = 0; ks < kKS; ++ks) kro[ks] = li * D + (((4 * ks + lg) ^ Tl::ksw(li)) * 8);
+#pragma unroll
+  for (int s = 0; s < 2; ++s) vro[s] = li * 64 + (((4 * s + lg) ^ Tl::vsw(li)) * 8);
 
   f32x4 oacc[kDT];
 #pragma unroll
   for (int dt = 0; dt < kDT; ++dt) oacc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  f32x4 lacc = {0.f, 0.f, 0.f, 0.f};   // row sums of P, by MFMA against ones
-  const u32x4 ones = {0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u};  // bf16 1.0 x 8
-  float m_run = -INFINITY;
+  f32x4 lacc = {0.f, 0.f, 0.f, 0.f};
+  f32x4 bias[4];
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) bias[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  st.load(k, v, (bh * g.Np + static_cast<int64_t>(sel[0]) * 64) * D);
-  st.store(smem);
+  // prologue: K(0), V(0), K(1) in flight together; S(0) and its row max
+  dma_tile<D>(k + cube(0), koff, kring, wave);
+  dma_tile<D>(vt + cube(0), voff, vring, wave);
+  if (K > 1) dma_tile<D>(k + cube(1), koff, kring + kT, wave);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
-
-  for (int n = 0; n < K; ++n) {
-    const uint16_t* const cur = smem + (n & 1) * Tile<D>::kElems;
-    const uint16_t* const k_lds = cur;
-    const uint16_t* const vt_lds = cur + Tile<D>::kKElems;
-    const int j = sel[n];
-    const bool has_next = n + 1 < K;
-    if (has_next) st.load(k, v, (bh * g.Np + static_cast<int64_t>(sel[n + 1]) * 64) * D);
-
-    // S^T[key][q] for the 4 key tiles: lane holds S[q=li][key=16kb+4lg+r]
-    // k-step outer, key tile inner: 4 independent accumulations between
-    // dependent MFMAs
-    f32x4 sacc[4];
+  bool biased = false;
+  if (is_edge(g, sel[0])) {
+    edge_bias(g, sel[0], lg, bias);
+    biased = true;
+  }
+  f32x4 tcur[4];
+  score_tile<D>(kring, kro, qf, bias, tcur);
+  float mb;   // running row max, exp2 units
 #pragma unroll
-    for (int ks = 0; ks < kKS; ++ks) {
+  for (int kb = 0; kb < 4; ++kb) tcur[kb] = tcur[kb] * c2;
+  mb = row_max(tcur);
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-        const int row = 16 * kb + li;
-        const int c = 4 * ks + lg;
-        const u32x4 kf =
-            *reinterpret_cast<const u32x4*>(k_lds + row * D + ((c ^ (row & (kKC - 1))) * 8));
-        sacc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-            as_bf16x8(kf), as_bf16x8(qf[ks]),
-            ks == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : sacc[kb], 0, 0, 0);
+  for (int kb = 0; kb < 4; ++kb) tcur[kb] = tcur[kb] - mb;
+
+  for (int n = 0; n + 1 < K; ++n) {
+    // K(n+1) and V(n) have landed for every wave; slots of K(n), V(n-1) are free
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    dma_tile<D>(vt + cube(n + 1), voff, vring + ((n + 1) & 1) * kT, wave);
+    if (n + 2 < K) dma_tile<D>(k + cube(n + 2), koff, kring + (n & 1) * kT, wave);
+    const int jn = sel[n + 1];
+    const bool edge = is_edge(g, jn);
+    if (edge || biased) {
+      if (edge) {
+        edge_bias(g, jn, lg, bias);
+      } else {
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) bias[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
       }
+      biased = edge;
     }
-
-    // pad key slots of an edge cube: slot 16kb + 4lg + r = (it=kb, ih=lg, iw=r)
-    const CubeExt e = cube_extent(g, j);
-    if (e.nt < 4 || e.nh < 4 || e.nw < 4) {
+    // S(n+1) on the matrix cores while exp2 of block n runs on the VALU
+    f32x4 tnext[4];
+    score_tile<D>(kring + ((n + 1) & 1) * kT, kro, qf, bias, tnext);
+    u32x4 pf[2];
+    probabilities(tcur, pf);
+    // PV(n) while S(n+1) is scaled into exp2 units and reduced
+    pv_tile<D>(vring + (n & 1) * kT, vro, pf, oacc, lacc);
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
+    for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-          if (kb >= e.nt || lg >= e.nh || r >= e.nw) sacc[kb][r] = -INFINITY;
-    }
-
-    // online softmax for row q = li (lanes li, li+16, li+32, li+48 share it)
-    float mloc = fmaxf(fmaxf(sacc[0][0], sacc[0][1]), fmaxf(sacc[0][2], sacc[0][3]));
-#pragma unroll
-    for (int kb = 1; kb < 4; ++kb)
-      mloc = fmaxf(mloc, fmaxf(fmaxf(sacc[kb][0], sacc[kb][1]), fmaxf(sacc[kb][2], sacc[kb][3])));
-    mloc = row_max4(mloc);
-    const bool grow = mloc > m_run + tau_raw;
+      for (int r = 0; r < 4; ++r) tnext[kb][r] = fmaf(tnext[kb][r], c2, -mb);
+    const float mt = row_max(tnext);
+    const bool grow = mt > kTau;
     if (__ballot(grow) != 0ull) {   // wave-uniform: rare after the first block
-      const float m_new = grow ? mloc : m_run;
-      const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c2);
+      const float delta = grow ? mt : 0.f;
+      const float alpha = __builtin_amdgcn_exp2f(-delta);
 #pragma unroll
       for (int dt = 0; dt < kDT; ++dt) oacc[dt] *= alpha;
       lacc *= alpha;
-      m_run = m_new;
+      mb += delta;
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) tnext[kb] = tnext[kb] - delta;
     }
-    const float mb = m_run * c2;
-
-    // P^T as B operand: k-step s covers keys 32s + 16(i/4) + 4lg + (i%4)
-    u32x4 pf[2];
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      float p[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-        p[i] = __builtin_amdgcn_exp2f(fmaf(sacc[2 * s + (i >> 2)][i & 3], c2, -mb));
-      pf[s] = u32x4{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
-                    pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7])};
-    }
-    // O^T[d][q] += V^T[d][keys] P^T[keys][q]; A lane holds Vt[16dt+li][same keys]
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      lacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ones), as_bf16x8(pf[s]), lacc,
-                                                     0, 0, 0);
-#pragma unroll
-      for (int dt = 0; dt < kDT; ++dt) {
-        const u32x4 a =
-            *reinterpret_cast<const u32x4*>(vt_lds + (16 * dt + li) * kVS + 32 * s + 8 * lg);
-        oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(pf[s]),
-                                                           oacc[dt], 0, 0, 0);
-      }
-    }
-
-    if (has_next) st.store(smem + ((n + 1) & 1) * Tile<D>::kElems);
-    __syncthreads();
+    for (int kb = 0; kb < 4; ++kb) tcur[kb] = tnext[kb];
   }
+  {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    u32x4 pf[2];
+    probabilities(tcur, pf);
+    pv_tile<D>(vring + ((K - 1) & 1) * kT, vro, pf, oacc, lacc);
+  }
+  __syncthreads();   // every wave is done with the rings: reuse them for O
 
   // ---- epilogue: l is the same in every accumulator row of lacc
   const float l = lacc[0];
   const float inv = 1.f / l;
   if (lse != nullptr && lg == 0)
-    lse[bh * g.Np + static_cast<int64_t>(qc) * 64 + wave * 16 + li] = (m_run * c2 + log2f(l)) * kLn2;
+    lse[bh * g.Np + static_cast<int64_t>(qc) * 64 + wave * 16 + li] = (mb + log2f(l)) * kLn2;
 
-  uint16_t* const o_lds = smem;  // [64][kOS]; every wave has passed the last barrier
+  uint16_t* const o_lds = smem;  // [64][kOS]
 #pragma unroll
   for (int dt = 0; dt < kDT; ++dt) {
     // lane holds O[q = 16w+li][d = 16dt + 4lg + r], r = 0..3

@@ -170,7 +170,10 @@ size_t vsa_workspace_bytes(const vsa_problem* p, int op) {
   switch (op) {
     case VSA_OP_FORWARD: carve_forward(p, nullptr, &total); return total;
     case VSA_OP_COARSE: carve_coarse(p, nullptr, &total); return total;
-    case VSA_OP_FINE: return 0;
+    case VSA_OP_FINE:  // bf16: V re-laid out as transposed cubes for the MFMA kernel
+      return p->dtype == VSA_BF16
+                 ? round_up(size_t(p->B) * p->H * geometry(p).Np * p->d * sizeof(uint16_t))
+                 : 0;
     case VSA_OP_BACKWARD:
       if (check_backward(p) != VSA_OK) return 0;
       carve_backward(p, nullptr, &total);
@@ -198,12 +201,16 @@ vsa_status vsa_reorder(const vsa_problem* p, const void* x, void* y, int inverse
   vsa_status st = check(p);
   if (st != VSA_OK) return st;
   if ((st = pointers({x, y}, {})) != VSA_OK) return st;
+  if (inverse < 0 || inverse > 2) return VSA_ERR_UNSUPPORTED;
+  if (inverse == 2 && p->dtype != VSA_BF16) return VSA_ERR_UNSUPPORTED;
   const Geo g = geometry(p);
   vsa::ReorderBatch b = {};
   b.x[0] = x;
   b.y[0] = y;
   b.count = 1;
-  return launched(vsa::launch_reorder(g, p->dtype, inverse ? 1 : 0, b, stream));
+  b.transposed = inverse == 2 ? 1 : 0;
+  const int mode = inverse == 0 ? 0 : (inverse == 1 ? 1 : 3);
+  return launched(vsa::launch_reorder(g, p->dtype, mode, b, stream));
 }
 
 vsa_status vsa_coarse(const vsa_problem* p, const void* qcube, const void* kcube,
@@ -233,7 +240,32 @@ vsa_status vsa_fine(const vsa_problem* p, const void* qcube, const void* kcube,
   if ((st = pointers({qcube, kcube, vcube, idx, o_fine}, {lse})) != VSA_OK) return st;
   if ((st = workspace(p, VSA_OP_FINE, ws, ws_bytes)) != VSA_OK) return st;
   const Geo g = geometry(p);
-  return launched(vsa::launch_fine(g, p->dtype, qcube, kcube, vcube, idx, o_fine, lse,
+  const void* v = vcube;
+  hipError_t e = hipSuccess;
+  if (p->dtype == VSA_BF16) {   // the bf16 kernel reads V^T cubes
+    vsa::ReorderBatch b = {};
+    b.x[0] = vcube;
+    b.y[0] = ws;
+    b.count = 1;
+    b.transposed = 1;
+    e = vsa::launch_reorder(g, p->dtype, 3, b, stream);
+    v = ws;
+  }
+  if (e == hipSuccess)
+    e = vsa::launch_fine(g, p->dtype, qcube, kcube, v, idx, o_fine, lse,
+                         /*raster_out=*/false, nullptr, nullptr, stream);
+  return launched(e);
+}
+
+vsa_status vsa_fine_vt(const vsa_problem* p, const void* qcube, const void* kcube,
+                       const void* vtcube, const int32_t* idx, void* o_fine, float* lse,
+                       hipStream_t stream) {
+  vsa_status st = check(p);
+  if (st != VSA_OK) return st;
+  if (p->dtype != VSA_BF16) return VSA_ERR_UNSUPPORTED;
+  if ((st = pointers({qcube, kcube, vtcube, idx, o_fine}, {lse})) != VSA_OK) return st;
+  const Geo g = geometry(p);
+  return launched(vsa::launch_fine(g, p->dtype, qcube, kcube, vtcube, idx, o_fine, lse,
                                    /*raster_out=*/false, nullptr, nullptr, stream));
 }
 
@@ -251,6 +283,7 @@ vsa_status vsa_forward(const vsa_problem* p, const void* q, const void* k, const
   b.y[0] = w.qc; b.y[1] = w.kc; b.y[2] = w.vc;
   b.mean[0] = w.qm; b.mean[1] = w.km; b.mean[2] = w.vm;
   b.count = 3;
+  b.transposed = p->dtype == VSA_BF16 ? 4 : 0;   // bf16 V goes out as V^T cubes
   hipError_t e = vsa::launch_reorder(g, p->dtype, 0, b, stream);
   if (e == hipSuccess)
     e = vsa::launch_coarse(g, p->dtype, w.qm, w.km, w.vm, w.oc, idx, nullptr, stream);
