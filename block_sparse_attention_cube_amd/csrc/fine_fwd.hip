@@ -79,21 +79,32 @@ __device__ __forceinline__ void dma_tile(const uint16_t* __restrict__ src, const
         16, 0, 0);
 }
 
-// Accumulator init of S^T for key cube j: 0 for valid key slots, -inf for
-// pad slots.  Lane (li, lg) element r of tile kb is key slot 16kb + 4lg + r,
-// i.e. (it, ih, iw) = (kb, lg, r).
-__device__ __forceinline__ void edge_bias(const Geo& g, int j, int lg, f32x4* bias) {
-  const CubeExt e = cube_extent(g, j);
-  const float vl = lg < e.nh ? 0.f : -INFINITY;
-#pragma unroll
-  for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) bias[kb][r] = (kb < e.nt && r < e.nw) ? vl : -INFINITY;
+// Valid extent of a key cube packed as nt | nh << 3 | nw << 6 (each 1..4);
+// a full cube packs to kFullExt.
+constexpr int kFullExt = 4 | (4 << 3) | (4 << 6);
+__device__ __forceinline__ int packed_extent(const Geo& g, int c) {
+  const CubeExt e = cube_extent(g, c);
+  return e.nt | (e.nh << 3) | (e.nw << 6);
 }
 
-__device__ __forceinline__ bool is_edge(const Geo& g, int j) {
-  const CubeExt e = cube_extent(g, j);
-  return e.nt < 4 || e.nh < 4 || e.nw < 4;
+// Extents of the key cubes sel[base .. base+63], one per lane, so that a
+// step reads its cube's extent with one v_readlane instead of scalar
+// divisions.
+__device__ __forceinline__ int lane_extents(const Geo& g, const int32_t* __restrict__ sel, int base,
+                                            int K, int lane) {
+  const int m = base + lane;
+  return m < K ? packed_extent(g, sel[m]) : kFullExt;
+}
+
+// Masking of pad key slots.  Lane (li, lg) element r of key tile kb is key
+// slot 16kb + 4lg + r, i.e. (it, ih, iw) = (kb, lg, r).  The (ih, iw) part
+// is the same for every kb: one accumulator init (0 valid, -inf pad) serves
+// the first MFMA of every key tile.  The it part masks whole key tiles: it
+// enters as a -inf offset of the exp2 argument of tiles kb >= nt.
+__device__ __forceinline__ f32x4 hw_bias(int ext, int lg) {
+  const int nh = (ext >> 3) & 7, nw = ext >> 6;
+  const float vl = lg < nh ? 0.f : -INFINITY;
+  return f32x4{vl, nw > 1 ? vl : -INFINITY, nw > 2 ? vl : -INFINITY, nw > 3 ? vl : -INFINITY};
 }
 
 // Max over one lane's 16 values and then over the 4 lanes l, l^16, l^32,
@@ -117,14 +128,14 @@ __device__ __forceinline__ float row_max(const f32x4* t) {
 // key tile inner: 4 independent accumulations between dependent MFMAs.
 template <int D>
 __device__ __forceinline__ void score_tile(const uint16_t* k_lds, const int* kro, const u32x4* qf,
-                                           const f32x4* bias, f32x4* sacc) {
+                                           const f32x4 bias, f32x4* sacc) {
 #pragma unroll
   for (int ks = 0; ks < D / 32; ++ks)
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
       const u32x4 kf = *reinterpret_cast<const u32x4*>(k_lds + kro[ks] + kb * 16 * D);
       sacc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kf), as_bf16x8(qf[ks]),
-                                                         ks == 0 ? bias[kb] : sacc[kb], 0, 0, 0);
+                                                         ks == 0 ? bias : sacc[kb], 0, 0, 0);
     }
 }
 
@@ -216,9 +227,6 @@ __global__ __launch_bounds__(256, 2) void fine_fwd_bf16_kernel(
 #pragma unroll
   for (int dt = 0; dt < kDT; ++dt) oacc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   f32x4 lacc = {0.f, 0.f, 0.f, 0.f};
-  f32x4 bias[4];
-#pragma unroll
-  for (int kb = 0; kb < 4; ++kb) bias[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // prologue: K(0), V(0), K(1) in flight together; S(0) and its row max
   dma_tile<D>(k + cube(0), koff, kring, wave);
@@ -226,19 +234,24 @@ __global__ __launch_bounds__(256, 2) void fine_fwd_bf16_kernel(
   if (K > 1) dma_tile<D>(k + cube(1), koff, kring + kT, wave);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
-  bool biased = false;
-  if (is_edge(g, sel[0])) {
-    edge_bias(g, sel[0], lg, bias);
-    biased = true;
-  }
+  // key cube extents, 64 steps per lane vector; the masks follow the extent
+  // and are rebuilt only when it changes
+  int ext_lanes = lane_extents(g, sel, 0, K, lane);
+  const int ext0 = __builtin_amdgcn_readlane(ext_lanes, 0);
+  int hw_cur = ext0 >> 3, nt_cur = ext0 & 7;
+  f32x4 bias = hw_bias(ext0, lg);
   f32x4 tcur[4];
   score_tile<D>(kring, kro, qf, bias, tcur);
-  float mb;   // running row max, exp2 units
+  float mb;     // running row max, exp2 units
+  float mbk[4]; // exp2 offset of key tile kb: -mb, or -inf for tiles past the cube's t extent
 #pragma unroll
-  for (int kb = 0; kb < 4; ++kb) tcur[kb] = tcur[kb] * c2;
+  for (int kb = 0; kb < 4; ++kb) tcur[kb] = kb < nt_cur ? tcur[kb] * c2 : f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
   mb = row_max(tcur);
 #pragma unroll
-  for (int kb = 0; kb < 4; ++kb) tcur[kb] = tcur[kb] - mb;
+  for (int kb = 0; kb < 4; ++kb) {
+    tcur[kb] = tcur[kb] - mb;
+    mbk[kb] = kb < nt_cur ? -mb : -INFINITY;
+  }
 
   for (int n = 0; n + 1 < K; ++n) {
     // K(n+1) and V(n) have landed for every wave; slots of K(n), V(n-1) are free
@@ -246,16 +259,16 @@ __global__ __launch_bounds__(256, 2) void fine_fwd_bf16_kernel(
     __syncthreads();
     dma_tile<D>(vt + cube(n + 1), voff, vring + ((n + 1) & 1) * kT, wave);
     if (n + 2 < K) dma_tile<D>(k + cube(n + 2), koff, kring + (n & 1) * kT, wave);
-    const int jn = sel[n + 1];
-    const bool edge = is_edge(g, jn);
-    if (edge || biased) {
-      if (edge) {
-        edge_bias(g, jn, lg, bias);
-      } else {
+    if (((n + 1) & 63) == 0) ext_lanes = lane_extents(g, sel, n + 1, K, lane);
+    const int ext = __builtin_amdgcn_readlane(ext_lanes, (n + 1) & 63);
+    if ((ext >> 3) != hw_cur) {
+      hw_cur = ext >> 3;
+      bias = hw_bias(ext, lg);
+    }
+    if ((ext & 7) != nt_cur) {
+      nt_cur = ext & 7;
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb) bias[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
-      }
-      biased = edge;
+      for (int kb = 0; kb < 4; ++kb) mbk[kb] = kb < nt_cur ? -mb : -INFINITY;
     }
     // S(n+1) on the matrix cores while exp2 of block n runs on the VALU
     f32x4 tnext[4];
@@ -267,7 +280,7 @@ __global__ __launch_bounds__(256, 2) void fine_fwd_bf16_kernel(
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) tnext[kb][r] = fmaf(tnext[kb][r], c2, -mb);
+      for (int r = 0; r < 4; ++r) tnext[kb][r] = fmaf(tnext[kb][r], c2, mbk[kb]);
     const float mt = row_max(tnext);
     const bool grow = mt > kTau;
     if (__ballot(grow) != 0ull) {   // wave-uniform: rare after the first block
@@ -278,7 +291,10 @@ __global__ __launch_bounds__(256, 2) void fine_fwd_bf16_kernel(
       lacc *= alpha;
       mb += delta;
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) tnext[kb] = tnext[kb] - delta;
+      for (int kb = 0; kb < 4; ++kb) {
+        tnext[kb] = tnext[kb] - delta;
+        mbk[kb] = mbk[kb] - delta;
+      }
     }
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) tcur[kb] = tnext[kb];

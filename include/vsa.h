@@ -126,7 +126,8 @@ vsa_status vsa_coarse(const vsa_problem* p, const void* qcube, const void* kcube
 /* Fine stage on cube-order inputs (the fine block-sparse kernel of the
  * results section).
  *   qcube, kcube, vcube : [B,H,Np,d] cube order; pad slots of kcube/vcube are
- *                         never attended to.
+ *                         never attended to but must hold finite values
+ *                         (vsa_reorder writes zeros there).
  *   idx                 : [B,H,C,topk] int32, each in [0, C), distinct per row
  *                         (any order; the result does not depend on it).
  *   o_fine              : [B,H,Np,d] out, cube order.  Rows of pad slots are
