@@ -164,8 +164,8 @@ def stage_only(args, w, grid, sets, cube_sets, step):
         idx = [vsa.coarse(c["q"], c["k"], c["v"], grid, w.topk)[1] for c in cube_sets]
         out = torch.empty_like(cube_sets[0]["q"])
         if args.stage == "fine":
-            fn = lambda i: vsa.fine(cube_sets[i]["q"], cube_sets[i]["k"], cube_sets[i]["vt"],
-                                    idx[i], grid, out=out, v_transposed=True)
+            fn = lambda i: vsa.fine(cube_sets[i]["q"], cube_sets[i]["k"], cube_sets[i]["v"],
+                                    idx[i], grid, out=out)
         else:
             fn = lambda i: vsa.coarse(cube_sets[i]["q"], cube_sets[i]["k"], cube_sets[i]["v"],
                                       grid, w.topk)
@@ -195,8 +195,6 @@ def main():
     host_sets = [inputs.make_inputs(w, seed=s) for s in range(N_SETS)]
     sets = [{n: inputs.as_torch(h[n], w.dtype, dev) for n in "qkv"} for h in host_sets]
     cube_sets = [{n: vsa.reorder(s[n], grid) for n in "qkv"} for s in sets]
-    for c in cube_sets:   # the bf16 fine kernel reads V as transposed cubes
-        c["vt"] = vsa.transpose_cubes(c["v"], grid)
 
     plan = vsa.ForwardPlan(w.B, w.H, grid, w.d, w.topk, torch.bfloat16, dev)
     step = lambda i: plan.run(sets[i]["q"], sets[i]["k"], sets[i]["v"])
@@ -212,26 +210,21 @@ def main():
         _, idx = vsa.coarse(c["q"], c["k"], c["v"], grid, w.topk)
         idx_sets.append(idx)
     o_buf = torch.empty_like(cube_sets[0]["q"])
-    # the fine kernel alone (V already in transposed cubes, as vsa_forward's
-    # reorder leaves it), and vsa_fine as called on plain cube-order V
-    fine_step = lambda i: vsa.fine(cube_sets[i]["q"], cube_sets[i]["k"], cube_sets[i]["vt"],
-                                   idx_sets[i], grid, out=o_buf, v_transposed=True)
+    fine_step = lambda i: vsa.fine(cube_sets[i]["q"], cube_sets[i]["k"], cube_sets[i]["v"],
+                                   idx_sets[i], grid, out=o_buf)
     fine_ms = timed(fine_step, args.steps, args.warmup, N_SETS)
     fine_launch_ms = per_launch(fine_step, args.steps, args.warmup, N_SETS)
-    fine_api_ms = timed(lambda i: vsa.fine(cube_sets[i]["q"], cube_sets[i]["k"], cube_sets[i]["v"],
-                                           idx_sets[i], grid, out=o_buf),
-                        args.steps, args.warmup, N_SETS)
 
     def coarse_fine(i):
         c = cube_sets[i]
         _, idx = vsa.coarse(c["q"], c["k"], c["v"], grid, w.topk)
-        vsa.fine(c["q"], c["k"], c["vt"], idx, grid, out=o_buf, v_transposed=True)
+        vsa.fine(c["q"], c["k"], c["v"], idx, grid, out=o_buf)
     cf_ms = timed(coarse_fine, args.steps, args.warmup, N_SETS)
 
     # dense baseline: every cube selected, pad keys masked, same 7168-token sequence
     all_idx = torch.arange(w.C, dtype=torch.int32, device=dev).expand(w.B, w.H, w.C, w.C).contiguous()
-    dense_step = lambda i: vsa.fine(cube_sets[i]["q"], cube_sets[i]["k"], cube_sets[i]["vt"],
-                                    all_idx, grid, out=o_buf, v_transposed=True)
+    dense_step = lambda i: vsa.fine(cube_sets[i]["q"], cube_sets[i]["k"], cube_sets[i]["v"],
+                                    all_idx, grid, out=o_buf)
     dense_ms = timed(dense_step, max(10, args.steps // 8), max(2, args.warmup // 4), N_SETS)
 
     sweep = sparsity_sweep(args, dev)
@@ -265,7 +258,6 @@ def main():
         "warm_ms": round(warm_ms, 5),
         "fine_ms": round(fine_ms, 5),
         "fine_tflops": round(fine_tflops, 2),
-        "fine_api_ms": round(fine_api_ms, 5),
         "coarse_fine_ms": round(cf_ms, 5),
         "dense_fa_ms": round(dense_ms, 5),
         "speedup_fine_vs_dense": round(dense_ms / fine_ms, 3),
@@ -274,7 +266,7 @@ def main():
         "dense_tflops": round(fl_dense / (dense_ms * 1e-3) / 1e12, 2),
         "sweep": sweep,
         "fine_launch_ms": round(fine_launch_ms, 5),
-        "roofline": {"bound": "mfma", "kernel": "fine_fwd_bf16_kernel<128,false> (vsa_fine_vt)",
+        "roofline": {"bound": "mfma", "kernel": "fine_fwd_bf16_kernel<128,false> (vsa_fine)",
                      "achieved": round(launch_tflops, 2), "peak": flops.PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(launch_tflops / flops.PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic,

@@ -5,10 +5,9 @@ PyTorch binding.  Importing it does not load the library; the first call does,
 and fails loudly if the library is missing.
 """
 from .binding import (BackwardPlan, ForwardPlan, VSAFunction, backward, check_problem, coarse, cube_counts,
-                      fine, forward, make_problem, reorder, transpose_cubes, vsa_attention,
-                      workspace_bytes)
+                      fine, forward, make_problem, reorder, vsa_attention, workspace_bytes)
 from ._lib import VSAError, LIB_PATH
 
 __all__ = ["BackwardPlan", "ForwardPlan", "VSAFunction", "VSAError", "LIB_PATH", "backward", "check_problem",
            "coarse", "cube_counts", "fine", "forward", "make_problem", "reorder",
-           "transpose_cubes", "vsa_attention", "workspace_bytes"]
+           "vsa_attention", "workspace_bytes"]

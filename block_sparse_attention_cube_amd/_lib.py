@@ -27,7 +27,7 @@ VSA_OP_COARSE = 2
 VSA_OP_FINE = 3
 
 EXPORTS = ("vsa_workspace_bytes", "vsa_check_problem", "vsa_reorder", "vsa_coarse",
-           "vsa_fine", "vsa_fine_vt", "vsa_forward", "vsa_backward", "vsa_status_string")
+           "vsa_fine", "vsa_forward", "vsa_backward", "vsa_status_string")
 
 
 class VSAProblem(ctypes.Structure):
@@ -54,7 +54,6 @@ _SIG = {
     "vsa_reorder": (ctypes.c_int, [_P, _V, _V, ctypes.c_int, _V]),
     "vsa_coarse": (ctypes.c_int, [_P, _V, _V, _V, _V, _V, _V, _V, ctypes.c_size_t, _V]),
     "vsa_fine": (ctypes.c_int, [_P, _V, _V, _V, _V, _V, _V, _V, ctypes.c_size_t, _V]),
-    "vsa_fine_vt": (ctypes.c_int, [_P, _V, _V, _V, _V, _V, _V, _V]),
     "vsa_forward": (ctypes.c_int, [_P, _V, _V, _V, _V, _V, _V, _V, _V, ctypes.c_size_t, _V]),
     "vsa_backward": (ctypes.c_int, [_P, _V, _V, _V, _V, _V, _V, _V, _V, _V, _V, _V, _V,
                                     ctypes.c_size_t, _V]),

@@ -106,22 +106,6 @@ def reorder(x: torch.Tensor, grid: Grid, inverse: bool = False) -> torch.Tensor:
     return y
 
 
-def transpose_cubes(vcube: torch.Tensor, grid: Grid) -> torch.Tensor:
-    """Cube order [B,H,Np,d] -> transposed cube order (same shape and storage
-    size; per cube a [d][64] block), the V layout of fine(..., v_transposed=True).
-    bf16 only."""
-    _device_tensor(vcube, "vcube")
-    B, H, n, d = vcube.shape
-    C, Np = cube_counts(grid)
-    if n != Np:
-        raise ValueError(f"vcube has {n} rows, expected {Np}")
-    y = torch.empty_like(vcube)
-    prob = make_problem(B, H, grid, d, 1, vcube.dtype)
-    L.check(L.lib().vsa_reorder(ctypes.byref(prob), _ptr(vcube), _ptr(y), 2,
-                                _stream(vcube.device)), "vsa_reorder")
-    return y
-
-
 def coarse(qcube: torch.Tensor, kcube: torch.Tensor, vcube: torch.Tensor, grid: Grid,
            topk: int, return_scores: bool = False):
     """Coarse stage on cube-order inputs: (o_coarse [B,H,C,d], idx [B,H,C,K][, scores])."""
@@ -146,11 +130,8 @@ def coarse(qcube: torch.Tensor, kcube: torch.Tensor, vcube: torch.Tensor, grid: 
 
 
 def fine(qcube: torch.Tensor, kcube: torch.Tensor, vcube: torch.Tensor, idx: torch.Tensor,
-         grid: Grid, return_lse: bool = True, out: Optional[torch.Tensor] = None,
-         v_transposed: bool = False):
-    """Fine stage on cube-order inputs: (o_fine cube order [B,H,Np,d], lse [B,H,Np]).
-    With v_transposed, vcube is in transposed cube order (transpose_cubes) and
-    vsa_fine_vt runs (bf16)."""
+         grid: Grid, return_lse: bool = True, out: Optional[torch.Tensor] = None):
+    """Fine stage on cube-order inputs: (o_fine cube order [B,H,Np,d], lse [B,H,Np])."""
     _device_tensor(qcube, "qcube")
     B, H, Np_in, d = qcube.shape
     C, Np = cube_counts(grid)
@@ -167,10 +148,6 @@ def fine(qcube: torch.Tensor, kcube: torch.Tensor, vcube: torch.Tensor, idx: tor
     o = out if out is not None else torch.empty_like(qcube)
     _expect(o, qcube.shape, qcube.dtype, "out")
     lse = torch.empty((B, H, Np), dtype=torch.float32, device=dev) if return_lse else None
-    if v_transposed:
-        L.check(L.lib().vsa_fine_vt(ctypes.byref(prob), _ptr(qcube), _ptr(kcube), _ptr(vcube),
-                                    _ptr(idx), _ptr(o), _ptr(lse), _stream(dev)), "vsa_fine_vt")
-        return o, lse
     ws, nws = _workspace(prob, L.VSA_OP_FINE, dev)
     L.check(L.lib().vsa_fine(ctypes.byref(prob), _ptr(qcube), _ptr(kcube), _ptr(vcube),
                              _ptr(idx), _ptr(o), _ptr(lse), _ptr(ws), nws, _stream(dev)),

@@ -43,8 +43,9 @@ __device__ inline uint32_t hi_hi(uint32_t a, uint32_t b) { return __builtin_amdg
 __device__ inline float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ inline float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
-// Column of token kappa in a transposed row (see the forward kernel): the 8
-// tokens one lane feeds to an MFMA k-step end up in one 16-byte run.
+// Column of token kappa in a transposed row: tokens 32s + 16h + 4g + r go
+// to 32s + 8g + 4h + r, so the 8 tokens one lane feeds to an MFMA k-step
+// ({32s + 4g + r} and {32s + 16 + 4g + r}) end up in one 16-byte run.
 __device__ constexpr int tr_col(int kappa) {
   return (kappa & ~31) | (((kappa >> 2) & 3) << 3) | (((kappa >> 4) & 1) << 2) | (kappa & 3);
 }

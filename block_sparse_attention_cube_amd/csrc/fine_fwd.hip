@@ -3,17 +3,24 @@
 //
 // bf16 path (the hot loop), one workgroup = 4 waves = one query cube; wave w
 // owns query slots 16w..16w+15 and keeps its Q fragment in VGPRs.
-//   * Staging: K cubes (row major, [64][D]) and V^T cubes ([D][64], keys in
-//     vt_col order, written that way by the reorder) go from HBM/L2 straight
-//     into LDS with global_load_lds_dwordx4; no VGPRs, no VALU.  Each lane's
-//     source chunk is chosen so that LDS holds the tiles XOR-swizzled and
-//     the MFMA operand reads below hit 16 distinct bank groups.  K runs one
-//     key cube ahead of V in a 2-slot ring each (64 KB at D = 128).
+//   * Gather: q, k, v are read either in cube order (64 rows per cube) or
+//     straight from raster order, where slot (it, ih, iw) of a cube is row
+//     base(cube) + (it*Hh + ih)*Ww + iw, so no reordered copy is needed.
+//   * Staging: the 64 K rows and 64 V rows of a key cube go from HBM/L2
+//     straight into LDS with global_load_lds_dwordx4 (no VGPRs, no VALU).
+//     Each lane's source chunk is chosen so that LDS holds the tiles
+//     XOR-swizzled for the reads below; K runs one key cube ahead of V in a
+//     2-slot ring each (64 KB at D = 128).  Pad slots of a raster edge cube
+//     are redirected to the cube's first row (finite, masked).
 //   * S^T = K Q^T with v_mfma_f32_16x16x32_bf16: the accumulator then holds,
 //     per lane, 16 scores of ONE query row, which is the B-operand layout of
 //     O^T += V^T P^T, so probabilities go from the softmax straight into the
-//     PV MFMAs.  Pad key slots of an edge cube enter the first MFMA of each
-//     chain as a -inf accumulator, so no masking pass follows the product.
+//     PV MFMAs.  The V^T operand comes from row-major V by gfx950 transposed
+//     LDS reads (ds_read_b64_tr_b16).
+//   * Pad key slots: one accumulator init (0 / -inf) masks the (ih, iw) part
+//     for every key tile; tiles past the cube's t extent get a -inf offset in
+//     the exp2 argument.  Extents come from a per-lane table, one v_readlane
+//     per step, and the masks change only when the extent does.
 //   * Software pipeline per wave: while the MFMAs of S(n+1) run, the VALU
 //     evaluates exp2 of block n; while PV(n) runs, it scales S(n+1) into exp2
 //     units (t = s log2(e)/sqrt(d) - m) and takes its row max.  The running
@@ -37,6 +44,7 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -51,24 +59,38 @@ __device__ inline uint32_t pack_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2));  // RNE
 }
 
-// LDS geometry of one key cube.  A K row is D/8 16-byte chunks; chunk c of
-// row r is stored at chunk position c ^ ksw(r).  A V^T row (one head dim,
-// 64 keys) is 8 chunks stored at c ^ vsw(r).  With 256-byte K rows the
-// 16 rows an MFMA operand read touches land on 16 distinct chunk positions;
-// with 128-byte rows (V^T, and K at D = 64) two rows share a bank line and
-// the row pair index spreads them.
+// LDS geometry of one key cube: K and V tiles, both row major [64][D].
+// A row is D/8 16-byte chunks.
+//  * K is read 16 B per lane down 16 rows (MFMA A operand): chunk c of row r
+//    sits at c ^ ksw(r), which puts the 16 rows on 16 distinct chunk
+//    positions (256-byte rows) or spreads row pairs over the bank line
+//    (128-byte rows, D = 64).
+//  * V is read 8 B per lane by transposed reads, 16 rows x 32 bytes per
+//    half-wave: chunk c of row r sits at c ^ vsw(r), which makes those 16
+//    reads land on distinct bank positions.
 template <int D>
 struct FineTile {
-  static constexpr int kElems = 64 * D;            // elements of a K or V^T tile
-  static constexpr int kKC = D / 8;                // chunks per K row
+  static constexpr int kElems = 64 * D;            // elements of a K or V tile
+  static constexpr int kKC = D / 8;                // chunks per row
   static constexpr int kDma = kElems / (256 * 8);  // 16-byte DMA loads per thread per tile
   __device__ static constexpr int ksw(int r) { return kKC == 16 ? (r & 15) : ((r >> 1) & 7); }
-  __device__ static constexpr int vsw(int r) { return (r >> 1) & 7; }
+  __device__ static constexpr int vsw(int r) { return kKC == 16 ? 2 * (r & 7) : 2 * ((r >> 1) & 3); }
 };
 
-// Issues the DMA loads of one tile: thread t moves physical chunks
-// u*256 + t, whose source offsets (elements) were precomputed in off[].
-// The LDS destination of a load is wave-uniform; lane l lands at +16*l bytes.
+// Slot (it, ih, iw) of the u-th DMA chunk of thread (wave, lane): chunk
+// P = 256u + 64 wave + lane is row P / (D/8) of the tile.
+template <int D>
+__device__ __forceinline__ void dma_slot(int u, int wave, int lane, int& it, int& ih, int& iw) {
+  if (D == 128) {
+    it = u; ih = wave; iw = lane >> 4;
+  } else {
+    it = 2 * u + (wave >> 1); ih = ((wave & 1) << 1) | (lane >> 5); iw = (lane >> 3) & 3;
+  }
+}
+
+// Issues the DMA loads of one tile from src (the cube's first row): thread t
+// moves physical chunks u*256 + t, whose element offsets are in off[].  The
+// LDS destination of a load is wave-uniform; lane l lands at +16*l bytes.
 template <int D>
 __device__ __forceinline__ void dma_tile(const uint16_t* __restrict__ src, const int* off,
                                          uint16_t* slot, int wave) {
@@ -82,18 +104,33 @@ __device__ __forceinline__ void dma_tile(const uint16_t* __restrict__ src, const
 // Valid extent of a key cube packed as nt | nh << 3 | nw << 6 (each 1..4);
 // a full cube packs to kFullExt.
 constexpr int kFullExt = 4 | (4 << 3) | (4 << 6);
-__device__ __forceinline__ int packed_extent(const Geo& g, int c) {
-  const CubeExt e = cube_extent(g, c);
-  return e.nt | (e.nh << 3) | (e.nw << 6);
+
+// First input row (within its head) of cube c: 64c in cube order, the token
+// of slot (0, 0, 0) in raster order.
+template <bool RASTER>
+__device__ __forceinline__ int cube_row(const Geo& g, const CubeExt& e, int c) {
+  return RASTER ? ((4 * e.ct) * g.Hh + 4 * e.ch) * g.Ww + 4 * e.cw : 64 * c;
+}
+// Row offset of slot (it, ih, iw) from its cube's first row.
+template <bool RASTER>
+__device__ __forceinline__ int slot_row(const Geo& g, int it, int ih, int iw) {
+  return RASTER ? (it * g.Hh + ih) * g.Ww + iw : 16 * it + 4 * ih + iw;
 }
 
-// Extents of the key cubes sel[base .. base+63], one per lane, so that a
-// step reads its cube's extent with one v_readlane instead of scalar
-// divisions.
-__device__ __forceinline__ int lane_extents(const Geo& g, const int32_t* __restrict__ sel, int base,
-                                            int K, int lane) {
-  const int m = base + lane;
-  return m < K ? packed_extent(g, sel[m]) : kFullExt;
+// Extent and first row of the key cubes sel[first .. first+63], one per
+// lane, so that a step reads them with one v_readlane each.
+template <bool RASTER>
+__device__ __forceinline__ void lane_keys(const Geo& g, const int32_t* __restrict__ sel, int first,
+                                          int K, int lane, int& ext, int& row) {
+  ext = kFullExt;
+  row = 0;
+  const int m = first + lane;
+  if (m < K) {
+    const int c = sel[m];
+    const CubeExt e = cube_extent(g, c);
+    ext = e.nt | (e.nh << 3) | (e.nw << 6);
+    row = cube_row<RASTER>(g, e, c);
+  }
 }
 
 // Masking of pad key slots.  Lane (li, lg) element r of key tile kb is key
@@ -153,9 +190,12 @@ __device__ __forceinline__ void probabilities(const f32x4* t, u32x4* pf) {
 }
 
 // O^T[d][q] += V^T[d][keys] P^T[keys][q] and the row sums of P (MFMA
-// against ones).  A lane holds V^T[16dt + li][the same 8 keys as pf].
+// against ones).  The A operand of lane (li, lg) is V[key][16dt + li] for
+// the same 8 keys as pf: a transposed read hands 16 lanes a 16 x 4 block
+// supplied as 4 rows x 4 runs of 4 dims, lane s supplying row 4lg + s/4,
+// dims 16dt + 4(s%4) .. +3; vtr[dt] holds that address for key tile 0.
 template <int D>
-__device__ __forceinline__ void pv_tile(const uint16_t* vt_lds, const int* vro, const u32x4* pf,
+__device__ __forceinline__ void pv_tile(const uint16_t* v_lds, const int* vtr, const u32x4* pf,
                                         f32x4* oacc, f32x4& lacc) {
   const u32x4 ones = {0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u};  // bf16 1.0 x 8
 #pragma unroll
@@ -163,17 +203,25 @@ __device__ __forceinline__ void pv_tile(const uint16_t* vt_lds, const int* vro, 
     lacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ones), as_bf16x8(pf[s]), lacc, 0, 0, 0);
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt) {
-      const u32x4 a = *reinterpret_cast<const u32x4*>(vt_lds + vro[s] + dt * 16 * 64);
+      // keys 32s + 4lg + j (elements 0..3) and 32s + 16 + 4lg + j (elements 4..7)
+      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) i16x4*)(v_lds + vtr[dt] + (32 * s) * D));
+      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) i16x4*)(v_lds + vtr[dt] + (32 * s + 16) * D));
+      const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+      const u32x4 a = {l2[0], l2[1], h2[0], h2[1]};
       oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(pf[s]),
                                                          oacc[dt], 0, 0, 0);
     }
   }
 }
 
+// RASTER: q, k, v are raster [B,H,N,D] and o, o_coarse are raster;
+// otherwise q, k, v and o are cube order [B,H,Np,D].
 template <int D, bool RASTER>
 __global__ __launch_bounds__(256, 2) void fine_fwd_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
-    const uint16_t* __restrict__ vt, const int32_t* __restrict__ idx,
+    const uint16_t* __restrict__ v, const int32_t* __restrict__ idx,
     uint16_t* __restrict__ o, float* __restrict__ lse, const uint16_t* __restrict__ oc,
     uint16_t* __restrict__ o_coarse, Geo g) {
   using Tl = FineTile<D>;
@@ -184,7 +232,7 @@ __global__ __launch_bounds__(256, 2) void fine_fwd_bf16_kernel(
   constexpr int kOutReg = 64 * kKC / 256;  // 16-byte output chunks per thread
   constexpr int kOS = D + 8;               // padded row stride of the O staging tile
   constexpr float kTau = 8.0f;             // lazy rescale threshold (exp2 units)
-  __shared__ __attribute__((aligned(16))) uint16_t smem[4 * kT];   // K ring (2), V^T ring (2)
+  __shared__ __attribute__((aligned(16))) uint16_t smem[4 * kT];   // K ring (2), V ring (2)
   uint16_t* const kring = smem;
   uint16_t* const vring = smem + 2 * kT;
 
@@ -197,47 +245,85 @@ __global__ __launch_bounds__(256, 2) void fine_fwd_bf16_kernel(
   const int K = g.K;
   const int32_t* __restrict__ sel = idx + static_cast<int64_t>(tile) * K;
   const float c2 = inv_sqrt_d<D>() * kLog2e;
-  const int64_t kv0 = bh * g.Np * D;
-  auto cube = [&](int n) { return kv0 + static_cast<int64_t>(sel[n]) * 64 * D; };
+  const int64_t head0 = bh * (RASTER ? g.N : g.Np) * D;   // element offset of this head's rows
+  const uint16_t* const kh = k + head0;
+  const uint16_t* const vh = v + head0;
 
-  // DMA source offsets of this thread's chunks (loop invariant)
-  int koff[Tl::kDma], voff[Tl::kDma];
+  // DMA offsets (elements, from the cube's first row) of this thread's
+  // chunks; *alt: the same chunk of the cube's first row, for pad slots of
+  // raster edge cubes
+  int koff[Tl::kDma], voff[Tl::kDma], kalt[Tl::kDma], valt[Tl::kDma];
 #pragma unroll
   for (int u = 0; u < Tl::kDma; ++u) {
     const int P = u * 256 + tid;
-    const int kr = P / kKC, vr = P / 8;
-    koff[u] = kr * D + (((P % kKC) ^ Tl::ksw(kr)) * 8);
-    voff[u] = vr * 64 + (((P % 8) ^ Tl::vsw(vr)) * 8);
+    const int r = P / kKC, c = P % kKC;
+    int it, ih, iw;
+    dma_slot<D>(u, wave, lane, it, ih, iw);
+    const int rowoff = slot_row<RASTER>(g, it, ih, iw) * D;
+    kalt[u] = ((c ^ Tl::ksw(r)) * 8);
+    valt[u] = ((c ^ Tl::vsw(r)) * 8);
+    koff[u] = rowoff + kalt[u];
+    voff[u] = rowoff + valt[u];
   }
+  // stage K or V of a key cube (first row `row`, packed extent `ext`)
+  auto stage = [&](const uint16_t* src, const int* off, const int* alt, int row, int ext,
+                   uint16_t* slot) {
+    if (RASTER && ext != kFullExt) {
+      const int nt = ext & 7, nh = (ext >> 3) & 7, nw = ext >> 6;
+      int eoff[Tl::kDma];
+#pragma unroll
+      for (int u = 0; u < Tl::kDma; ++u) {
+        int it, ih, iw;
+        dma_slot<D>(u, wave, lane, it, ih, iw);
+        eoff[u] = (it < nt && ih < nh && iw < nw) ? off[u] : alt[u];
+      }
+      dma_tile<D>(src + static_cast<int64_t>(row) * D, eoff, slot, wave);
+    } else {
+      dma_tile<D>(src + static_cast<int64_t>(row) * D, off, slot, wave);
+    }
+  };
+
   // Q fragment: B operand of S^T, lane holds Q[slot 16w+li][32ks + 8lg .. +7]
   u32x4 qf[kKS];
+  const CubeExt eq = cube_extent(g, qc);
   {
-    const uint16_t* qrow = q + (bh * g.Np + static_cast<int64_t>(qc) * 64 + wave * 16 + li) * D;
+    const int it = wave, ih = li >> 2, iw = li & 3;
+    const bool valid = !RASTER || (it < eq.nt && ih < eq.nh && iw < eq.nw);
+    const int row = cube_row<RASTER>(g, eq, qc) + (valid ? slot_row<RASTER>(g, it, ih, iw) : 0);
+    const uint16_t* qrow = q + head0 + static_cast<int64_t>(row) * D;
 #pragma unroll
     for (int ks = 0; ks < kKS; ++ks) qf[ks] = *reinterpret_cast<const u32x4*>(qrow + 32 * ks + 8 * lg);
   }
-  // per-lane LDS element offsets of the MFMA operand reads (loop invariant)
-  int kro[kKS], vro[2];
+  // per-lane LDS element offsets of the operand reads (loop invariant)
+  int kro[kKS], vtr[kDT];
 #pragma unroll
   for (int ks = 0; ks < kKS; ++ks) kro[ks] = li * D + (((4 * ks + lg) ^ Tl::ksw(li)) * 8);
+  {
+    const int r = 4 * lg + (li >> 2);        // V row of key tile 0 this lane supplies
 #pragma unroll
-  for (int s = 0; s < 2; ++s) vro[s] = li * 64 + (((4 * s + lg) ^ Tl::vsw(li)) * 8);
+    for (int dt = 0; dt < kDT; ++dt)
+      vtr[dt] = r * D + (((2 * dt + ((li & 3) >> 1)) ^ Tl::vsw(r)) * 8) + (li & 1) * 4;
+  }
 
   f32x4 oacc[kDT];
 #pragma unroll
   for (int dt = 0; dt < kDT; ++dt) oacc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   f32x4 lacc = {0.f, 0.f, 0.f, 0.f};
 
+  // key cube extents and first rows, 64 steps per lane vector
+  int ext_lanes, row_lanes;
+  lane_keys<RASTER>(g, sel, 0, K, lane, ext_lanes, row_lanes);
+  auto key_ext = [&](int n) { return __builtin_amdgcn_readlane(ext_lanes, n & 63); };
+  auto key_row = [&](int n) { return __builtin_amdgcn_readlane(row_lanes, n & 63); };
+
   // prologue: K(0), V(0), K(1) in flight together; S(0) and its row max
-  dma_tile<D>(k + cube(0), koff, kring, wave);
-  dma_tile<D>(vt + cube(0), voff, vring, wave);
-  if (K > 1) dma_tile<D>(k + cube(1), koff, kring + kT, wave);
+  const int ext0 = key_ext(0);
+  stage(kh, koff, kalt, key_row(0), ext0, kring);
+  stage(vh, voff, valt, key_row(0), ext0, vring);
+  if (K > 1) stage(kh, koff, kalt, key_row(1), key_ext(1), kring + kT);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
-  // key cube extents, 64 steps per lane vector; the masks follow the extent
-  // and are rebuilt only when it changes
-  int ext_lanes = lane_extents(g, sel, 0, K, lane);
-  const int ext0 = __builtin_amdgcn_readlane(ext_lanes, 0);
+  // the masks follow the key cube's extent and are rebuilt only when it changes
   int hw_cur = ext0 >> 3, nt_cur = ext0 & 7;
   f32x4 bias = hw_bias(ext0, lg);
   f32x4 tcur[4];
@@ -245,7 +331,8 @@ __global__ __launch_bounds__(256, 2) void fine_fwd_bf16_kernel(
   float mb;     // running row max, exp2 units
   float mbk[4]; // exp2 offset of key tile kb: -mb, or -inf for tiles past the cube's t extent
 #pragma unroll
-  for (int kb = 0; kb < 4; ++kb) tcur[kb] = kb < nt_cur ? tcur[kb] * c2 : f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+  for (int kb = 0; kb < 4; ++kb)
+    tcur[kb] = kb < nt_cur ? tcur[kb] * c2 : f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
   mb = row_max(tcur);
 #pragma unroll
   for (int kb = 0; kb < 4; ++kb) {
@@ -257,10 +344,12 @@ __global__ __launch_bounds__(256, 2) void fine_fwd_bf16_kernel(
     // K(n+1) and V(n) have landed for every wave; slots of K(n), V(n-1) are free
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    dma_tile<D>(vt + cube(n + 1), voff, vring + ((n + 1) & 1) * kT, wave);
-    if (n + 2 < K) dma_tile<D>(k + cube(n + 2), koff, kring + (n & 1) * kT, wave);
-    if (((n + 1) & 63) == 0) ext_lanes = lane_extents(g, sel, n + 1, K, lane);
-    const int ext = __builtin_amdgcn_readlane(ext_lanes, (n + 1) & 63);
+    const int ext = key_ext(n + 1);
+    stage(vh, voff, valt, key_row(n + 1), ext, vring + ((n + 1) & 1) * kT);
+    if (n + 2 < K) {
+      if (((n + 2) & 63) == 0) lane_keys<RASTER>(g, sel, n + 2, K, lane, ext_lanes, row_lanes);
+      stage(kh, koff, kalt, key_row(n + 2), key_ext(n + 2), kring + (n & 1) * kT);
+    }
     if ((ext >> 3) != hw_cur) {
       hw_cur = ext >> 3;
       bias = hw_bias(ext, lg);
@@ -276,7 +365,7 @@ __global__ __launch_bounds__(256, 2) void fine_fwd_bf16_kernel(
     u32x4 pf[2];
     probabilities(tcur, pf);
     // PV(n) while S(n+1) is scaled into exp2 units and reduced
-    pv_tile<D>(vring + (n & 1) * kT, vro, pf, oacc, lacc);
+    pv_tile<D>(vring + (n & 1) * kT, vtr, pf, oacc, lacc);
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
@@ -304,7 +393,7 @@ __global__ __launch_bounds__(256, 2) void fine_fwd_bf16_kernel(
     __syncthreads();
     u32x4 pf[2];
     probabilities(tcur, pf);
-    pv_tile<D>(vring + ((K - 1) & 1) * kT, vro, pf, oacc, lacc);
+    pv_tile<D>(vring + ((K - 1) & 1) * kT, vtr, pf, oacc, lacc);
   }
   __syncthreads();   // every wave is done with the rings: reuse them for O
 
@@ -323,7 +412,6 @@ __global__ __launch_bounds__(256, 2) void fine_fwd_bf16_kernel(
     *reinterpret_cast<u32x2*>(o_lds + (wave * 16 + li) * kOS + 16 * dt + 4 * lg) = w;
   }
   __syncthreads();
-  const CubeExt eq = cube_extent(g, qc);
 #pragma unroll
   for (int u = 0; u < kOutReg; ++u) {
     const int ch = tid + 256 * u, row = ch / kKC, c = ch % kKC;

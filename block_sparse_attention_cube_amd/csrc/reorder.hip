@@ -42,10 +42,8 @@ struct ChunkOps<float> {
 // MODE 0: raster -> cube (pads written as zero), optional means.
 // MODE 1: cube -> raster (pads dropped).
 // MODE 2: cube -> means only.
-// MODE 3: cube -> transposed cube (bf16).
-// In modes 0 and 3 a bf16 tensor flagged in b.transposed is written as V^T
-// cubes: the 64 rows are staged in LDS and every thread then gathers 8 keys
-// of one dim (vt_col order) into one 16-byte store.
+// MODE 3: raster -> means only (the pooling pass of a forward that gathers
+//         q, k, v straight from raster rows).
 template <typename T, int D, int MODE>
 __global__ __launch_bounds__(256) void reorder_kernel(ReorderBatch b, Geo g) {
   using Ops = ChunkOps<T>;
@@ -68,8 +66,6 @@ __global__ __launch_bounds__(256) void reorder_kernel(ReorderBatch b, Geo g) {
   float acc[kE];
 #pragma unroll
   for (int i = 0; i < kE; ++i) acc[i] = 0.f;
-  const bool to_vt = (MODE == 0 || MODE == 3) && sizeof(T) == 2 && ((b.transposed >> tensor) & 1);
-  __shared__ __attribute__((aligned(16))) T rows_lds[kSlots * D];
 
 #pragma unroll
   for (int u = 0; u < kPasses; ++u) {
@@ -78,14 +74,8 @@ __global__ __launch_bounds__(256) void reorder_kernel(ReorderBatch b, Geo g) {
     const int64_t crow = bh * g.Np + (int64_t)c * kSlots + s;
     if (MODE == 0 || MODE == 3) {
       uint4 val = make_uint4(0u, 0u, 0u, 0u);
-      if (r >= 0) {
-        const T* src = (MODE == 0) ? x + (bh * g.N + r) * D : x + crow * D;
-        val = *reinterpret_cast<const uint4*>(src + chunk * kE);
-      }
-      if (to_vt)
-        *reinterpret_cast<uint4*>(rows_lds + s * D + chunk * kE) = val;
-      else
-        *reinterpret_cast<uint4*>(y + crow * D + chunk * kE) = val;
+      if (r >= 0) val = *reinterpret_cast<const uint4*>(x + (bh * g.N + r) * D + chunk * kE);
+      if (MODE == 0) *reinterpret_cast<uint4*>(y + crow * D + chunk * kE) = val;
       Ops::add(val, acc);
     } else if (MODE == 1) {
       if (r >= 0) {
@@ -97,24 +87,6 @@ __global__ __launch_bounds__(256) void reorder_kernel(ReorderBatch b, Geo g) {
         const uint4 val = *reinterpret_cast<const uint4*>(x + crow * D + chunk * kE);
         Ops::add(val, acc);
       }
-    }
-  }
-
-  if (to_vt) {  // uniform across the workgroup
-    __syncthreads();
-    const uint16_t* rl = reinterpret_cast<const uint16_t*>(rows_lds);
-    uint16_t* yt = reinterpret_cast<uint16_t*>(y) + (bh * g.Np + (int64_t)c * kSlots) * D;
-    // D rows x 8 chunks of 8 keys; thread handles chunks tid, tid + 256, ...
-    for (int ch = tid; ch < D * 8; ch += 256) {
-      const int d = ch >> 3, p0 = (ch & 7) * 8;
-      uint32_t w[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const uint32_t lo = rl[vt_key(p0 + 2 * i) * D + d];
-        const uint32_t hi = rl[vt_key(p0 + 2 * i + 1) * D + d];
-        w[i] = lo | (hi << 16);
-      }
-      *reinterpret_cast<uint4*>(yt + d * kSlots + p0) = make_uint4(w[0], w[1], w[2], w[3]);
     }
   }
 

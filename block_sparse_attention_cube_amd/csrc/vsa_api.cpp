@@ -58,18 +58,23 @@ struct Carver {
 };
 
 struct FwdWs {
-  void* qc; void* kc; void* vc;
+  void* qc; void* kc; void* vc;   // fp32 only: cube-order copies
   float* qm; float* km; float* vm;
   void* oc;
 };
+// bf16: the fine kernel gathers q, k, v from raster rows, so the forward
+// keeps only the per-cube means and O_coarse; fp32 also keeps cube-order
+// copies of q, k, v.
 FwdWs carve_forward(const vsa_problem* p, void* ws, size_t* total) {
   const Geo g = geometry(p);
   const size_t e = elem_bytes(p);
   const size_t cube = size_t(g.B) * g.H * g.Np * g.D * e;
   const size_t mean = size_t(g.B) * g.H * g.C * g.D * sizeof(float);
   Carver c(ws);
-  FwdWs w;
-  w.qc = c.take(cube); w.kc = c.take(cube); w.vc = c.take(cube);
+  FwdWs w = {};
+  if (p->dtype != VSA_BF16) {
+    w.qc = c.take(cube); w.kc = c.take(cube); w.vc = c.take(cube);
+  }
   w.qm = static_cast<float*>(c.take(mean));
   w.km = static_cast<float*>(c.take(mean));
   w.vm = static_cast<float*>(c.take(mean));
@@ -170,10 +175,7 @@ size_t vsa_workspace_bytes(const vsa_problem* p, int op) {
   switch (op) {
     case VSA_OP_FORWARD: carve_forward(p, nullptr, &total); return total;
     case VSA_OP_COARSE: carve_coarse(p, nullptr, &total); return total;
-    case VSA_OP_FINE:  // bf16: V re-laid out as transposed cubes for the MFMA kernel
-      return p->dtype == VSA_BF16
-                 ? round_up(size_t(p->B) * p->H * geometry(p).Np * p->d * sizeof(uint16_t))
-                 : 0;
+    case VSA_OP_FINE: return 0;
     case VSA_OP_BACKWARD:
       if (check_backward(p) != VSA_OK) return 0;
       carve_backward(p, nullptr, &total);
@@ -201,16 +203,13 @@ vsa_status vsa_reorder(const vsa_problem* p, const void* x, void* y, int inverse
   vsa_status st = check(p);
   if (st != VSA_OK) return st;
   if ((st = pointers({x, y}, {})) != VSA_OK) return st;
-  if (inverse < 0 || inverse > 2) return VSA_ERR_UNSUPPORTED;
-  if (inverse == 2 && p->dtype != VSA_BF16) return VSA_ERR_UNSUPPORTED;
+  if (inverse != 0 && inverse != 1) return VSA_ERR_UNSUPPORTED;
   const Geo g = geometry(p);
   vsa::ReorderBatch b = {};
   b.x[0] = x;
   b.y[0] = y;
   b.count = 1;
-  b.transposed = inverse == 2 ? 1 : 0;
-  const int mode = inverse == 0 ? 0 : (inverse == 1 ? 1 : 3);
-  return launched(vsa::launch_reorder(g, p->dtype, mode, b, stream));
+  return launched(vsa::launch_reorder(g, p->dtype, inverse, b, stream));
 }
 
 vsa_status vsa_coarse(const vsa_problem* p, const void* qcube, const void* kcube,
@@ -240,33 +239,8 @@ vsa_status vsa_fine(const vsa_problem* p, const void* qcube, const void* kcube,
   if ((st = pointers({qcube, kcube, vcube, idx, o_fine}, {lse})) != VSA_OK) return st;
   if ((st = workspace(p, VSA_OP_FINE, ws, ws_bytes)) != VSA_OK) return st;
   const Geo g = geometry(p);
-  const void* v = vcube;
-  hipError_t e = hipSuccess;
-  if (p->dtype == VSA_BF16) {   // the bf16 kernel reads V^T cubes
-    vsa::ReorderBatch b = {};
-    b.x[0] = vcube;
-    b.y[0] = ws;
-    b.count = 1;
-    b.transposed = 1;
-    e = vsa::launch_reorder(g, p->dtype, 3, b, stream);
-    v = ws;
-  }
-  if (e == hipSuccess)
-    e = vsa::launch_fine(g, p->dtype, qcube, kcube, v, idx, o_fine, lse,
-                         /*raster_out=*/false, nullptr, nullptr, stream);
-  return launched(e);
-}
-
-vsa_status vsa_fine_vt(const vsa_problem* p, const void* qcube, const void* kcube,
-                       const void* vtcube, const int32_t* idx, void* o_fine, float* lse,
-                       hipStream_t stream) {
-  vsa_status st = check(p);
-  if (st != VSA_OK) return st;
-  if (p->dtype != VSA_BF16) return VSA_ERR_UNSUPPORTED;
-  if ((st = pointers({qcube, kcube, vtcube, idx, o_fine}, {lse})) != VSA_OK) return st;
-  const Geo g = geometry(p);
-  return launched(vsa::launch_fine(g, p->dtype, qcube, kcube, vtcube, idx, o_fine, lse,
-                                   /*raster_out=*/false, nullptr, nullptr, stream));
+  return launched(vsa::launch_fine(g, p->dtype, qcube, kcube, vcube, idx, o_fine, lse,
+                                   /*raster=*/false, nullptr, nullptr, stream));
 }
 
 vsa_status vsa_forward(const vsa_problem* p, const void* q, const void* k, const void* v,
@@ -278,18 +252,19 @@ vsa_status vsa_forward(const vsa_problem* p, const void* q, const void* k, const
   if ((st = workspace(p, VSA_OP_FORWARD, ws, ws_bytes)) != VSA_OK) return st;
   const Geo g = geometry(p);
   const FwdWs w = carve_forward(p, ws, nullptr);
+  const bool bf16 = p->dtype == VSA_BF16;
   vsa::ReorderBatch b = {};
   b.x[0] = q; b.x[1] = k; b.x[2] = v;
   b.y[0] = w.qc; b.y[1] = w.kc; b.y[2] = w.vc;
   b.mean[0] = w.qm; b.mean[1] = w.km; b.mean[2] = w.vm;
   b.count = 3;
-  b.transposed = p->dtype == VSA_BF16 ? 4 : 0;   // bf16 V goes out as V^T cubes
-  hipError_t e = vsa::launch_reorder(g, p->dtype, 0, b, stream);
+  // bf16: pool only (the fine kernel gathers from raster); fp32: cube-order copies + means
+  hipError_t e = vsa::launch_reorder(g, p->dtype, bf16 ? 3 : 0, b, stream);
   if (e == hipSuccess)
     e = vsa::launch_coarse(g, p->dtype, w.qm, w.km, w.vm, w.oc, idx, nullptr, stream);
   if (e == hipSuccess)
-    e = vsa::launch_fine(g, p->dtype, w.qc, w.kc, w.vc, idx, o_fine, lse,
-                         /*raster_out=*/true, w.oc, o_coarse, stream);
+    e = vsa::launch_fine(g, p->dtype, bf16 ? q : w.qc, bf16 ? k : w.kc, bf16 ? v : w.vc, idx,
+                         o_fine, lse, /*raster=*/true, w.oc, o_coarse, stream);
   return launched(e);
 }
 

@@ -84,28 +84,14 @@ hipError_t launch_kernel(void (*k)(P...), dim3 grid, dim3 block, size_t lds_byte
 // ---- launchers (each returns the first HIP launch error, or hipSuccess) ----
 
 // mode 0: raster -> cube order (+ optional fp32 means), mode 1: cube -> raster,
-// mode 2: cube order -> fp32 means only, mode 3: cube order -> transposed
-// cube order.  Up to 3 tensors per launch.  Tensor t with bit t of
-// `transposed` set (bf16, modes 0 and 3) is written as V^T cubes: per cube a
-// [D][64] block whose row d holds the 64 keys in vt_col order.
+// mode 2: cube order -> fp32 means only, mode 3: raster -> fp32 means only.
+// Up to 3 tensors per launch.
 struct ReorderBatch {
   const void* x[3];
   void* y[3];
   float* mean[3];
   int count;
-  int transposed;
 };
-
-// Column of key kappa inside a transposed cube row.  Keys 32s + 16h + 4g + r
-// go to 32s + 8g + 4h + r, so the 8 keys one lane feeds to a PV MFMA k-step
-// ({32s + 4g + r} and {32s + 16 + 4g + r}, r = 0..3) sit in one 16-byte run.
-__host__ __device__ constexpr int vt_col(int kappa) {
-  return (kappa & ~31) | (((kappa >> 2) & 3) << 3) | (((kappa >> 4) & 1) << 2) | (kappa & 3);
-}
-// Key held by column p of a transposed cube row (inverse of vt_col).
-__host__ __device__ constexpr int vt_key(int p) {
-  return (p & ~31) | (((p >> 2) & 1) << 4) | (((p >> 3) & 3) << 2) | (p & 3);
-}
 hipError_t launch_reorder(const Geo& g, int dtype, int mode, const ReorderBatch& b,
                           hipStream_t s);
 
@@ -115,14 +101,13 @@ hipError_t launch_coarse(const Geo& g, int dtype, const float* qm, const float* 
                          const float* vm, void* oc, int32_t* idx, float* scores,
                          hipStream_t s);
 
-// Fine stage on cube-order q, k.  v is cube order [B,H,Np,D] for fp32 and
-// transposed cube order (per cube [D][64], keys in vt_col order, as the
-// reorder writes it for flagged tensors) for bf16.
-// raster_out = false: o is cube order [B,H,Np,D];
-// raster_out = true: o is raster [B,H,N,D] and, if oc != nullptr, o_coarse
-// (raster) receives the per-cube coarse row of every valid token.
+// Fine stage.  raster = false: q, k, v and o are cube order [B,H,Np,D].
+// raster = true: o is raster [B,H,N,D] and, if oc != nullptr, o_coarse
+// (raster) receives the per-cube coarse row of every valid token; q, k, v
+// are raster [B,H,N,D] for bf16 (gathered by cube in the kernel) and cube
+// order for fp32.
 hipError_t launch_fine(const Geo& g, int dtype, const void* q, const void* k, const void* v,
-                       const int32_t* idx, void* o, float* lse, bool raster_out,
+                       const int32_t* idx, void* o, float* lse, bool raster,
                        const void* oc, void* o_coarse, hipStream_t s);
 
 }  // namespace vsa

@@ -100,13 +100,8 @@ vsa_status vsa_check_problem(const vsa_problem* p);
  *                y are written as zero.
  *   inverse = 1: x cube order [B,H,Np,d] -> y raster [B,H,N,d]; pad slots of
  *                x are ignored.
- *   inverse = 2: x cube order [B,H,Np,d] -> y transposed cube order, the V
- *                layout of vsa_fine_vt (VSA_BF16 only): per cube c a [d][64]
- *                block at element offset (b*H + h)*Np*d + 64*c*d whose row i
- *                holds dim i of the cube's 64 slots, slot 32s + 16u + 4g + r
- *                (s, u in {0,1}; g, r in 0..3) at column 32s + 8g + 4u + r.
  * A pure permutation: bit-exact.  x and y must not overlap.  Any other
- * inverse value, or inverse = 2 on VSA_F32, returns VSA_ERR_UNSUPPORTED. */
+ * inverse value returns VSA_ERR_UNSUPPORTED. */
 vsa_status vsa_reorder(const vsa_problem* p, const void* x, void* y, int inverse,
                        hipStream_t stream);
 
@@ -134,21 +129,13 @@ vsa_status vsa_coarse(const vsa_problem* p, const void* qcube, const void* kcube
  *                         written with unspecified values.
  *   lse                 : [B,H,Np] fp32 out (natural log), or NULL.
  *   ws, ws_bytes        : workspace of vsa_workspace_bytes(p, VSA_OP_FINE)
- *                         (bf16: room for a transposed copy of vcube; fp32: 0).
+ *                         (currently 0 bytes; ws may then be NULL).
  * bf16 inputs use bf16 MFMA with fp32 accumulation and fp32 softmax; fp32
  * inputs are computed in fp32 throughout.  Entries of idx outside [0, C) are
  * not checked on the device; they are the caller's error. */
 vsa_status vsa_fine(const vsa_problem* p, const void* qcube, const void* kcube,
                     const void* vcube, const int32_t* idx, void* o_fine, float* lse,
                     void* ws, size_t ws_bytes, hipStream_t stream);
-
-/* vsa_fine with V already in transposed cube order (vsa_reorder inverse = 2),
- * for callers that keep V in that layout: no workspace, no transposition
- * pass.  VSA_BF16 only (else VSA_ERR_UNSUPPORTED); arguments otherwise as
- * vsa_fine. */
-vsa_status vsa_fine_vt(const vsa_problem* p, const void* qcube, const void* kcube,
-                       const void* vtcube, const int32_t* idx, void* o_fine, float* lse,
-                       hipStream_t stream);
 
 /* Whole forward on raster tensors: reorder + coarse + fine + inverse reorder
  * (the drop-in for FlashAttention of the section on why sparse attention

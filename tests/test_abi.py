@@ -66,14 +66,13 @@ def test_workspace_sizes():
     p = prob()
     lib = L.lib()
     fwd = lib.vsa_workspace_bytes(ctypes.byref(p), L.VSA_OP_FORWARD)
-    # cube-order q, k, v (bf16) + fp32 means of q, k, v + per-cube coarse output
-    assert fwd >= 3 * 12 * 7168 * 128 * 2 + 3 * 12 * 112 * 128 * 4 + 12 * 112 * 128 * 2
+    # bf16: fp32 means of q, k, v + per-cube coarse output (q, k, v are gathered
+    # from raster rows); fp32 adds cube-order copies of q, k, v
+    assert fwd >= 3 * 12 * 112 * 128 * 4 + 12 * 112 * 128 * 2
+    fwd32 = lib.vsa_workspace_bytes(ctypes.byref(prob(dtype=L.VSA_F32)), L.VSA_OP_FORWARD)
+    assert fwd32 >= 3 * 12 * 7168 * 128 * 4 + 3 * 12 * 112 * 128 * 4 + 12 * 112 * 128 * 4
     assert lib.vsa_workspace_bytes(ctypes.byref(p), L.VSA_OP_COARSE) >= 3 * 12 * 112 * 128 * 4
-    # bf16 fine stage: one transposed copy of the cube-order V; fp32 needs none
-    assert lib.vsa_workspace_bytes(ctypes.byref(p), L.VSA_OP_FINE) >= 12 * 7168 * 128 * 2
-    p32 = prob()
-    p32.dtype = L.VSA_F32
-    assert lib.vsa_workspace_bytes(ctypes.byref(p32), L.VSA_OP_FINE) == 0
+    assert lib.vsa_workspace_bytes(ctypes.byref(p), L.VSA_OP_FINE) == 0
     assert lib.vsa_workspace_bytes(ctypes.byref(p), 99) == 0
 
 
@@ -114,25 +113,11 @@ def test_other_entry_points_validate_first():
                             FAKE, FAKE, FAKE, FAKE, big, None) == L.VSA_ERR_NULL
 
 
-def test_transposed_v_entry_points_validate_first():
+def test_reorder_direction_codes():
     lib = L.lib()
-    p, p32 = prob(), prob(dtype=L.VSA_F32)
-    # reorder direction codes: 0, 1, 2 (2 = transposed cubes, bf16 only)
-    assert lib.vsa_reorder(ctypes.byref(p), FAKE, FAKE, 3, None) == L.VSA_ERR_UNSUPPORTED
+    p = prob()
+    assert lib.vsa_reorder(ctypes.byref(p), FAKE, FAKE, 2, None) == L.VSA_ERR_UNSUPPORTED
     assert lib.vsa_reorder(ctypes.byref(p), FAKE, FAKE, -1, None) == L.VSA_ERR_UNSUPPORTED
-    assert lib.vsa_reorder(ctypes.byref(p32), FAKE, FAKE, 2, None) == L.VSA_ERR_UNSUPPORTED
-    assert lib.vsa_fine_vt(ctypes.byref(p32), FAKE, FAKE, FAKE, FAKE, FAKE, None,
-                           None) == L.VSA_ERR_UNSUPPORTED
-    assert lib.vsa_fine_vt(ctypes.byref(p), FAKE, FAKE, None, FAKE, FAKE, None,
-                           None) == L.VSA_ERR_NULL
-    assert lib.vsa_fine_vt(ctypes.byref(p), FAKE, MISALIGNED, FAKE, FAKE, FAKE, None,
-                           None) == L.VSA_ERR_ALIGN
-    assert lib.vsa_fine_vt(None, FAKE, FAKE, FAKE, FAKE, FAKE, None, None) == L.VSA_ERR_NULL
-    # the bf16 vsa_fine needs its workspace (room for V^T)
-    assert lib.vsa_fine(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, None, None, 0,
-                        None) == L.VSA_ERR_NULL
-    assert lib.vsa_fine(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, 16,
-                        None) == L.VSA_ERR_WORKSPACE
 
 
 def test_status_strings():

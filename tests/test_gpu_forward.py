@@ -74,45 +74,6 @@ def test_reorder_is_bit_exact(w, cache):
     assert torch.equal(back, q)
 
 
-BF16 = [w for w in CASES if w.dtype == "bf16"]
-
-
-def transposed_columns():
-    """Column of each cube slot in the transposed cube layout of vsa_reorder
-    (inverse = 2): slot 32s + 16u + 4g + r sits at column 32s + 8g + 4u + r."""
-    col = np.empty(64, dtype=np.int64)
-    for s_ in range(2):
-        for u in range(2):
-            for g_ in range(4):
-                for r in range(4):
-                    col[32 * s_ + 16 * u + 4 * g_ + r] = 32 * s_ + 8 * g_ + 4 * u + r
-    return col
-
-
-@pytest.mark.parametrize("w", BF16, ids=ids(BF16))
-def test_transposed_cubes_layout(w, cache):
-    x, _, (_, _, vc), ref = case_data(w, cache)
-    vt = vsa.transpose_cubes(vc, grid(w))
-    torch.cuda.synchronize()
-    B, H, Np, d = vc.shape
-    C = Np // 64
-    got = vt.view(torch.int16).cpu().numpy().reshape(B, H, C, d, 64)
-    src = vc.view(torch.int16).cpu().numpy().reshape(B, H, C, 64, d)
-    want = np.empty_like(got)
-    want[..., transposed_columns()] = np.swapaxes(src, -1, -2)
-    np.testing.assert_array_equal(got, want)
-
-
-@pytest.mark.parametrize("w", BF16, ids=ids(BF16))
-def test_fine_on_transposed_v_matches_fine(w, cache):
-    x, _, (qc, kc, vc), ref = case_data(w, cache)
-    idx = torch.from_numpy(ref["idx"]).to(DEV)
-    o1, l1 = vsa.fine(qc, kc, vc, idx, grid(w))
-    o2, l2 = vsa.fine(qc, kc, vsa.transpose_cubes(vc, grid(w)), idx, grid(w), v_transposed=True)
-    torch.cuda.synchronize()
-    assert torch.equal(o1, o2) and torch.equal(l1, l2)
-
-
 @pytest.mark.parametrize("w", CASES, ids=ids(CASES))
 def test_coarse_scores_selection_and_output(w, cache):
     x, _, (qc, kc, vc), ref = case_data(w, cache)
