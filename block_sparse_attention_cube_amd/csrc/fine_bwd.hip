@@ -13,8 +13,10 @@
 //
 // Both kernels follow the forward's MFMA layouts (v_mfma_f32_16x16x32_bf16,
 // scores kept in the accumulator layout of the transposed product so that
-// probabilities feed the next MFMA straight from registers); operands whose
-// contraction index is the token index are staged transposed in LDS.
+// probabilities feed the next MFMA straight from registers).  Tiles reach
+// LDS by DMA (global_load_lds) in a 2-slot ring, one barrier per step;
+// operands contracted over the token index come from the row-major tiles
+// through gfx950 transposed LDS reads (ds_read_b64_tr_b16).
 #include "vsa_internal.h"
 #include "vsa_bwd.h"
 
@@ -38,67 +40,71 @@ __device__ inline uint32_t pack_bf16x2(float a, float b) {
   const f32x2 f = {a, b};
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2));
 }
-__device__ inline uint32_t lo_lo(uint32_t a, uint32_t b) { return __builtin_amdgcn_perm(b, a, 0x05040100u); }
-__device__ inline uint32_t hi_hi(uint32_t a, uint32_t b) { return __builtin_amdgcn_perm(b, a, 0x07060302u); }
 __device__ inline float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ inline float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
-// Column of token kappa in a transposed row: tokens 32s + 16h + 4g + r go
-// to 32s + 8g + 4h + r, so the 8 tokens one lane feeds to an MFMA k-step
-// ({32s + 4g + r} and {32s + 16 + 4g + r}) end up in one 16-byte run.
-__device__ constexpr int tr_col(int kappa) {
-  return (kappa & ~31) | (((kappa >> 2) & 3) << 3) | (((kappa >> 4) & 1) << 2) | (kappa & 3);
-}
-constexpr int kTrStride = 72;   // transposed rows: 64 tokens + 8 pad (144 bytes)
+typedef short i16x4 __attribute__((ext_vector_type(4)));
 
-// One 64-token block staged twice in LDS: row-major [64][D] (16-byte chunks
-// XOR-swizzled by row) and transposed [D][72] in tr_col order.  A thread
-// moves 4 tokens x 8 dims: token 4*tg + u, dims 8*dc .. 8*dc + 7.
+// LDS tile of one 64-token block, row major [64][D], filled by DMA.  It is
+// read two ways: 16 bytes per lane down 16 rows (MFMA operands contracted
+// over the head dim) and by transposed reads, 8 bytes per lane, 16 rows x
+// 32 bytes per half-wave (operands contracted over the tokens).  Chunk c of
+// row r sits at c ^ sw(r); sw is one-to-one on every 16 consecutive rows
+// (the row reads) and its upper bits are one-to-one on every 8 (the
+// transposed reads), so both patterns hit distinct bank positions.
 template <int D>
-struct BlockStage {
-  static constexpr int kRowElems = 64 * D;
-  static constexpr int kTrElems = D * kTrStride;
-  static constexpr int kThreads = 2 * D;   // 16 token groups x D/8 dim chunks
-  u32x4 r[4];
-  int tid, tg, dc;
-  __device__ __forceinline__ void init(int t) { tid = t; tg = t % 16; dc = t / 16; }
-  __device__ __forceinline__ void load(const uint16_t* __restrict__ src) {
-    if (tid < kThreads) {
-      const uint16_t* b = src + (4 * tg) * D + 8 * dc;
-#pragma unroll
-      for (int u = 0; u < 4; ++u) r[u] = *reinterpret_cast<const u32x4*>(b + u * D);
-    }
-  }
-  __device__ __forceinline__ void store_rows(uint16_t* rows) const {
-    constexpr int kKC = D / 8;
-    if (tid < kThreads) {
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int row = 4 * tg + u;
-        *reinterpret_cast<u32x4*>(rows + row * D + ((dc ^ (row & (kKC - 1))) * 8)) = r[u];
-      }
-    }
-  }
-  __device__ __forceinline__ void store_tr(uint16_t* tr) const {
-    if (tid < kThreads) {
-      const int col = tr_col(4 * tg);
-#pragma unroll
-      for (int h = 0; h < 4; ++h) {
-        const int d0 = 8 * dc + 2 * h;
-        const u32x2 lo = {lo_lo(r[0][h], r[1][h]), lo_lo(r[2][h], r[3][h])};
-        const u32x2 hi = {hi_hi(r[0][h], r[1][h]), hi_hi(r[2][h], r[3][h])};
-        *reinterpret_cast<u32x2*>(tr + d0 * kTrStride + col) = lo;
-        *reinterpret_cast<u32x2*>(tr + (d0 + 1) * kTrStride + col) = hi;
-      }
-    }
+struct BwdTile {
+  static constexpr int kElems = 64 * D;
+  static constexpr int kKC = D / 8;                // 16-byte chunks per row
+  static constexpr int kDma = kElems / (256 * 8);  // DMA loads per thread per tile
+  __device__ static constexpr int sw(int r) {
+    return kKC == 16 ? (((r & 7) << 1) | ((r >> 3) & 1))
+                     : ((((r >> 1) & 3) << 1) | ((r >> 3) & 1));
   }
 };
 
-// Row-major operand read: 8 consecutive dims of token `row` starting at chunk c.
+// DMA of one tile (src = its first row): thread t moves physical chunks
+// u*256 + t (element offsets in off[]); lane l lands at +16*l bytes of the
+// wave-uniform LDS destination.
 template <int D>
-__device__ __forceinline__ u32x4 read_row(const uint16_t* rows, int row, int c) {
-  constexpr int kKC = D / 8;
-  return *reinterpret_cast<const u32x4*>(rows + row * D + ((c ^ (row & (kKC - 1))) * 8));
+__device__ __forceinline__ void dma_rows(const uint16_t* __restrict__ src, const int* off,
+                                         uint16_t* slot, int wave) {
+#pragma unroll
+  for (int u = 0; u < BwdTile<D>::kDma; ++u)
+    __builtin_amdgcn_global_load_lds(
+        src + off[u], (__attribute__((address_space(3))) void*)(slot + (u * 256 + wave * 64) * 8),
+        16, 0, 0);
+}
+// DMA of 64 fp32 per-slot statistics (one wave): lane l's value lands at +4*l bytes.
+__device__ __forceinline__ void dma_stats(const float* __restrict__ src, float* slot, int lane) {
+  __builtin_amdgcn_global_load_lds(src + lane, (__attribute__((address_space(3))) void*)slot, 4, 0, 0);
+}
+
+// Row read: 8 consecutive dims of tile row r (r & 15 as for its 16-row
+// block), starting at logical chunk c.
+template <int D>
+__device__ __forceinline__ int row_offset(int r, int c) {
+  return r * D + ((c ^ BwdTile<D>::sw(r)) * 8);
+}
+// Transposed read for an operand contracted over tokens: lane (li, lg) gets
+// T[tok][16dt + li] for tok = 32s + 4lg + j (elements 0..3) and
+// 32s + 16 + 4lg + j (elements 4..7).  Within 16 lanes, lane m of a
+// transposed read receives element m % 4 of the 8-byte runs supplied by
+// lanes m/4 + 4j, so lane s supplies row 4lg + s/4, dims 16dt + 4(s%4)..+3;
+// tro(dt) is that address for s = 0.
+template <int D>
+__device__ __forceinline__ int tr_offset(int li, int lg, int dt) {
+  const int r = 4 * lg + (li >> 2);
+  return row_offset<D>(r, 2 * dt + ((li & 3) >> 1)) + (li & 1) * 4;
+}
+template <int D>
+__device__ __forceinline__ u32x4 tok_read(const uint16_t* t, int tro, int s) {
+  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) i16x4*)(t + tro + (32 * s) * D));
+  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) i16x4*)(t + tro + (32 * s + 16) * D));
+  const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+  return u32x4{l2[0], l2[1], h2[0], h2[1]};
 }
 
 // Writes a [64][D] fp32 tile held in MFMA accumulators to raster rows of a
@@ -173,7 +179,10 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdPrepArgs a, Geo g) {
     }
 #pragma unroll
     for (int o = kCpr / 2; o >= 1; o >>= 1) dot += __shfl_xor(dot, o);
-    if (chunk == 0) a.delta[crow] = dot;
+    if (chunk == 0) {
+      a.delta[crow] = dot;
+      a.lse2[crow] = r >= 0 ? a.lse[crow] * kLog2e : INFINITY;
+    }
   }
 
   __shared__ float red[4][kRowsPerPass][D];
@@ -268,24 +277,40 @@ __global__ __launch_bounds__(256) void idx_transpose_kernel(const int32_t* __res
 
 // ---------------------------------------------------------------------------
 // dQ: one workgroup per query cube, 4 waves x 16 query slots (as the forward).
+// Per selected key cube the K and V tiles go from cube order straight into
+// a 2-slot LDS ring by DMA; K^T comes from transposed reads of the K tile.
+// Pad key slots get P = 0 as in the forward: a -inf accumulator init for the
+// (ih, iw) part, a -inf exp2 offset for key tiles past the cube's t extent,
+// extents read per step from a per-lane table.
 template <int D>
 __global__ __launch_bounds__(256, 2) void fine_bwd_dq_kernel(BwdFineArgs a, Geo g) {
-  constexpr int kKS = D / 32, kDT = D / 16, kOS = D + 8;
-  using Stage = BlockStage<D>;
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * Stage::kRowElems + Stage::kTrElems];
-  uint16_t* const k_rows = smem;
-  uint16_t* const v_rows = smem + Stage::kRowElems;
-  uint16_t* const k_tr = smem + 2 * Stage::kRowElems;
+  using Tl = BwdTile<D>;
+  constexpr int kKS = D / 32, kDT = D / 16, kOS = D + 8, kT = Tl::kElems;
+  __shared__ __attribute__((aligned(16))) uint16_t smem[4 * kT];   // [2 slots][K | V]
 
   const int tile = xcd_remap(blockIdx.x, gridDim.x);
   const int64_t bh = tile / g.C;
   const int qc = tile % g.C;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int li = lane & 15, lg = lane >> 4;
   const int K = g.K;
   const int32_t* __restrict__ sel = a.idx + static_cast<int64_t>(tile) * K;
   const float c2 = inv_sqrt_d<D>() * kLog2e;
   const int64_t qrow = bh * g.Np + static_cast<int64_t>(qc) * 64 + wave * 16 + li;
+  const int64_t head0 = bh * g.Np * D;
+
+  int off[Tl::kDma];
+#pragma unroll
+  for (int u = 0; u < Tl::kDma; ++u) {
+    const int P = u * 256 + tid;
+    off[u] = row_offset<D>(P / Tl::kKC, P % Tl::kKC);
+  }
+  int rro[kKS], tro[kDT];
+#pragma unroll
+  for (int ks = 0; ks < kKS; ++ks) rro[ks] = row_offset<D>(li, 4 * ks + lg);
+#pragma unroll
+  for (int dt = 0; dt < kDT; ++dt) tro[dt] = tr_offset<D>(li, lg, dt);
 
   u32x4 qf[kKS], df[kKS];
 #pragma unroll
@@ -293,47 +318,60 @@ __global__ __launch_bounds__(256, 2) void fine_bwd_dq_kernel(BwdFineArgs a, Geo 
     qf[ks] = *reinterpret_cast<const u32x4*>(a.qc + qrow * D + 32 * ks + 8 * lg);
     df[ks] = *reinterpret_cast<const u32x4*>(a.dofc + qrow * D + 32 * ks + 8 * lg);
   }
-  const float lse2 = a.lse[qrow] * kLog2e;
+  const float lse2 = a.lse2[qrow];
   const float delta = a.delta[qrow];
-
-  Stage ks_, vs_;
-  ks_.init(tid);
-  vs_.init(tid);
+  // extents of the selected key cubes (nt | nh << 3 | nw << 6), 64 per lane vector
+  auto extents = [&](int first) {
+    const int m = first + lane;
+    if (m >= K) return 4 | (4 << 3) | (4 << 6);
+    const CubeExt e = cube_extent(g, sel[m]);
+    return e.nt | (e.nh << 3) | (e.nw << 6);
+  };
+  int ext_lanes = extents(0);
+  int ext_cur = -1;
+  f32x4 bias = {0.f, 0.f, 0.f, 0.f};   // (ih, iw) mask of S^T, first MFMA of each key tile
+  float offk[4];                        // exp2 offset of key tile kb: -lse2, or -inf past nt
   f32x4 dacc[kDT];
 #pragma unroll
   for (int dt = 0; dt < kDT; ++dt) dacc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  int64_t base = (bh * g.Np + static_cast<int64_t>(sel[0]) * 64) * D;
-  ks_.load(a.kc + base);
-  vs_.load(a.vc + base);
+  auto stage = [&](int j, int slot) {
+    const uint16_t* src = a.kc + head0 + static_cast<int64_t>(j) * 64 * D;
+    dma_rows<D>(src, off, smem + slot * 2 * kT, wave);
+    dma_rows<D>(a.vc + (src - a.kc), off, smem + slot * 2 * kT + kT, wave);
+  };
+  stage(sel[0], 0);
   for (int n = 0; n < K; ++n) {
-    const int j = sel[n];
-    ks_.store_rows(k_rows);
-    ks_.store_tr(k_tr);
-    vs_.store_rows(v_rows);
+    // tiles of key cube n have landed for every wave; slot (n+1)&1 is free
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    if (n + 1 < K) {
-      base = (bh * g.Np + static_cast<int64_t>(sel[n + 1]) * 64) * D;
-      ks_.load(a.kc + base);
-      vs_.load(a.vc + base);
+    if (n + 1 < K) stage(sel[n + 1], (n + 1) & 1);
+    const uint16_t* k_t = smem + (n & 1) * 2 * kT;
+    const uint16_t* v_t = k_t + kT;
+    if (n > 0 && (n & 63) == 0) ext_lanes = extents(n);
+    const int ext = __builtin_amdgcn_readlane(ext_lanes, n & 63);
+    if (ext != ext_cur) {
+      ext_cur = ext;
+      const int nt = ext & 7, nh = (ext >> 3) & 7, nw = ext >> 6;
+      const float vl = lg < nh ? 0.f : -INFINITY;
+      bias = f32x4{vl, nw > 1 ? vl : -INFINITY, nw > 2 ? vl : -INFINITY, nw > 3 ? vl : -INFINITY};
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) offk[kb] = kb < nt ? -lse2 : -INFINITY;
     }
-    // S^T and dP^T: lane holds (q = li, key = 16kb + 4lg + r)
+    // S^T and dP^T: lane holds (key = 16kb + 4lg + r, q = li)
     f32x4 sacc[4], pacc[4];
 #pragma unroll
-    for (int ks = 0; ks < kKS; ++ks) {
+    for (int ks = 0; ks < kKS; ++ks)
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
-        const int row = 16 * kb + li;
-        const u32x4 kf = read_row<D>(k_rows, row, 4 * ks + lg);
-        const u32x4 vf = read_row<D>(v_rows, row, 4 * ks + lg);
+        const u32x4 kf = *reinterpret_cast<const u32x4*>(k_t + rro[ks] + kb * 16 * D);
+        const u32x4 vf = *reinterpret_cast<const u32x4*>(v_t + rro[ks] + kb * 16 * D);
         sacc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-            as_bf16x8(kf), as_bf16x8(qf[ks]), ks == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : sacc[kb], 0, 0, 0);
+            as_bf16x8(kf), as_bf16x8(qf[ks]), ks == 0 ? bias : sacc[kb], 0, 0, 0);
         pacc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
             as_bf16x8(vf), as_bf16x8(df[ks]), ks == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : pacc[kb], 0, 0, 0);
       }
-    }
-    const CubeExt e = cube_extent(g, j);
-    const bool edge = e.nt < 4 || e.nh < 4 || e.nw < 4;
+    // dS^T as the B operand: k-step s covers keys 32s + 16(i/4) + 4lg + (i%4)
     u32x4 dsf[2];
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
@@ -341,8 +379,7 @@ __global__ __launch_bounds__(256, 2) void fine_bwd_dq_kernel(BwdFineArgs a, Geo 
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const int kb = 2 * s + (i >> 2), r = i & 3;
-        float p = __builtin_amdgcn_exp2f(fmaf(sacc[kb][r], c2, -lse2));
-        if (edge && (kb >= e.nt || lg >= e.nh || r >= e.nw)) p = 0.f;
+        const float p = __builtin_amdgcn_exp2f(fmaf(sacc[kb][r], c2, offk[kb]));
         ds[i] = p * (pacc[kb][r] - delta);
       }
       dsf[s] = u32x4{pack_bf16x2(ds[0], ds[1]), pack_bf16x2(ds[2], ds[3]),
@@ -352,17 +389,14 @@ __global__ __launch_bounds__(256, 2) void fine_bwd_dq_kernel(BwdFineArgs a, Geo 
 #pragma unroll
     for (int s = 0; s < 2; ++s)
 #pragma unroll
-      for (int dt = 0; dt < kDT; ++dt) {
-        const u32x4 kt =
-            *reinterpret_cast<const u32x4*>(k_tr + (16 * dt + li) * kTrStride + 32 * s + 8 * lg);
-        dacc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kt), as_bf16x8(dsf[s]),
-                                                           dacc[dt], 0, 0, 0);
-      }
-    __syncthreads();
+      for (int dt = 0; dt < kDT; ++dt)
+        dacc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(tok_read<D>(k_t, tro[dt], s)),
+                                                           as_bf16x8(dsf[s]), dacc[dt], 0, 0, 0);
   }
+  __syncthreads();   // every wave is done with the ring
 
   // epilogue: dq[q][d] = scale * acc + dQc[qc][d] / n_qc
-  uint16_t* const stage = smem;
+  uint16_t* const stage_o = smem;
   const CubeExt eq = cube_extent(g, qc);
   const float inv_n = 1.f / static_cast<float>(eq.nt * eq.nh * eq.nw);
   const float* cq = a.dqc == nullptr ? nullptr : a.dqc + (bh * g.C + qc) * D;
@@ -375,34 +409,46 @@ __global__ __launch_bounds__(256, 2) void fine_bwd_dq_kernel(BwdFineArgs a, Geo 
       x[r] = dacc[dt][r] * inv_sqrt_d<D>() + (cq ? cq[d] * inv_n : 0.f);
     }
     const u32x2 w = {pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3])};
-    *reinterpret_cast<u32x2*>(stage + (wave * 16 + li) * kOS + 16 * dt + 4 * lg) = w;
+    *reinterpret_cast<u32x2*>(stage_o + (wave * 16 + li) * kOS + 16 * dt + 4 * lg) = w;
   }
   __syncthreads();
-  write_cube_rows<D>(stage, a.dq, g, bh, qc, tid);
+  write_cube_rows<D>(stage_o, a.dq, g, bh, qc, tid);
 }
 
 // ---------------------------------------------------------------------------
 // dK/dV: one workgroup per key cube, wave w owns keys 16w..16w+15 and loops
-// over the query cubes that selected this key cube.
+// over the query cubes that selected this key cube.  Per query cube the Q
+// and dO tiles and its 64 lse2 / delta values go straight into a 2-slot LDS
+// ring by DMA; Q^T and dO^T come from transposed reads.  Pad query slots
+// have lse2 = +inf (P = 0) and zero dO rows, so they add nothing.
 template <int D>
 __global__ __launch_bounds__(256, 2) void fine_bwd_dkdv_kernel(BwdFineArgs a, Geo g) {
-  constexpr int kKS = D / 32, kDT = D / 16, kOS = D + 8;
-  using Stage = BlockStage<D>;
-  __shared__ __attribute__((aligned(16)))
-      uint16_t smem[2 * Stage::kRowElems + 2 * Stage::kTrElems];
-  __shared__ __attribute__((aligned(16))) float stat[2][64];   // lse*log2e, D per query slot
-  uint16_t* const q_rows = smem;
-  uint16_t* const o_rows = smem + Stage::kRowElems;
-  uint16_t* const q_tr = smem + 2 * Stage::kRowElems;
-  uint16_t* const o_tr = q_tr + Stage::kTrElems;
+  using Tl = BwdTile<D>;
+  constexpr int kKS = D / 32, kDT = D / 16, kOS = D + 8, kT = Tl::kElems;
+  __shared__ __attribute__((aligned(16))) uint16_t smem[4 * kT];   // [2 slots][Q | dO]
+  __shared__ __attribute__((aligned(16))) float stat[2][2][64];    // [slot][lse2 | delta][q]
 
   const int tile = xcd_remap(blockIdx.x, gridDim.x);
   const int64_t bh = tile / g.C;
   const int kc = tile % g.C;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int li = lane & 15, lg = lane >> 4;
   const float c2 = inv_sqrt_d<D>() * kLog2e;
   const int64_t krow = bh * g.Np + static_cast<int64_t>(kc) * 64 + wave * 16 + li;
+  const int64_t head0 = bh * g.Np;
+
+  int off[Tl::kDma];
+#pragma unroll
+  for (int u = 0; u < Tl::kDma; ++u) {
+    const int P = u * 256 + tid;
+    off[u] = row_offset<D>(P / Tl::kKC, P % Tl::kKC);
+  }
+  int rro[kKS], tro[kDT];
+#pragma unroll
+  for (int ks = 0; ks < kKS; ++ks) rro[ks] = row_offset<D>(li, 4 * ks + lg);
+#pragma unroll
+  for (int dt = 0; dt < kDT; ++dt) tro[dt] = tr_offset<D>(li, lg, dt);
 
   // B operands of S = Q K^T and dP = dO V^T: lane holds (key = 16w + li, dims 32ks + 8lg ..)
   u32x4 kf[kKS], vf[kKS];
@@ -418,64 +464,53 @@ __global__ __launch_bounds__(256, 2) void fine_bwd_dkdv_kernel(BwdFineArgs a, Ge
     dvacc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  const int32_t* off = a.offsets + bh * (g.C + 1);
-  const int beg = off[kc], end = off[kc + 1];
+  const int32_t* off_l = a.offsets + bh * (g.C + 1);
+  const int beg = off_l[kc], end = off_l[kc + 1];
   const int32_t* lst = a.list + bh * g.C * g.K;
-  Stage qs_, os_;
-  qs_.init(tid);
-  os_.init(tid);
-  float st_lse = 0.f, st_d = 0.f;
-  auto fetch = [&](int qcube) {
-    const int64_t base = bh * g.Np + static_cast<int64_t>(qcube) * 64;
-    qs_.load(a.qc + base * D);
-    os_.load(a.dofc + base * D);
-    if (tid < 64) {
-      st_lse = a.lse[base + tid] * kLog2e;
-      st_d = a.delta[base + tid];
-    }
+  auto stage = [&](int qcube, int slot) {
+    const int64_t row0 = head0 + static_cast<int64_t>(qcube) * 64;
+    dma_rows<D>(a.qc + row0 * D, off, smem + slot * 2 * kT, wave);
+    dma_rows<D>(a.dofc + row0 * D, off, smem + slot * 2 * kT + kT, wave);
+    if (wave == 0) dma_stats(a.lse2 + row0, &stat[slot][0][0], lane);
+    if (wave == 1) dma_stats(a.delta + row0, &stat[slot][1][0], lane);
   };
-  if (beg < end) fetch(lst[beg]);
+  if (beg < end) stage(lst[beg], 0);
   for (int n = beg; n < end; ++n) {
-    const int qcube = lst[n];
-    __syncthreads();   // previous iteration's readers are done
-    qs_.store_rows(q_rows);
-    qs_.store_tr(q_tr);
-    os_.store_rows(o_rows);
-    os_.store_tr(o_tr);
-    if (tid < 64) {
-      stat[0][tid] = st_lse;
-      stat[1][tid] = st_d;
-    }
+    const int slot = (n - beg) & 1;
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    if (n + 1 < end) fetch(lst[n + 1]);
+    if (n + 1 < end) stage(lst[n + 1], slot ^ 1);
+    const uint16_t* q_t = smem + slot * 2 * kT;
+    const uint16_t* o_t = q_t + kT;
 
     // S and dP: lane holds (q = 16qb + 4lg + r, key = 16w + li)
     f32x4 sacc[4], pacc[4];
 #pragma unroll
-    for (int ks = 0; ks < kKS; ++ks) {
+    for (int ks = 0; ks < kKS; ++ks)
 #pragma unroll
       for (int qb = 0; qb < 4; ++qb) {
-        const int row = 16 * qb + li;
-        const u32x4 qa = read_row<D>(q_rows, row, 4 * ks + lg);
-        const u32x4 oa = read_row<D>(o_rows, row, 4 * ks + lg);
+        const u32x4 qa = *reinterpret_cast<const u32x4*>(q_t + rro[ks] + qb * 16 * D);
+        const u32x4 oa = *reinterpret_cast<const u32x4*>(o_t + rro[ks] + qb * 16 * D);
         sacc[qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
             as_bf16x8(qa), as_bf16x8(kf[ks]), ks == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : sacc[qb], 0, 0, 0);
         pacc[qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
             as_bf16x8(oa), as_bf16x8(vf[ks]), ks == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : pacc[qb], 0, 0, 0);
       }
-    }
-    const CubeExt e = cube_extent(g, qcube);
+    // P^T and dS^T as A operands: k-step s covers q = 32s + 16(i/4) + 4lg + (i%4)
     u32x4 pf[2], dsf[2];
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       float p[8], ds[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int qb = 2 * s + (i >> 2), r = i & 3;
-        const int q = 16 * qb + 4 * lg + r;
-        const bool valid = qb < e.nt && lg < e.nh && r < e.nw;   // pad query slots add nothing
-        p[i] = valid ? __builtin_amdgcn_exp2f(fmaf(sacc[qb][r], c2, -stat[0][q])) : 0.f;
-        ds[i] = p[i] * (pacc[qb][r] - stat[1][q]);
+      for (int h = 0; h < 2; ++h) {
+        const int qb = 2 * s + h;
+        const f32x4 l2 = *reinterpret_cast<const f32x4*>(&stat[slot][0][16 * qb + 4 * lg]);
+        const f32x4 dl = *reinterpret_cast<const f32x4*>(&stat[slot][1][16 * qb + 4 * lg]);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          p[4 * h + r] = __builtin_amdgcn_exp2f(fmaf(sacc[qb][r], c2, -l2[r]));
+          ds[4 * h + r] = p[4 * h + r] * (pacc[qb][r] - dl[r]);
+        }
       }
       pf[s] = u32x4{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
                     pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7])};
@@ -487,16 +522,13 @@ __global__ __launch_bounds__(256, 2) void fine_bwd_dkdv_kernel(BwdFineArgs a, Ge
     for (int s = 0; s < 2; ++s)
 #pragma unroll
       for (int dt = 0; dt < kDT; ++dt) {
-        const int col = (16 * dt + li) * kTrStride + 32 * s + 8 * lg;
-        const u32x4 ot = *reinterpret_cast<const u32x4*>(o_tr + col);
-        const u32x4 qt = *reinterpret_cast<const u32x4*>(q_tr + col);
-        dvacc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(pf[s]), as_bf16x8(ot),
-                                                            dvacc[dt], 0, 0, 0);
-        dkacc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(dsf[s]), as_bf16x8(qt),
-                                                            dkacc[dt], 0, 0, 0);
+        dvacc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            as_bf16x8(pf[s]), as_bf16x8(tok_read<D>(o_t, tro[dt], s)), dvacc[dt], 0, 0, 0);
+        dkacc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            as_bf16x8(dsf[s]), as_bf16x8(tok_read<D>(q_t, tro[dt], s)), dkacc[dt], 0, 0, 0);
       }
   }
-  __syncthreads();
+  __syncthreads();   // every wave is done with the ring
 
   // epilogue: lane holds (key = 16w + 4lg + r, d = 16dt + li)
   const CubeExt ek = cube_extent(g, kc);

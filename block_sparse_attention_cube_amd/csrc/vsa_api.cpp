@@ -85,7 +85,7 @@ FwdWs carve_forward(const vsa_problem* p, void* ws, size_t* total) {
 
 struct BwdWs {
   uint16_t* qc; uint16_t* kc; uint16_t* vc; uint16_t* dofc;
-  float* delta;
+  float* delta; float* lse2;
   float* qm; float* km; float* vm; float* docs;
   float* stats;
   float* dqc; float* dkc; float* dvc;
@@ -103,6 +103,7 @@ BwdWs carve_backward(const vsa_problem* p, void* ws, size_t* total) {
   w.vc = static_cast<uint16_t*>(c.take(cube));
   w.dofc = static_cast<uint16_t*>(c.take(cube));
   w.delta = static_cast<float*>(c.take(bh * g.Np * sizeof(float)));
+  w.lse2 = static_cast<float*>(c.take(bh * g.Np * sizeof(float)));
   w.qm = static_cast<float*>(c.take(mean));
   w.km = static_cast<float*>(c.take(mean));
   w.vm = static_cast<float*>(c.take(mean));
@@ -285,7 +286,9 @@ vsa_status vsa_backward(const vsa_problem* p, const void* q, const void* k, cons
   pa.q = b16(q); pa.k = b16(k); pa.v = b16(v);
   pa.dof = b16(do_fine); pa.o = b16(o_fine); pa.doc = b16(do_coarse);
   pa.qc = w.qc; pa.kc = w.kc; pa.vc = w.vc; pa.dofc = w.dofc;
+  pa.lse = lse;
   pa.delta = w.delta;
+  pa.lse2 = w.lse2;
   pa.qm = w.qm; pa.km = w.km; pa.vm = w.vm; pa.docs = w.docs;
   hipError_t e = vsa::launch_bwd_prep(g, pa, stream);
   const bool coarse = do_coarse != nullptr;
@@ -296,7 +299,7 @@ vsa_status vsa_backward(const vsa_problem* p, const void* q, const void* k, cons
   if (e == hipSuccess) {
     vsa::BwdFineArgs fa;
     fa.qc = w.qc; fa.kc = w.kc; fa.vc = w.vc; fa.dofc = w.dofc;
-    fa.lse = lse; fa.delta = w.delta; fa.idx = idx;
+    fa.lse2 = w.lse2; fa.delta = w.delta; fa.idx = idx;
     fa.offsets = w.offsets; fa.list = w.list;
     fa.dqc = coarse ? w.dqc : nullptr;
     fa.dkc = coarse ? w.dkc : nullptr;

@@ -12,7 +12,9 @@ struct BwdPrepArgs {
   const uint16_t* o;     // O_fine
   const uint16_t* doc;   // upstream gradient of O_coarse, or nullptr (zero)
   uint16_t* qc; uint16_t* kc; uint16_t* vc; uint16_t* dofc;   // cube order out
+  const float* lse;      // [B,H,Np] forward log-sum-exp (natural log)
   float* delta;          // [B,H,Np] rowsum(dO * O), 0 on pad slots
+  float* lse2;           // [B,H,Np] lse * log2(e), +inf on pad slots (their P is 0)
   float* qm; float* km; float* vm;   // [B,H,C,D] means over valid slots
   float* docs;           // [B,H,C,D] sums of dO_coarse over valid slots
 };
@@ -30,7 +32,7 @@ hipError_t launch_idx_transpose(const Geo& g, const int32_t* idx, int32_t* offse
 
 struct BwdFineArgs {
   const uint16_t* qc; const uint16_t* kc; const uint16_t* vc; const uint16_t* dofc;
-  const float* lse;      // [B,H,Np] natural log
+  const float* lse2;     // [B,H,Np] lse * log2(e), +inf on pad slots
   const float* delta;    // [B,H,Np]
   const int32_t* idx;    // [B,H,C,K]
   const int32_t* offsets; const int32_t* list;
