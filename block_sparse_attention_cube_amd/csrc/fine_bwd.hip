@@ -127,8 +127,9 @@ __device__ __forceinline__ void write_cube_rows(const uint16_t* stage, uint16_t*
 }
 
 // ---------------------------------------------------------------------------
-// Preparation: raster q, k, v, dO -> cube order; D = rowsum(dO * O) per slot;
-// per-cube means of q, k, v and the per-cube sum of dO_coarse.
+// Preparation: per slot D = rowsum(dO * O) and lse * log2(e) (+inf on pad
+// slots), per cube the means of q, k, v and the sum of dO_coarse.  The
+// gradient kernels gather q, k, v, dO straight from raster rows.
 template <int D>
 __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdPrepArgs a, Geo g) {
   constexpr int kCpr = D / 8;                  // 16-byte chunks per row
@@ -139,7 +140,6 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdPrepArgs a, Geo g) {
   const CubeExt e = cube_extent(g, c);
   const int tid = threadIdx.x, chunk = tid % kCpr, row0 = tid / kCpr;
   const uint16_t* src[4] = {a.q, a.k, a.v, a.dof};
-  uint16_t* dst[4] = {a.qc, a.kc, a.vc, a.dofc};
   float acc[4][8];
 #pragma unroll
   for (int t = 0; t < 4; ++t)
@@ -154,11 +154,9 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdPrepArgs a, Geo g) {
     const int64_t rrow = bh * g.N + r;
     u32x4 val[4];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
+    for (int t = 0; t < 4; ++t)
       val[t] = (r >= 0) ? *reinterpret_cast<const u32x4*>(src[t] + rrow * D + chunk * 8)
                         : u32x4{0u, 0u, 0u, 0u};
-      *reinterpret_cast<u32x4*>(dst[t] + crow * D + chunk * 8) = val[t];
-    }
     const u32x4 ov = (r >= 0) ? *reinterpret_cast<const u32x4*>(a.o + rrow * D + chunk * 8)
                               : u32x4{0u, 0u, 0u, 0u};
     const u32x4 cv = (r >= 0 && a.doc != nullptr)
@@ -297,14 +295,20 @@ __global__ __launch_bounds__(256, 2) void fine_bwd_dq_kernel(BwdFineArgs a, Geo 
   const int K = g.K;
   const int32_t* __restrict__ sel = a.idx + static_cast<int64_t>(tile) * K;
   const float c2 = inv_sqrt_d<D>() * kLog2e;
-  const int64_t qrow = bh * g.Np + static_cast<int64_t>(qc) * 64 + wave * 16 + li;
-  const int64_t head0 = bh * g.Np * D;
+  const int64_t qrow = bh * g.Np + static_cast<int64_t>(qc) * 64 + wave * 16 + li;   // cube-order stats
+  const int64_t head0 = bh * g.N * D;   // raster q, k, v, dO of this head
 
-  int off[Tl::kDma];
+  // DMA offsets (elements from a key cube's first raster row) of this
+  // thread's chunks; alt: the same chunk of the first row, for pad slots
+  int off[Tl::kDma], alt[Tl::kDma];
 #pragma unroll
   for (int u = 0; u < Tl::kDma; ++u) {
     const int P = u * 256 + tid;
-    off[u] = row_offset<D>(P / Tl::kKC, P % Tl::kKC);
+    const int r = P / Tl::kKC;
+    int it, ih, iw;
+    dma_slot<D>(u, wave, lane, it, ih, iw);
+    alt[u] = row_offset<D>(r, P % Tl::kKC) - r * D;
+    off[u] = slot_row<true>(g, it, ih, iw) * D + alt[u];
   }
   int rro[kKS], tro[kDT];
 #pragma unroll
@@ -313,21 +317,34 @@ __global__ __launch_bounds__(256, 2) void fine_bwd_dq_kernel(BwdFineArgs a, Geo 
   for (int dt = 0; dt < kDT; ++dt) tro[dt] = tr_offset<D>(li, lg, dt);
 
   u32x4 qf[kKS], df[kKS];
+  {
+    const CubeExt eq = cube_extent(g, qc);
+    const int it = wave, ih = li >> 2, iw = li & 3;
+    const bool valid = it < eq.nt && ih < eq.nh && iw < eq.nw;   // pad rows: P = 0 via lse2
+    const int64_t row = cube_row<true>(g, eq, qc) + (valid ? slot_row<true>(g, it, ih, iw) : 0);
 #pragma unroll
-  for (int ks = 0; ks < kKS; ++ks) {
-    qf[ks] = *reinterpret_cast<const u32x4*>(a.qc + qrow * D + 32 * ks + 8 * lg);
-    df[ks] = *reinterpret_cast<const u32x4*>(a.dofc + qrow * D + 32 * ks + 8 * lg);
+    for (int ks = 0; ks < kKS; ++ks) {
+      qf[ks] = *reinterpret_cast<const u32x4*>(a.q + head0 + row * D + 32 * ks + 8 * lg);
+      df[ks] = *reinterpret_cast<const u32x4*>(a.dof + head0 + row * D + 32 * ks + 8 * lg);
+    }
   }
   const float lse2 = a.lse2[qrow];
   const float delta = a.delta[qrow];
-  // extents of the selected key cubes (nt | nh << 3 | nw << 6), 64 per lane vector
-  auto extents = [&](int first) {
+  // extents (nt | nh << 3 | nw << 6) and first raster rows of the selected
+  // key cubes, 64 steps per lane vector
+  constexpr int kFull = 4 | (4 << 3) | (4 << 6);
+  int ext_lanes, row_lanes;
+  auto keys = [&](int first) {
     const int m = first + lane;
-    if (m >= K) return 4 | (4 << 3) | (4 << 6);
-    const CubeExt e = cube_extent(g, sel[m]);
-    return e.nt | (e.nh << 3) | (e.nw << 6);
+    ext_lanes = kFull;
+    row_lanes = 0;
+    if (m < K) {
+      const CubeExt e = cube_extent(g, sel[m]);
+      ext_lanes = e.nt | (e.nh << 3) | (e.nw << 6);
+      row_lanes = cube_row<true>(g, e, sel[m]);
+    }
   };
-  int ext_lanes = extents(0);
+  keys(0);
   int ext_cur = -1;
   f32x4 bias = {0.f, 0.f, 0.f, 0.f};   // (ih, iw) mask of S^T, first MFMA of each key tile
   float offk[4];                        // exp2 offset of key tile kb: -lse2, or -inf past nt
@@ -335,21 +352,33 @@ __global__ __launch_bounds__(256, 2) void fine_bwd_dq_kernel(BwdFineArgs a, Geo 
 #pragma unroll
   for (int dt = 0; dt < kDT; ++dt) dacc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  auto stage = [&](int j, int slot) {
-    const uint16_t* src = a.kc + head0 + static_cast<int64_t>(j) * 64 * D;
-    dma_rows<D>(src, off, smem + slot * 2 * kT, wave);
-    dma_rows<D>(a.vc + (src - a.kc), off, smem + slot * 2 * kT + kT, wave);
+  // stage K and V of step n (pad slots of an edge cube read its first row)
+  auto stage = [&](int n, int slot) {
+    const int ext = __builtin_amdgcn_readlane(ext_lanes, n & 63);
+    const int64_t row = __builtin_amdgcn_readlane(row_lanes, n & 63);
+    int eoff[Tl::kDma];
+#pragma unroll
+    for (int u = 0; u < Tl::kDma; ++u) {
+      int it, ih, iw;
+      dma_slot<D>(u, wave, lane, it, ih, iw);
+      eoff[u] = (ext == kFull || (it < (ext & 7) && ih < ((ext >> 3) & 7) && iw < (ext >> 6)))
+                    ? off[u] : alt[u];
+    }
+    dma_rows<D>(a.k + head0 + row * D, eoff, smem + slot * 2 * kT, wave);
+    dma_rows<D>(a.v + head0 + row * D, eoff, smem + slot * 2 * kT + kT, wave);
   };
-  stage(sel[0], 0);
+  stage(0, 0);
   for (int n = 0; n < K; ++n) {
     // tiles of key cube n have landed for every wave; slot (n+1)&1 is free
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    if (n + 1 < K) stage(sel[n + 1], (n + 1) & 1);
+    const int ext = __builtin_amdgcn_readlane(ext_lanes, n & 63);
+    if (n + 1 < K) {
+      if (((n + 1) & 63) == 0) keys(n + 1);
+      stage(n + 1, (n + 1) & 1);
+    }
     const uint16_t* k_t = smem + (n & 1) * 2 * kT;
     const uint16_t* v_t = k_t + kT;
-    if (n > 0 && (n & 63) == 0) ext_lanes = extents(n);
-    const int ext = __builtin_amdgcn_readlane(ext_lanes, n & 63);
     if (ext != ext_cur) {
       ext_cur = ext;
       const int nt = ext & 7, nh = (ext >> 3) & 7, nw = ext >> 6;
@@ -435,14 +464,20 @@ __global__ __launch_bounds__(256, 2) void fine_bwd_dkdv_kernel(BwdFineArgs a, Ge
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int li = lane & 15, lg = lane >> 4;
   const float c2 = inv_sqrt_d<D>() * kLog2e;
-  const int64_t krow = bh * g.Np + static_cast<int64_t>(kc) * 64 + wave * 16 + li;
-  const int64_t head0 = bh * g.Np;
+  const int64_t head0 = bh * g.N * D;   // raster q, k, v, dO of this head
+  const int64_t stat0 = bh * g.Np;      // cube-order lse2 / delta of this head
 
-  int off[Tl::kDma];
+  // DMA offsets (elements from a query cube's first raster row) of this
+  // thread's chunks; alt: the same chunk of the first row, for pad slots
+  int off[Tl::kDma], alt[Tl::kDma];
 #pragma unroll
   for (int u = 0; u < Tl::kDma; ++u) {
     const int P = u * 256 + tid;
-    off[u] = row_offset<D>(P / Tl::kKC, P % Tl::kKC);
+    const int r = P / Tl::kKC;
+    int it, ih, iw;
+    dma_slot<D>(u, wave, lane, it, ih, iw);
+    alt[u] = row_offset<D>(r, P % Tl::kKC) - r * D;
+    off[u] = slot_row<true>(g, it, ih, iw) * D + alt[u];
   }
   int rro[kKS], tro[kDT];
 #pragma unroll
@@ -452,10 +487,16 @@ __global__ __launch_bounds__(256, 2) void fine_bwd_dkdv_kernel(BwdFineArgs a, Ge
 
   // B operands of S = Q K^T and dP = dO V^T: lane holds (key = 16w + li, dims 32ks + 8lg ..)
   u32x4 kf[kKS], vf[kKS];
+  {
+    const CubeExt ek = cube_extent(g, kc);
+    const int it = wave, ih = li >> 2, iw = li & 3;
+    const bool valid = it < ek.nt && ih < ek.nh && iw < ek.nw;   // pad key rows are not written
+    const int64_t row = cube_row<true>(g, ek, kc) + (valid ? slot_row<true>(g, it, ih, iw) : 0);
 #pragma unroll
-  for (int ks = 0; ks < kKS; ++ks) {
-    kf[ks] = *reinterpret_cast<const u32x4*>(a.kc + krow * D + 32 * ks + 8 * lg);
-    vf[ks] = *reinterpret_cast<const u32x4*>(a.vc + krow * D + 32 * ks + 8 * lg);
+    for (int ks = 0; ks < kKS; ++ks) {
+      kf[ks] = *reinterpret_cast<const u32x4*>(a.k + head0 + row * D + 32 * ks + 8 * lg);
+      vf[ks] = *reinterpret_cast<const u32x4*>(a.v + head0 + row * D + 32 * ks + 8 * lg);
+    }
   }
   f32x4 dkacc[kDT], dvacc[kDT];
 #pragma unroll
@@ -467,19 +508,51 @@ __global__ __launch_bounds__(256, 2) void fine_bwd_dkdv_kernel(BwdFineArgs a, Ge
   const int32_t* off_l = a.offsets + bh * (g.C + 1);
   const int beg = off_l[kc], end = off_l[kc + 1];
   const int32_t* lst = a.list + bh * g.C * g.K;
-  auto stage = [&](int qcube, int slot) {
-    const int64_t row0 = head0 + static_cast<int64_t>(qcube) * 64;
-    dma_rows<D>(a.qc + row0 * D, off, smem + slot * 2 * kT, wave);
-    dma_rows<D>(a.dofc + row0 * D, off, smem + slot * 2 * kT + kT, wave);
-    if (wave == 0) dma_stats(a.lse2 + row0, &stat[slot][0][0], lane);
-    if (wave == 1) dma_stats(a.delta + row0, &stat[slot][1][0], lane);
+  // extents (nt | nh << 3 | nw << 6) and first raster rows of the listed
+  // query cubes, 64 steps per lane vector
+  constexpr int kFull = 4 | (4 << 3) | (4 << 6);
+  int ext_lanes = kFull, row_lanes = 0;
+  auto cubes = [&](int first) {   // list positions beg + first ...
+    const int m = beg + first + lane;
+    ext_lanes = kFull;
+    row_lanes = 0;
+    if (m < end) {
+      const CubeExt e = cube_extent(g, lst[m]);
+      ext_lanes = e.nt | (e.nh << 3) | (e.nw << 6);
+      row_lanes = cube_row<true>(g, e, lst[m]);
+    }
   };
-  if (beg < end) stage(lst[beg], 0);
+  // stage Q, dO (pad slots of an edge cube read its first row) and the
+  // statistics of list position beg + i
+  auto stage = [&](int i, int slot) {
+    const int ext = __builtin_amdgcn_readlane(ext_lanes, i & 63);
+    const int64_t row = __builtin_amdgcn_readlane(row_lanes, i & 63);
+    int eoff[Tl::kDma];
+#pragma unroll
+    for (int u = 0; u < Tl::kDma; ++u) {
+      int it, ih, iw;
+      dma_slot<D>(u, wave, lane, it, ih, iw);
+      eoff[u] = (ext == kFull || (it < (ext & 7) && ih < ((ext >> 3) & 7) && iw < (ext >> 6)))
+                    ? off[u] : alt[u];
+    }
+    dma_rows<D>(a.q + head0 + row * D, eoff, smem + slot * 2 * kT, wave);
+    dma_rows<D>(a.dof + head0 + row * D, eoff, smem + slot * 2 * kT + kT, wave);
+    const int64_t srow = stat0 + static_cast<int64_t>(lst[beg + i]) * 64;
+    if (wave == 0) dma_stats(a.lse2 + srow, &stat[slot][0][0], lane);
+    if (wave == 1) dma_stats(a.delta + srow, &stat[slot][1][0], lane);
+  };
+  if (beg < end) {
+    cubes(0);
+    stage(0, 0);
+  }
   for (int n = beg; n < end; ++n) {
-    const int slot = (n - beg) & 1;
+    const int i = n - beg, slot = i & 1;
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    if (n + 1 < end) stage(lst[n + 1], slot ^ 1);
+    if (n + 1 < end) {
+      if (((i + 1) & 63) == 0) cubes(i + 1);
+      stage(i + 1, slot ^ 1);
+    }
     const uint16_t* q_t = smem + slot * 2 * kT;
     const uint16_t* o_t = q_t + kT;
 

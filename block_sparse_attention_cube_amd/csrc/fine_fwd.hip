@@ -77,17 +77,6 @@ struct FineTile {
   __device__ static constexpr int vsw(int r) { return kKC == 16 ? 2 * (r & 7) : 2 * ((r >> 1) & 3); }
 };
 
-// Slot (it, ih, iw) of the u-th DMA chunk of thread (wave, lane): chunk
-// P = 256u + 64 wave + lane is row P / (D/8) of the tile.
-template <int D>
-__device__ __forceinline__ void dma_slot(int u, int wave, int lane, int& it, int& ih, int& iw) {
-  if (D == 128) {
-    it = u; ih = wave; iw = lane >> 4;
-  } else {
-    it = 2 * u + (wave >> 1); ih = ((wave & 1) << 1) | (lane >> 5); iw = (lane >> 3) & 3;
-  }
-}
-
 // Issues the DMA loads of one tile from src (the cube's first row): thread t
 // moves physical chunks u*256 + t, whose element offsets are in off[].  The
 // LDS destination of a load is wave-uniform; lane l lands at +16*l bytes.
@@ -104,18 +93,6 @@ __device__ __forceinline__ void dma_tile(const uint16_t* __restrict__ src, const
 // Valid extent of a key cube packed as nt | nh << 3 | nw << 6 (each 1..4);
 // a full cube packs to kFullExt.
 constexpr int kFullExt = 4 | (4 << 3) | (4 << 6);
-
-// First input row (within its head) of cube c: 64c in cube order, the token
-// of slot (0, 0, 0) in raster order.
-template <bool RASTER>
-__device__ __forceinline__ int cube_row(const Geo& g, const CubeExt& e, int c) {
-  return RASTER ? ((4 * e.ct) * g.Hh + 4 * e.ch) * g.Ww + 4 * e.cw : 64 * c;
-}
-// Row offset of slot (it, ih, iw) from its cube's first row.
-template <bool RASTER>
-__device__ __forceinline__ int slot_row(const Geo& g, int it, int ih, int iw) {
-  return RASTER ? (it * g.Hh + ih) * g.Ww + iw : 16 * it + 4 * ih + iw;
-}
 
 // Extent and first row of the key cubes sel[first .. first+63], one per
 // lane, so that a step reads them with one v_readlane each.

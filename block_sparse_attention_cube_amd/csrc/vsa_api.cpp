@@ -29,6 +29,8 @@ vsa_status check(const vsa_problem* p) {
   if (bh * C > (int64_t(1) << 30)) return VSA_ERR_UNSUPPORTED; // 1-D tile grid
   // B*H*Np*d elements must stay far from int64 overflow
   if (bh * C * 64 * p->d > (int64_t(1) << 58)) return VSA_ERR_UNSUPPORTED;
+  // in-cube raster offsets (elements) are 32-bit: 4 frames of the grid
+  if (int64_t(4) * p->Hh * p->Ww * p->d >= (int64_t(1) << 31)) return VSA_ERR_UNSUPPORTED;
   return VSA_OK;
 }
 
@@ -84,7 +86,6 @@ FwdWs carve_forward(const vsa_problem* p, void* ws, size_t* total) {
 }
 
 struct BwdWs {
-  uint16_t* qc; uint16_t* kc; uint16_t* vc; uint16_t* dofc;
   float* delta; float* lse2;
   float* qm; float* km; float* vm; float* docs;
   float* stats;
@@ -94,14 +95,9 @@ struct BwdWs {
 BwdWs carve_backward(const vsa_problem* p, void* ws, size_t* total) {
   const Geo g = geometry(p);
   const size_t bh = size_t(g.B) * g.H;
-  const size_t cube = bh * g.Np * g.D * sizeof(uint16_t);
   const size_t mean = bh * g.C * g.D * sizeof(float);
   Carver c(ws);
   BwdWs w;
-  w.qc = static_cast<uint16_t*>(c.take(cube));
-  w.kc = static_cast<uint16_t*>(c.take(cube));
-  w.vc = static_cast<uint16_t*>(c.take(cube));
-  w.dofc = static_cast<uint16_t*>(c.take(cube));
   w.delta = static_cast<float*>(c.take(bh * g.Np * sizeof(float)));
   w.lse2 = static_cast<float*>(c.take(bh * g.Np * sizeof(float)));
   w.qm = static_cast<float*>(c.take(mean));
@@ -285,7 +281,6 @@ vsa_status vsa_backward(const vsa_problem* p, const void* q, const void* k, cons
   vsa::BwdPrepArgs pa;
   pa.q = b16(q); pa.k = b16(k); pa.v = b16(v);
   pa.dof = b16(do_fine); pa.o = b16(o_fine); pa.doc = b16(do_coarse);
-  pa.qc = w.qc; pa.kc = w.kc; pa.vc = w.vc; pa.dofc = w.dofc;
   pa.lse = lse;
   pa.delta = w.delta;
   pa.lse2 = w.lse2;
@@ -298,7 +293,7 @@ vsa_status vsa_backward(const vsa_problem* p, const void* q, const void* k, cons
   if (e == hipSuccess) e = vsa::launch_idx_transpose(g, idx, w.offsets, w.list, stream);
   if (e == hipSuccess) {
     vsa::BwdFineArgs fa;
-    fa.qc = w.qc; fa.kc = w.kc; fa.vc = w.vc; fa.dofc = w.dofc;
+    fa.q = b16(q); fa.k = b16(k); fa.v = b16(v); fa.dof = b16(do_fine);
     fa.lse2 = w.lse2; fa.delta = w.delta; fa.idx = idx;
     fa.offsets = w.offsets; fa.list = w.list;
     fa.dqc = coarse ? w.dqc : nullptr;

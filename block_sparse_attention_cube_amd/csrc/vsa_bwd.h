@@ -11,7 +11,6 @@ struct BwdPrepArgs {
   const uint16_t* dof;   // upstream gradient of O_fine
   const uint16_t* o;     // O_fine
   const uint16_t* doc;   // upstream gradient of O_coarse, or nullptr (zero)
-  uint16_t* qc; uint16_t* kc; uint16_t* vc; uint16_t* dofc;   // cube order out
   const float* lse;      // [B,H,Np] forward log-sum-exp (natural log)
   float* delta;          // [B,H,Np] rowsum(dO * O), 0 on pad slots
   float* lse2;           // [B,H,Np] lse * log2(e), +inf on pad slots (their P is 0)
@@ -31,7 +30,7 @@ hipError_t launch_idx_transpose(const Geo& g, const int32_t* idx, int32_t* offse
                                 int32_t* list, hipStream_t s);
 
 struct BwdFineArgs {
-  const uint16_t* qc; const uint16_t* kc; const uint16_t* vc; const uint16_t* dofc;
+  const uint16_t* q; const uint16_t* k; const uint16_t* v; const uint16_t* dof;   // raster
   const float* lse2;     // [B,H,Np] lse * log2(e), +inf on pad slots
   const float* delta;    // [B,H,Np]
   const int32_t* idx;    // [B,H,C,K]

@@ -47,6 +47,29 @@ __host__ __device__ inline int64_t slot_token(const Geo& g, const CubeExt& e, in
   return (t * g.Hh + y) * g.Ww + x;
 }
 
+// First input row (within its head) of cube c: 64c in cube order, the token
+// of slot (0, 0, 0) in raster order.
+template <bool RASTER>
+__device__ __forceinline__ int cube_row(const Geo& g, const CubeExt& e, int c) {
+  return RASTER ? ((kCube * e.ct) * g.Hh + kCube * e.ch) * g.Ww + kCube * e.cw : kSlots * c;
+}
+// Row offset of slot (it, ih, iw) from its cube's first row.
+template <bool RASTER>
+__device__ __forceinline__ int slot_row(const Geo& g, int it, int ih, int iw) {
+  return RASTER ? (it * g.Hh + ih) * g.Ww + iw : 16 * it + 4 * ih + iw;
+}
+// Slot (it, ih, iw) of the u-th 16-byte DMA chunk of thread (wave, lane) of
+// a 256-thread workgroup staging a [64][D] bf16 tile: chunk
+// P = 256u + 64 wave + lane is row P / (D/8) of the tile.
+template <int D>
+__device__ __forceinline__ void dma_slot(int u, int wave, int lane, int& it, int& ih, int& iw) {
+  if (D == 128) {
+    it = u; ih = wave; iw = lane >> 4;
+  } else {
+    it = 2 * u + (wave >> 1); ih = ((wave & 1) << 1) | (lane >> 5); iw = (lane >> 3) & 3;
+  }
+}
+
 // fp32 -> bfloat16 bits, round to nearest even (finite inputs).
 __device__ inline uint16_t f32_to_bf16_rne(float f) {
   uint32_t u = __float_as_uint(f);

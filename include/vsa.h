@@ -44,8 +44,8 @@
  *     16-byte aligned (VSA_ERR_ALIGN).  Limits: B, H, T, Hh, Ww >= 1;
  *     cube = 4x4x4 (else VSA_ERR_UNSUPPORTED); d in {64, 128}
  *     (else VSA_ERR_UNSUPPORTED); 1 <= topk <= C (else VSA_ERR_SHAPE);
- *     C <= 2048 cubes, B*H <= 65535 and B*H*Np*d < 2^58 (else
- *     VSA_ERR_UNSUPPORTED).
+ *     C <= 2048 cubes, B*H <= 65535, B*H*Np*d < 2^58 and
+ *     4*Hh*Ww*d < 2^31 (else VSA_ERR_UNSUPPORTED).
  *   - A kernel launch failure is reported as VSA_ERR_LAUNCH.
  *   - Offsets are 64-bit throughout.
  */
