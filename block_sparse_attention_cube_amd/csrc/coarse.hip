@@ -291,7 +291,7 @@ __device__ __forceinline__ void rows_dot(const float* __restrict__ A, int a0,
     af[kk] = (r < C) ? *reinterpret_cast<const float4*>(A + (int64_t)r * D + 16 * kk + 4 * lg)
                      : make_float4(0.f, 0.f, 0.f, 0.f);
   const int ntile = (C + 15) / 16;
-  for (int ct = wave; ct < ntile; ct += 4) {
+  for (int ct = wave; ct < ntile; ct += kWaves) {
     const int col = ct * 16 + li;
     const f32x4 acc = dot_tile<D>(af, B + (int64_t)col * D, col < C, lg);
 #pragma unroll
@@ -307,20 +307,32 @@ __device__ __forceinline__ void lds_times(const float* T, int ldc, const float* 
                                           int wave, int lane) {
   const int li = lane & 15, lg = lane >> 4;
   const float* trow = T + li * ldc;
-  for (int dt = wave; dt < D / 16; dt += 4) {
+  for (int dt = wave; dt < D / 16; dt += kWaves) {
     f32x4 acc[4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f},
                     {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-    for (int j0 = 0; j0 < C; j0 += 64) {
-      float a[16], b[16];
+    // each batch of 16 Y loads is issued one batch ahead of its MFMAs
+    float b[16];
+    auto load_batch = [&](int j0) {
 #pragma unroll
       for (int u = 0; u < 16; ++u) {
         const int j = j0 + 16 * (u >> 2) + 4 * lg + (u & 3);
         b[u] = (j < C) ? Y[(int64_t)j * D + dt * 16 + li] : 0.f;
+      }
+    };
+    load_batch(0);
+    for (int j0 = 0; j0 < C; j0 += 64) {
+      float a[16], bc[16];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) bc[u] = b[u];
+      if (j0 + 64 < C) load_batch(j0 + 64);
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        const int j = j0 + 16 * (u >> 2) + 4 * lg + (u & 3);
         a[u] = (j < C) ? trow[j] : 0.f;
       }
 #pragma unroll
       for (int u = 0; u < 16; ++u)
-        acc[u & 3] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[u], b[u], acc[u & 3], 0, 0, 0);
+        acc[u & 3] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[u], bc[u], acc[u & 3], 0, 0, 0);
     }
     const f32x4 tot = (acc[0] + acc[1]) + (acc[2] + acc[3]);
 #pragma unroll
@@ -332,7 +344,7 @@ __device__ __forceinline__ void lds_times(const float* T, int ldc, const float* 
 }
 
 template <int D>
-__global__ __launch_bounds__(256) void coarse_bwd_rows_kernel(
+__global__ __launch_bounds__(64 * kWaves) void coarse_bwd_rows_kernel(
     const float* __restrict__ qm, const float* __restrict__ km, const float* __restrict__ vm,
     const float* __restrict__ docs, float* __restrict__ stats, float* __restrict__ dqc, Geo g,
     int ldc) {
@@ -348,7 +360,7 @@ __global__ __launch_bounds__(256) void coarse_bwd_rows_kernel(
   rows_dot<D>(qm + hoff, row0, km + hoff, C, kScale, s1, ldc, wave, lane);
   rows_dot<D>(docs + hoff, row0, vm + hoff, C, 1.f, s2, ldc, wave, lane);
   __syncthreads();
-  for (int rr = wave; rr < kRows; rr += 4) {
+  for (int rr = wave; rr < kRows; rr += kWaves) {
     float* p = s1 + rr * ldc;
     float* dp = s2 + rr * ldc;
     float m = -INFINITY;
@@ -378,7 +390,7 @@ __global__ __launch_bounds__(256) void coarse_bwd_rows_kernel(
 }
 
 template <int D>
-__global__ __launch_bounds__(256) void coarse_bwd_cols_kernel(
+__global__ __launch_bounds__(64 * kWaves) void coarse_bwd_cols_kernel(
     const float* __restrict__ qm, const float* __restrict__ km, const float* __restrict__ vm,
     const float* __restrict__ docs, const float* __restrict__ stats, float* __restrict__ dkc,
     float* __restrict__ dvc, Geo g, int ldc) {
@@ -398,7 +410,7 @@ __global__ __launch_bounds__(256) void coarse_bwd_cols_kernel(
   const float* sm = stats + bh * C;
   const float* sl = sm + plane;
   const float* sr = sm + 2 * plane;
-  for (int e = threadIdx.x; e < kRows * C; e += 256) {
+  for (int e = threadIdx.x; e < kRows * C; e += 64 * kWaves) {
     const int jj = e / C, i = e % C;
     const float p = __expf(t1[jj * ldc + i] - sm[i]) / sl[i];
     t1[jj * ldc + i] = p;
@@ -426,7 +438,7 @@ hipError_t launch_coarse_bwd_typed(const Geo& g, const float* qm, const float* k
                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
   }
-  const dim3 grid(ntile, g.B * g.H), block(256);
+  const dim3 grid(ntile, g.B * g.H), block(64 * kWaves);
   hipError_t e = launch_kernel(rows, grid, block, lds, s, qm, km, vm, docs, stats, dqc, g, ldc);
   if (e != hipSuccess) return e;
   return launch_kernel(cols, grid, block, lds, s, qm, km, vm, docs,

@@ -7,7 +7,9 @@
 //     straight from raster order, where slot (it, ih, iw) of a cube is row
 //     base(cube) + (it*Hh + ih)*Ww + iw, so no reordered copy is needed.
 //   * Staging: the 64 K rows and 64 V rows of a key cube go from HBM/L2
-//     straight into LDS with global_load_lds_dwordx4 (no VGPRs, no VALU).
+//     straight into LDS with buffer_load_dwordx4 ... lds (no VGPRs; the
+//     per-lane offsets stay in registers and only a scalar row offset
+//     changes from cube to cube, so staging costs no VALU).
 //     Each lane's source chunk is chosen so that LDS holds the tiles
 //     XOR-swizzled for the reads below; K runs one key cube ahead of V in a
 //     2-slot ring each (64 KB at D = 128).  Pad slots of a raster edge cube
@@ -23,9 +25,10 @@
 //     per step, and the masks change only when the extent does.
 //   * Software pipeline per wave: while the MFMAs of S(n+1) run, the VALU
 //     evaluates exp2 of block n; while PV(n) runs, it scales S(n+1) into exp2
-//     units (t = s log2(e)/sqrt(d) - m) and takes its row max.  The running
-//     max m is raised lazily (only when a row exceeds it by 2^8), so
-//     probabilities stay <= 256 and the common step has no rescale.
+//     units (t = s log2(e)/sqrt(d) - m).  The running max m is raised
+//     lazily (only when a row exceeds it by 2^8), so probabilities stay
+//     <= 256; the common step checks each lane's own maximum against that
+//     bound and needs neither the cross-lane row max nor a rescale.
 //   * Row sums come from one extra MFMA per k-step against a ones operand.
 //   * The epilogue stages O through LDS and writes whole 16-byte chunks,
 //     either in cube order or straight to raster order (fusing the inverse
@@ -33,6 +36,8 @@
 //     every valid token (O_coarse in raster order).
 // Workgroups are remapped so each XCD walks one contiguous range of
 // (head, query cube) tiles, keeping that head's K/V in its own L2.
+#include <type_traits>
+
 #include "vsa_internal.h"
 
 namespace vsa {
@@ -77,17 +82,27 @@ struct FineTile {
   __device__ static constexpr int vsw(int r) { return kKC == 16 ? 2 * (r & 7) : 2 * ((r >> 1) & 3); }
 };
 
-// Issues the DMA loads of one tile from src (the cube's first row): thread t
-// moves physical chunks u*256 + t, whose element offsets are in off[].  The
-// LDS destination of a load is wave-uniform; lane l lands at +16*l bytes.
+// Buffer resource over one head of a [rows][D] bf16 tensor.  Reads beyond
+// `bytes` return zeros instead of faulting; a head holds at most
+// 2048 cubes x 64 rows x 256 bytes, so byte offsets fit 32 bits.
+static_assert(int64_t(kMaxCubes) * kSlots * 128 * 2 < (int64_t(1) << 32), "32-bit head offsets");
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t head_rsrc(const uint16_t* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(base), 0, static_cast<int>(bytes),
+                                           0x00020000);  // raw 32-bit data format
+}
+
+// Issues the DMA loads of one tile: thread t moves physical chunks u*256 + t
+// from byte offset row_bytes + off[u] of the head.  The LDS destination of a
+// load is wave-uniform; lane l lands at +16*l bytes.  The per-lane offsets
+// stay in registers across tiles and only the scalar row offset changes.
 template <int D>
-__device__ __forceinline__ void dma_tile(const uint16_t* __restrict__ src, const int* off,
-                                         uint16_t* slot, int wave) {
+__device__ __forceinline__ void dma_tile(const __amdgpu_buffer_rsrc_t& rs, uint32_t row_bytes,
+                                         const uint32_t* off, uint16_t* slot, int wave) {
 #pragma unroll
   for (int u = 0; u < FineTile<D>::kDma; ++u)
-    __builtin_amdgcn_global_load_lds(
-        src + off[u], (__attribute__((address_space(3))) void*)(slot + (u * 256 + wave * 64) * 8),
-        16, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rs, (__attribute__((address_space(3))) void*)(slot + (u * 256 + wave * 64) * 8), 16, off[u],
+        row_bytes, 0, 0);
 }
 
 // Valid extent of a key cube packed as nt | nh << 3 | nw << 6 (each 1..4);
@@ -121,15 +136,20 @@ __device__ __forceinline__ f32x4 hw_bias(int ext, int lg) {
   return f32x4{vl, nw > 1 ? vl : -INFINITY, nw > 2 ? vl : -INFINITY, nw > 3 ? vl : -INFINITY};
 }
 
-// Max over one lane's 16 values and then over the 4 lanes l, l^16, l^32,
-// l^48 that hold the same query row (gfx950 cross-row swaps, no LDS).  The
-// inputs come out of VALU arithmetic, so the compiler needs no canonicalising
-// maxes on them.
+__device__ __forceinline__ float max3f(float a, float b, float c) { return fmaxf(a, fmaxf(b, c)); }
+
+// Max over one lane's 16 values (3-input maxes).  The inputs come out of VALU
+// arithmetic, so the compiler needs no canonicalising maxes on them.
+__device__ __forceinline__ float lane_max(const f32x4* t) {
+  const float x = max3f(max3f(t[0][0], t[0][1], t[0][2]), max3f(t[0][3], t[1][0], t[1][1]),
+                        max3f(t[1][2], t[1][3], t[2][0]));
+  return max3f(x, max3f(t[2][1], t[2][2], t[2][3]), max3f(t[3][0], t[3][1], fmaxf(t[3][2], t[3][3])));
+}
+
+// Row max: the lane's max, then over the 4 lanes l, l^16, l^32, l^48 that
+// hold the same query row (gfx950 cross-row swaps, no LDS).
 __device__ __forceinline__ float row_max(const f32x4* t) {
-  float x = fmaxf(fmaxf(fmaxf(fmaxf(t[0][0], t[0][1]), fmaxf(t[0][2], t[0][3])),
-                        fmaxf(fmaxf(t[1][0], t[1][1]), fmaxf(t[1][2], t[1][3]))),
-                  fmaxf(fmaxf(fmaxf(t[2][0], t[2][1]), fmaxf(t[2][2], t[2][3])),
-                        fmaxf(fmaxf(t[3][0], t[3][1]), fmaxf(t[3][2], t[3][3]))));
+  float x = lane_max(t);
   const uint32_t u = __float_as_uint(x);
   const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
   x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
@@ -223,40 +243,42 @@ __global__ __launch_bounds__(256, 2) void fine_fwd_bf16_kernel(
   const int32_t* __restrict__ sel = idx + static_cast<int64_t>(tile) * K;
   const float c2 = inv_sqrt_d<D>() * kLog2e;
   const int64_t head0 = bh * (RASTER ? g.N : g.Np) * D;   // element offset of this head's rows
-  const uint16_t* const kh = k + head0;
-  const uint16_t* const vh = v + head0;
+  const uint32_t head_bytes = static_cast<uint32_t>((RASTER ? g.N : g.Np) * D * 2);
+  const __amdgpu_buffer_rsrc_t krs = head_rsrc(k + head0, head_bytes);
+  const __amdgpu_buffer_rsrc_t vrs = head_rsrc(v + head0, head_bytes);
 
-  // DMA offsets (elements, from the cube's first row) of this thread's
-  // chunks; *alt: the same chunk of the cube's first row, for pad slots of
-  // raster edge cubes
-  int koff[Tl::kDma], voff[Tl::kDma], kalt[Tl::kDma], valt[Tl::kDma];
+  // DMA byte offsets (from the cube's first row) of this thread's chunks;
+  // *alt: the same chunk of the cube's first row, for pad slots of raster
+  // edge cubes
+  uint32_t koff[Tl::kDma], voff[Tl::kDma], kalt[Tl::kDma], valt[Tl::kDma];
 #pragma unroll
   for (int u = 0; u < Tl::kDma; ++u) {
     const int P = u * 256 + tid;
     const int r = P / kKC, c = P % kKC;
     int it, ih, iw;
     dma_slot<D>(u, wave, lane, it, ih, iw);
-    const int rowoff = slot_row<RASTER>(g, it, ih, iw) * D;
-    kalt[u] = ((c ^ Tl::ksw(r)) * 8);
-    valt[u] = ((c ^ Tl::vsw(r)) * 8);
+    const uint32_t rowoff = static_cast<uint32_t>(slot_row<RASTER>(g, it, ih, iw) * D) * 2u;
+    kalt[u] = (c ^ Tl::ksw(r)) * 16;
+    valt[u] = (c ^ Tl::vsw(r)) * 16;
     koff[u] = rowoff + kalt[u];
     voff[u] = rowoff + valt[u];
   }
   // stage K or V of a key cube (first row `row`, packed extent `ext`)
-  auto stage = [&](const uint16_t* src, const int* off, const int* alt, int row, int ext,
-                   uint16_t* slot) {
+  auto stage = [&](const __amdgpu_buffer_rsrc_t& rs, const uint32_t* off, const uint32_t* alt,
+                   int row, int ext, uint16_t* slot) {
+    const uint32_t row_bytes = static_cast<uint32_t>(row) * (D * 2);
     if (RASTER && ext != kFullExt) {
       const int nt = ext & 7, nh = (ext >> 3) & 7, nw = ext >> 6;
-      int eoff[Tl::kDma];
+      uint32_t eoff[Tl::kDma];
 #pragma unroll
       for (int u = 0; u < Tl::kDma; ++u) {
         int it, ih, iw;
         dma_slot<D>(u, wave, lane, it, ih, iw);
         eoff[u] = (it < nt && ih < nh && iw < nw) ? off[u] : alt[u];
       }
-      dma_tile<D>(src + static_cast<int64_t>(row) * D, eoff, slot, wave);
+      dma_tile<D>(rs, row_bytes, eoff, slot, wave);
     } else {
-      dma_tile<D>(src + static_cast<int64_t>(row) * D, off, slot, wave);
+      dma_tile<D>(rs, row_bytes, off, slot, wave);
     }
   };
 
@@ -295,9 +317,9 @@ __global__ __launch_bounds__(256, 2) void fine_fwd_bf16_kernel(
 
   // prologue: K(0), V(0), K(1) in flight together; S(0) and its row max
   const int ext0 = key_ext(0);
-  stage(kh, koff, kalt, key_row(0), ext0, kring);
-  stage(vh, voff, valt, key_row(0), ext0, vring);
-  if (K > 1) stage(kh, koff, kalt, key_row(1), key_ext(1), kring + kT);
+  stage(krs, koff, kalt, key_row(0), ext0, kring);
+  stage(vrs, voff, valt, key_row(0), ext0, vring);
+  if (K > 1) stage(krs, koff, kalt, key_row(1), key_ext(1), kring + kT);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   // the masks follow the key cube's extent and are rebuilt only when it changes
@@ -317,15 +339,19 @@ __global__ __launch_bounds__(256, 2) void fine_fwd_bf16_kernel(
     mbk[kb] = kb < nt_cur ? -mb : -INFINITY;
   }
 
-  for (int n = 0; n + 1 < K; ++n) {
+  // One step per selected key cube.  The loop is unrolled by two so that the
+  // ring slots (P0 = n & 1) are constants and every LDS address is a
+  // register plus an immediate offset.
+  auto step = [&](auto p0c, int n) {
+    constexpr int P0 = decltype(p0c)::value, P1 = P0 ^ 1;
     // K(n+1) and V(n) have landed for every wave; slots of K(n), V(n-1) are free
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     const int ext = key_ext(n + 1);
-    stage(vh, voff, valt, key_row(n + 1), ext, vring + ((n + 1) & 1) * kT);
+    stage(vrs, voff, valt, key_row(n + 1), ext, vring + P1 * kT);
     if (n + 2 < K) {
       if (((n + 2) & 63) == 0) lane_keys<RASTER>(g, sel, n + 2, K, lane, ext_lanes, row_lanes);
-      stage(kh, koff, kalt, key_row(n + 2), key_ext(n + 2), kring + (n & 1) * kT);
+      stage(krs, koff, kalt, key_row(n + 2), key_ext(n + 2), kring + P0 * kT);
     }
     if ((ext >> 3) != hw_cur) {
       hw_cur = ext >> 3;
@@ -338,18 +364,21 @@ __global__ __launch_bounds__(256, 2) void fine_fwd_bf16_kernel(
     }
     // S(n+1) on the matrix cores while exp2 of block n runs on the VALU
     f32x4 tnext[4];
-    score_tile<D>(kring + ((n + 1) & 1) * kT, kro, qf, bias, tnext);
+    score_tile<D>(kring + P1 * kT, kro, qf, bias, tnext);
     u32x4 pf[2];
     probabilities(tcur, pf);
-    // PV(n) while S(n+1) is scaled into exp2 units and reduced
-    pv_tile<D>(vring + (n & 1) * kT, vtr, pf, oacc, lacc);
+    // PV(n) while S(n+1) is scaled into exp2 units
+    pv_tile<D>(vring + P0 * kT, vtr, pf, oacc, lacc);
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
       for (int r = 0; r < 4; ++r) tnext[kb][r] = fmaf(tnext[kb][r], c2, mbk[kb]);
-    const float mt = row_max(tnext);
-    const bool grow = mt > kTau;
-    if (__ballot(grow) != 0ull) {   // wave-uniform: rare after the first block
+    // Every value of the wave within 2^tau of the running max (the common
+    // case) needs no row max at all: the cross-lane reduction and the rescale
+    // run only when some lane exceeds it.  Wave-uniform branch.
+    if (__ballot(lane_max(tnext) > kTau) != 0ull) {
+      const float mt = row_max(tnext);
+      const bool grow = mt > kTau;
       const float delta = grow ? mt : 0.f;
       const float alpha = __builtin_amdgcn_exp2f(-delta);
 #pragma unroll
@@ -364,13 +393,19 @@ __global__ __launch_bounds__(256, 2) void fine_fwd_bf16_kernel(
     }
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) tcur[kb] = tnext[kb];
+  };
+  for (int n = 0; n + 1 < K; n += 2) {
+    step(std::integral_constant<int, 0>{}, n);
+    if (n + 2 >= K) break;
+    step(std::integral_constant<int, 1>{}, n + 1);
   }
   {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     u32x4 pf[2];
     probabilities(tcur, pf);
-    pv_tile<D>(vring + ((K - 1) & 1) * kT, vtr, pf, oacc, lacc);
+    if ((K - 1) & 1) pv_tile<D>(vring + kT, vtr, pf, oacc, lacc);
+    else pv_tile<D>(vring, vtr, pf, oacc, lacc);
   }
   __syncthreads();   // every wave is done with the rings: reuse them for O
 
