@@ -14,9 +14,11 @@
 // Both kernels follow the forward's MFMA layouts (v_mfma_f32_16x16x32_bf16,
 // scores kept in the accumulator layout of the transposed product so that
 // probabilities feed the next MFMA straight from registers).  Tiles reach
-// LDS by DMA (global_load_lds) in a 2-slot ring, one barrier per step;
+// LDS by DMA (buffer loads to LDS) in a 2-slot ring, one barrier per step;
 // operands contracted over the token index come from the row-major tiles
 // through gfx950 transposed LDS reads (ds_read_b64_tr_b16).
+#include <type_traits>
+
 #include "vsa_internal.h"
 #include "vsa_bwd.h"
 
@@ -63,21 +65,34 @@ struct BwdTile {
   }
 };
 
-// DMA of one tile (src = its first row): thread t moves physical chunks
-// u*256 + t (element offsets in off[]); lane l lands at +16*l bytes of the
-// wave-uniform LDS destination.
+// Buffer resource over `bytes` bytes from base (one head of a tensor);
+// reads beyond it return zeros.  A head holds at most 2048 cubes x 64 rows
+// x 256 bytes, so byte offsets fit 32 bits.
+static_assert(int64_t(kMaxCubes) * kSlots * 128 * 2 < (int64_t(1) << 32), "32-bit head offsets");
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t head_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes),
+                                           0x00020000);  // raw 32-bit data format
+}
+
+// DMA of one tile whose first row starts at byte row_bytes of the head:
+// thread t moves physical chunks u*256 + t (byte offsets from that row in
+// off[]); lane l lands at +16*l bytes of the wave-uniform LDS destination.
+// The per-lane offsets stay in registers; only the scalar row offset changes.
 template <int D>
-__device__ __forceinline__ void dma_rows(const uint16_t* __restrict__ src, const int* off,
-                                         uint16_t* slot, int wave) {
+__device__ __forceinline__ void dma_rows(const __amdgpu_buffer_rsrc_t& rs, uint32_t row_bytes,
+                                         const uint32_t* off, uint16_t* slot, int wave) {
 #pragma unroll
   for (int u = 0; u < BwdTile<D>::kDma; ++u)
-    __builtin_amdgcn_global_load_lds(
-        src + off[u], (__attribute__((address_space(3))) void*)(slot + (u * 256 + wave * 64) * 8),
-        16, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rs, (__attribute__((address_space(3))) void*)(slot + (u * 256 + wave * 64) * 8), 16, off[u],
+        row_bytes, 0, 0);
 }
-// DMA of 64 fp32 per-slot statistics (one wave): lane l's value lands at +4*l bytes.
-__device__ __forceinline__ void dma_stats(const float* __restrict__ src, float* slot, int lane) {
-  __builtin_amdgcn_global_load_lds(src + lane, (__attribute__((address_space(3))) void*)slot, 4, 0, 0);
+// DMA of 64 fp32 per-slot statistics starting at byte `at` of the head (one
+// wave): lane l's value lands at +4*l bytes.
+__device__ __forceinline__ void dma_stats(const __amdgpu_buffer_rsrc_t& rs, uint32_t at, float* slot,
+                                          int lane) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)slot, 4,
+                                           static_cast<uint32_t>(lane) * 4u, at, 0, 0);
 }
 
 // Row read: 8 consecutive dims of tile row r (r & 15 as for its 16-row
@@ -298,18 +313,21 @@ __global__ __launch_bounds__(256, 2) void fine_bwd_dq_kernel(BwdFineArgs a, Geo 
   const int64_t qrow = bh * g.Np + static_cast<int64_t>(qc) * 64 + wave * 16 + li;   // cube-order stats
   const int64_t head0 = bh * g.N * D;   // raster q, k, v, dO of this head
 
-  // DMA offsets (elements from a key cube's first raster row) of this
-  // thread's chunks; alt: the same chunk of the first row, for pad slots
-  int off[Tl::kDma], alt[Tl::kDma];
+  // DMA byte offsets (from a key cube's first raster row) of this thread's
+  // chunks; alt: the same chunk of the first row, for pad slots
+  uint32_t off[Tl::kDma], alt[Tl::kDma];
 #pragma unroll
   for (int u = 0; u < Tl::kDma; ++u) {
     const int P = u * 256 + tid;
     const int r = P / Tl::kKC;
     int it, ih, iw;
     dma_slot<D>(u, wave, lane, it, ih, iw);
-    alt[u] = row_offset<D>(r, P % Tl::kKC) - r * D;
-    off[u] = slot_row<true>(g, it, ih, iw) * D + alt[u];
+    alt[u] = static_cast<uint32_t>(row_offset<D>(r, P % Tl::kKC) - r * D) * 2u;
+    off[u] = static_cast<uint32_t>(slot_row<true>(g, it, ih, iw) * D) * 2u + alt[u];
   }
+  const uint32_t head_bytes = static_cast<uint32_t>(g.N * D * 2);
+  const __amdgpu_buffer_rsrc_t krs = head_rsrc(a.k + head0, head_bytes);
+  const __amdgpu_buffer_rsrc_t vrs = head_rsrc(a.v + head0, head_bytes);
   int rro[kKS], tro[kDT];
 #pragma unroll
   for (int ks = 0; ks < kKS; ++ks) rro[ks] = row_offset<D>(li, 4 * ks + lg);
@@ -353,31 +371,38 @@ __global__ __launch_bounds__(256, 2) void fine_bwd_dq_kernel(BwdFineArgs a, Geo 
   for (int dt = 0; dt < kDT; ++dt) dacc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // stage K and V of step n (pad slots of an edge cube read its first row)
-  auto stage = [&](int n, int slot) {
+  auto stage = [&](int n, uint16_t* slot) {
     const int ext = __builtin_amdgcn_readlane(ext_lanes, n & 63);
-    const int64_t row = __builtin_amdgcn_readlane(row_lanes, n & 63);
-    int eoff[Tl::kDma];
+    const uint32_t row_bytes = static_cast<uint32_t>(__builtin_amdgcn_readlane(row_lanes, n & 63)) * (D * 2);
+    if (ext == kFull) {
+      dma_rows<D>(krs, row_bytes, off, slot, wave);
+      dma_rows<D>(vrs, row_bytes, off, slot + kT, wave);
+    } else {
+      uint32_t eoff[Tl::kDma];
 #pragma unroll
-    for (int u = 0; u < Tl::kDma; ++u) {
-      int it, ih, iw;
-      dma_slot<D>(u, wave, lane, it, ih, iw);
-      eoff[u] = (ext == kFull || (it < (ext & 7) && ih < ((ext >> 3) & 7) && iw < (ext >> 6)))
-                    ? off[u] : alt[u];
+      for (int u = 0; u < Tl::kDma; ++u) {
+        int it, ih, iw;
+        dma_slot<D>(u, wave, lane, it, ih, iw);
+        eoff[u] = (it < (ext & 7) && ih < ((ext >> 3) & 7) && iw < (ext >> 6)) ? off[u] : alt[u];
+      }
+      dma_rows<D>(krs, row_bytes, eoff, slot, wave);
+      dma_rows<D>(vrs, row_bytes, eoff, slot + kT, wave);
     }
-    dma_rows<D>(a.k + head0 + row * D, eoff, smem + slot * 2 * kT, wave);
-    dma_rows<D>(a.v + head0 + row * D, eoff, smem + slot * 2 * kT + kT, wave);
   };
-  stage(0, 0);
-  for (int n = 0; n < K; ++n) {
-    // tiles of key cube n have landed for every wave; slot (n+1)&1 is free
+  stage(0, smem);
+  // one step per selected key cube, unrolled by two so that the ring slot
+  // (n & 1) is a constant and LDS addresses are registers plus immediates
+  auto step = [&](auto slotc, int n) {
+    constexpr int SLOT = decltype(slotc)::value;
+    // tiles of key cube n have landed for every wave; the other slot is free
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     const int ext = __builtin_amdgcn_readlane(ext_lanes, n & 63);
     if (n + 1 < K) {
       if (((n + 1) & 63) == 0) keys(n + 1);
-      stage(n + 1, (n + 1) & 1);
+      stage(n + 1, smem + (SLOT ^ 1) * 2 * kT);
     }
-    const uint16_t* k_t = smem + (n & 1) * 2 * kT;
+    const uint16_t* k_t = smem + SLOT * 2 * kT;
     const uint16_t* v_t = k_t + kT;
     if (ext != ext_cur) {
       ext_cur = ext;
@@ -421,6 +446,11 @@ __global__ __launch_bounds__(256, 2) void fine_bwd_dq_kernel(BwdFineArgs a, Geo 
       for (int dt = 0; dt < kDT; ++dt)
         dacc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(tok_read<D>(k_t, tro[dt], s)),
                                                            as_bf16x8(dsf[s]), dacc[dt], 0, 0, 0);
+  };
+  for (int n = 0; n < K; n += 2) {
+    step(std::integral_constant<int, 0>{}, n);
+    if (n + 1 >= K) break;
+    step(std::integral_constant<int, 1>{}, n + 1);
   }
   __syncthreads();   // every wave is done with the ring
 
@@ -467,18 +497,24 @@ __global__ __launch_bounds__(256, 2) void fine_bwd_dkdv_kernel(BwdFineArgs a, Ge
   const int64_t head0 = bh * g.N * D;   // raster q, k, v, dO of this head
   const int64_t stat0 = bh * g.Np;      // cube-order lse2 / delta of this head
 
-  // DMA offsets (elements from a query cube's first raster row) of this
+  // DMA byte offsets (from a query cube's first raster row) of this
   // thread's chunks; alt: the same chunk of the first row, for pad slots
-  int off[Tl::kDma], alt[Tl::kDma];
+  uint32_t off[Tl::kDma], alt[Tl::kDma];
 #pragma unroll
   for (int u = 0; u < Tl::kDma; ++u) {
     const int P = u * 256 + tid;
     const int r = P / Tl::kKC;
     int it, ih, iw;
     dma_slot<D>(u, wave, lane, it, ih, iw);
-    alt[u] = row_offset<D>(r, P % Tl::kKC) - r * D;
-    off[u] = slot_row<true>(g, it, ih, iw) * D + alt[u];
+    alt[u] = static_cast<uint32_t>(row_offset<D>(r, P % Tl::kKC) - r * D) * 2u;
+    off[u] = static_cast<uint32_t>(slot_row<true>(g, it, ih, iw) * D) * 2u + alt[u];
   }
+  const uint32_t head_bytes = static_cast<uint32_t>(g.N * D * 2);
+  const __amdgpu_buffer_rsrc_t qrs = head_rsrc(a.q + head0, head_bytes);
+  const __amdgpu_buffer_rsrc_t ors = head_rsrc(a.dof + head0, head_bytes);
+  const uint32_t stat_bytes = static_cast<uint32_t>(g.Np * 4);
+  const __amdgpu_buffer_rsrc_t lrs = head_rsrc(a.lse2 + stat0, stat_bytes);
+  const __amdgpu_buffer_rsrc_t drs = head_rsrc(a.delta + stat0, stat_bytes);
   int rro[kKS], tro[kDT];
 #pragma unroll
   for (int ks = 0; ks < kKS; ++ks) rro[ks] = row_offset<D>(li, 4 * ks + lg);
@@ -526,27 +562,35 @@ __global__ __launch_bounds__(256, 2) void fine_bwd_dkdv_kernel(BwdFineArgs a, Ge
   // statistics of list position beg + i
   auto stage = [&](int i, int slot) {
     const int ext = __builtin_amdgcn_readlane(ext_lanes, i & 63);
-    const int64_t row = __builtin_amdgcn_readlane(row_lanes, i & 63);
-    int eoff[Tl::kDma];
+    const uint32_t row_bytes = static_cast<uint32_t>(__builtin_amdgcn_readlane(row_lanes, i & 63)) * (D * 2);
+    uint16_t* const dst = smem + slot * 2 * kT;
+    if (ext == kFull) {
+      dma_rows<D>(qrs, row_bytes, off, dst, wave);
+      dma_rows<D>(ors, row_bytes, off, dst + kT, wave);
+    } else {
+      uint32_t eoff[Tl::kDma];
 #pragma unroll
-    for (int u = 0; u < Tl::kDma; ++u) {
-      int it, ih, iw;
-      dma_slot<D>(u, wave, lane, it, ih, iw);
-      eoff[u] = (ext == kFull || (it < (ext & 7) && ih < ((ext >> 3) & 7) && iw < (ext >> 6)))
-                    ? off[u] : alt[u];
+      for (int u = 0; u < Tl::kDma; ++u) {
+        int it, ih, iw;
+        dma_slot<D>(u, wave, lane, it, ih, iw);
+        eoff[u] = (it < (ext & 7) && ih < ((ext >> 3) & 7) && iw < (ext >> 6)) ? off[u] : alt[u];
+      }
+      dma_rows<D>(qrs, row_bytes, eoff, dst, wave);
+      dma_rows<D>(ors, row_bytes, eoff, dst + kT, wave);
     }
-    dma_rows<D>(a.q + head0 + row * D, eoff, smem + slot * 2 * kT, wave);
-    dma_rows<D>(a.dof + head0 + row * D, eoff, smem + slot * 2 * kT + kT, wave);
-    const int64_t srow = stat0 + static_cast<int64_t>(lst[beg + i]) * 64;
-    if (wave == 0) dma_stats(a.lse2 + srow, &stat[slot][0][0], lane);
-    if (wave == 1) dma_stats(a.delta + srow, &stat[slot][1][0], lane);
+    const uint32_t at = static_cast<uint32_t>(lst[beg + i]) * (64 * 4);
+    if (wave == 0) dma_stats(lrs, at, &stat[slot][0][0], lane);
+    if (wave == 1) dma_stats(drs, at, &stat[slot][1][0], lane);
   };
   if (beg < end) {
     cubes(0);
     stage(0, 0);
   }
-  for (int n = beg; n < end; ++n) {
-    const int i = n - beg, slot = i & 1;
+  // one step per listed query cube, unrolled by two so that the ring slot is
+  // a constant and LDS addresses are registers plus immediates
+  auto step = [&](auto slotc, int i) {
+    constexpr int slot = decltype(slotc)::value;
+    const int n = beg + i;
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     if (n + 1 < end) {
@@ -600,6 +644,11 @@ __global__ __launch_bounds__(256, 2) void fine_bwd_dkdv_kernel(BwdFineArgs a, Ge
         dkacc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
             as_bf16x8(dsf[s]), as_bf16x8(tok_read<D>(q_t, tro[dt], s)), dkacc[dt], 0, 0, 0);
       }
+  };
+  for (int i = 0; beg + i < end; i += 2) {
+    step(std::integral_constant<int, 0>{}, i);
+    if (beg + i + 1 >= end) break;
+    step(std::integral_constant<int, 1>{}, i + 1);
   }
   __syncthreads();   // every wave is done with the ring
 
