@@ -1,17 +1,19 @@
 // Coarse stage of VSA: cube-level attention and the top-K block selection.
 //
 // Input: fp32 means of q, k, v per cube, [B,H,C,D] (written by the reorder).
-// One workgroup (4 waves) owns 16 query-cube rows of one head:
+// One workgroup (16 waves) owns 16 query-cube rows of one head:
 //   1. Sc[16, C] = Qc Kc^T / sqrt(D) on fp32 MFMA (v_mfma_f32_16x16x4_f32),
 //      kept in LDS (16 x C fp32, C <= 2048) and optionally written out;
 //   2. row max and 1/sum(exp) per row (one wave per row, wave reductions);
 //   3. O_coarse[16, D] = softmax(Sc) Vc on fp32 MFMA, probabilities formed on
-//      the fly from the LDS scores;
-//   4. top-K per row: the K-th largest score is found exactly by a 32-step
-//      bitwise search over order-preserving uint32 keys of the fp32 scores,
-//      each step counting with 64-bit wave ballots (no shuffles); then one
-//      ordered pass with ballots emits every index above it plus the
-//      lowest-index ties, already in ascending order.
+//      the fly from the LDS scores (D/16 waves; their Vc loads are issued at
+//      the start so that the latency overlaps phase 1);
+//   4. concurrently on the other waves, top-K per row: the K-th largest
+//      score is found exactly by a 32-step bitwise search over
+//      order-preserving uint32 keys of the fp32 scores, each step counting
+//      with 64-bit wave ballots (no shuffles); then one ordered pass with
+//      ballots emits every index above it plus the lowest-index ties,
+//      already in ascending order.
 // Everything is fp32 (no bf16 rounding of means or scores), so the selection
 // differs from an exact one only where two scores are within fp32 rounding.
 #include "vsa_internal.h"
@@ -62,7 +64,11 @@ __device__ inline void store_out(uint16_t* p, float x) { *p = f32_to_bf16_rne(x)
 
 constexpr int kRows = 16;
 
-constexpr int kWaves = 8;   // 512 threads: 2 rows of statistics / top-K per wave
+constexpr int kWaves = 8;   // backward kernels: 512 threads
+// Forward kernel: 1024 threads.  One row of statistics per wave; then the
+// first D/16 waves form O_coarse while the others run the top-K, so the two
+// final phases overlap instead of following each other.
+constexpr int kFwdWaves = 16;
 
 // 16x16 fp32 tile out[r][j] = dot(A row r, B row j) over D, with the D/4
 // MFMA steps spread over 4 independent accumulators (short dependency chains).
@@ -88,19 +94,20 @@ __device__ __forceinline__ f32x4 dot_tile(const float4 (&af)[D / 16],
 
 // KPL: keys per lane in the top-K, ceil(C / 64) rounded up to a power of two.
 template <typename TOut, int D, int KPL>
-__global__ __launch_bounds__(64 * kWaves) void coarse_kernel(const float* __restrict__ qm,
-                                                            const float* __restrict__ km,
-                                                            const float* __restrict__ vm,
-                                                            TOut* __restrict__ oc,
-                                                            int32_t* __restrict__ idx,
-                                                            float* __restrict__ scores, Geo g,
-                                                            int ldc) {
+__global__ __launch_bounds__(64 * kFwdWaves) void coarse_kernel(const float* __restrict__ qm,
+                                                               const float* __restrict__ km,
+                                                               const float* __restrict__ vm,
+                                                               TOut* __restrict__ oc,
+                                                               int32_t* __restrict__ idx,
+                                                               float* __restrict__ scores, Geo g,
+                                                               int ldc) {
   extern __shared__ float lds[];
   float* sc = lds;                       // [kRows][ldc]
   float* rowmax = lds + kRows * ldc;     // [kRows]
   float* rowinv = rowmax + kRows;        // [kRows]
 
   constexpr float kScale = (D == 64) ? 0.125f : 0.08838834764831845f;  // 1/sqrt(D)
+  constexpr int kOcWaves = D / 16;       // one 16-wide slice of O_coarse per wave
   const int C = g.C;
   const int64_t bh = blockIdx.y;
   const int row0 = blockIdx.x * kRows;
@@ -109,6 +116,19 @@ __global__ __launch_bounds__(64 * kWaves) void coarse_kernel(const float* __rest
   const float* qh = qm + bh * C * D;
   const float* kh = km + bh * C * D;
   const float* vh = vm + bh * C * D;
+
+  // Vc operand of the first 64 key cubes for the O_coarse waves, issued now
+  // so that its latency overlaps the score phase.  Lane (li, lg) feeds
+  // B[k=lg][n=li] = Vc[j][16*wave + li] for j = j0 + 16(u/4) + 4lg + u%4.
+  float b[16];
+  auto load_batch = [&](int j0) {
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const int j = j0 + 16 * (u >> 2) + 4 * lg + (u & 3);
+      b[u] = (j < C) ? vh[(int64_t)j * D + wave * 16 + li] : 0.f;
+    }
+  };
+  if (wave < kOcWaves) load_batch(0);
 
   // -- 1. scores.  Lane (li, lg) feeds A[m=li][k=lg] and B[k=lg][n=li]; the
   // t-th of four MFMAs per 16-wide slice of D uses d = 16*kk + 4*lg + t for
@@ -122,7 +142,7 @@ __global__ __launch_bounds__(64 * kWaves) void coarse_kernel(const float* __rest
                        : make_float4(0.f, 0.f, 0.f, 0.f);
   }
   const int ntile = (C + 15) / 16;
-  for (int ct = wave; ct < ntile; ct += kWaves) {
+  for (int ct = wave; ct < ntile; ct += kFwdWaves) {
     const int col = ct * 16 + li;
     const f32x4 acc = dot_tile<D>(qf, kh + (int64_t)col * D, col < C, lg);
     // acc[r] is the dot product of query row 4*lg + r with key column col
@@ -137,8 +157,8 @@ __global__ __launch_bounds__(64 * kWaves) void coarse_kernel(const float* __rest
   }
   __syncthreads();
 
-  // -- 2. softmax statistics per row
-  for (int rr = wave; rr < kRows; rr += kWaves) {
+  // -- 2. softmax statistics, one row per wave
+  for (int rr = wave; rr < kRows; rr += kFwdWaves) {
     const float* srow = sc + rr * ldc;
     float m = -INFINITY;
     for (int j = lane; j < C; j += 64) m = fmaxf(m, srow[j]);
@@ -153,52 +173,43 @@ __global__ __launch_bounds__(64 * kWaves) void coarse_kernel(const float* __rest
   }
   __syncthreads();
 
-  // -- 3. O_coarse = P Vc: A[m=li][k=lg] = P[row li][j], B[k=lg][n=li] = Vc[j][col].
-  // Each batch of 16 Vc loads is issued one batch ahead of its MFMAs; the 16
-  // MFMAs of a batch alternate between 4 accumulators.
-  {
+  if (wave < kOcWaves) {
+    // -- 3. O_coarse = P Vc: A[m=li][k=lg] = P[row li][j], B[k=lg][n=li] = Vc[j][col].
+    // Each batch of 16 Vc loads is issued one batch ahead of its MFMAs; the 16
+    // MFMAs of a batch alternate between 4 accumulators.
     const float mrow = rowmax[li], irow = rowinv[li];
     const float* prow = sc + li * ldc;
-    for (int dt = wave; dt < D / 16; dt += kWaves) {
-      f32x4 acc[4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f},
-                      {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-      float b[16];
-      auto load_batch = [&](int j0) {
+    const int dt = wave;
+    f32x4 acc[4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f},
+                    {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+    for (int j0 = 0; j0 < C; j0 += 64) {
+      float bc[16], a[16];
 #pragma unroll
-        for (int u = 0; u < 16; ++u) {
-          const int j = j0 + 16 * (u >> 2) + 4 * lg + (u & 3);
-          b[u] = (j < C) ? vh[(int64_t)j * D + dt * 16 + li] : 0.f;
-        }
-      };
-      load_batch(0);
-      for (int j0 = 0; j0 < C; j0 += 64) {
-        float bc[16], a[16];
+      for (int u = 0; u < 16; ++u) bc[u] = b[u];
+      if (j0 + 64 < C) load_batch(j0 + 64);
 #pragma unroll
-        for (int u = 0; u < 16; ++u) bc[u] = b[u];
-        if (j0 + 64 < C) load_batch(j0 + 64);
-#pragma unroll
-        for (int u = 0; u < 16; ++u) {
-          const int j = j0 + 16 * (u >> 2) + 4 * lg + (u & 3);
-          a[u] = (j < C) ? __expf(prow[j] - mrow) * irow : 0.f;
-        }
-#pragma unroll
-        for (int u = 0; u < 16; ++u)
-          acc[u & 3] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[u], bc[u], acc[u & 3], 0, 0, 0);
+      for (int u = 0; u < 16; ++u) {
+        const int j = j0 + 16 * (u >> 2) + 4 * lg + (u & 3);
+        a[u] = (j < C) ? __expf(prow[j] - mrow) * irow : 0.f;
       }
-      const f32x4 tot = (acc[0] + acc[1]) + (acc[2] + acc[3]);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int row = row0 + 4 * lg + r;
-        if (row < C) store_out(oc + (bh * C + row) * D + dt * 16 + li, tot[r]);
-      }
+      for (int u = 0; u < 16; ++u)
+        acc[u & 3] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[u], bc[u], acc[u & 3], 0, 0, 0);
     }
+    const f32x4 tot = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int row = row0 + 4 * lg + r;
+      if (row < C) store_out(oc + (bh * C + row) * D + dt * 16 + li, tot[r]);
+    }
+    return;
   }
 
-  // -- 4. top-K per row (one wave per row).  Counting a predicate over the
-  // row is one 64-bit ballot plus a scalar popcount per 64 keys.
+  // -- 4. top-K per row, on the remaining waves.  Counting a predicate over
+  // the row is one 64-bit ballot plus a scalar popcount per 64 keys.
   const int K = g.K;
   const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  for (int rr = wave; rr < kRows; rr += kWaves) {
+  for (int rr = wave - kOcWaves; rr < kRows; rr += kFwdWaves - kOcWaves) {
     if (row0 + rr >= C) break;
     const float* srow = sc + rr * ldc;
     uint32_t key[KPL];
@@ -251,7 +262,7 @@ hipError_t launch_kpl(const Geo& g, const float* qm, const float* km, const floa
                                              static_cast<int>(lds));
     if (e != hipSuccess) return e;
   }
-  return launch_kernel(kern, dim3(ntile, g.B * g.H), dim3(64 * kWaves), lds, s, qm, km, vm,
+  return launch_kernel(kern, dim3(ntile, g.B * g.H), dim3(64 * kFwdWaves), lds, s, qm, km, vm,
                        static_cast<TOut*>(oc), idx, scores, g, ldc);
 }
 
