@@ -105,9 +105,11 @@ __global__ __launch_bounds__(64 * kFwdWaves) void coarse_kernel(const float* __r
   float* sc = lds;                       // [kRows][ldc]
   float* rowmax = lds + kRows * ldc;     // [kRows]
   float* rowinv = rowmax + kRows;        // [kRows]
+  float* qs = rowinv + kRows;            // [kRows][D + 4]: the query rows, loaded once
 
   constexpr float kScale = (D == 64) ? 0.125f : 0.08838834764831845f;  // 1/sqrt(D)
   constexpr int kOcWaves = D / 16;       // one 16-wide slice of O_coarse per wave
+  constexpr int kQS = D + 4;             // padded row stride of qs (floats)
   const int C = g.C;
   const int64_t bh = blockIdx.y;
   const int row0 = blockIdx.x * kRows;
@@ -133,15 +135,23 @@ __global__ __launch_bounds__(64 * kFwdWaves) void coarse_kernel(const float* __r
   // -- 1. scores.  Lane (li, lg) feeds A[m=li][k=lg] and B[k=lg][n=li]; the
   // t-th of four MFMAs per 16-wide slice of D uses d = 16*kk + 4*lg + t for
   // both operands, so their products pair up on the same d.
+  // The 16 query rows are read from memory once, coalesced, into LDS: every
+  // scoring wave needs all of them, and a per-wave load would fetch them 16
+  // times over the workgroup's vector memory path.
+  for (int e = threadIdx.x; e < kRows * D / 4; e += 64 * kFwdWaves) {
+    const int r = e / (D / 4), c4 = e % (D / 4);
+    const float4 x = (row0 + r < C) ? *reinterpret_cast<const float4*>(qh + (int64_t)(row0 + r) * D + 4 * c4)
+                                    : make_float4(0.f, 0.f, 0.f, 0.f);
+    *reinterpret_cast<float4*>(qs + r * kQS + 4 * c4) = x;
+  }
+  __syncthreads();
+  const int ntile = (C + 15) / 16;
   float4 qf[D / 16];
-  {
-    const int r = row0 + li;
+  if (wave < ntile) {
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk)
-      qf[kk] = (r < C) ? *reinterpret_cast<const float4*>(qh + (int64_t)r * D + 16 * kk + 4 * lg)
-                       : make_float4(0.f, 0.f, 0.f, 0.f);
+      qf[kk] = *reinterpret_cast<const float4*>(qs + li * kQS + 16 * kk + 4 * lg);
   }
-  const int ntile = (C + 15) / 16;
   for (int ct = wave; ct < ntile; ct += kFwdWaves) {
     const int col = ct * 16 + li;
     const f32x4 acc = dot_tile<D>(qf, kh + (int64_t)col * D, col < C, lg);
@@ -254,7 +264,7 @@ hipError_t launch_kpl(const Geo& g, const float* qm, const float* km, const floa
                       int32_t* idx, float* scores, hipStream_t s) {
   const int ntile = (g.C + 15) / 16;
   const int ldc = ntile * 16 + 1;  // odd stride spreads a column over the LDS banks
-  const size_t lds = (size_t)(kRows * ldc + 2 * kRows) * sizeof(float);
+  const size_t lds = (size_t)(kRows * ldc + 2 * kRows + kRows * (D + 4)) * sizeof(float);
   auto* kern = coarse_kernel<TOut, D, KPL>;
   if (lds > 65536) {
     const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
