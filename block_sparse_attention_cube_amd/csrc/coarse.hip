@@ -113,7 +113,7 @@ __global__ __launch_bounds__(64 * kFwdWaves) void coarse_kernel(const float* __r
   const int C = g.C;
   const int64_t bh = blockIdx.y;
   const int row0 = blockIdx.x * kRows;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int li = lane & 15, lg = lane >> 4;
   const float* qh = qm + bh * C * D;
   const float* kh = km + bh * C * D;
@@ -216,45 +216,64 @@ __global__ __launch_bounds__(64 * kFwdWaves) void coarse_kernel(const float* __r
   }
 
   // -- 4. top-K per row, on the remaining waves.  Counting a predicate over
-  // the row is one 64-bit ballot plus a scalar popcount per 64 keys.
+  // the row is one 64-bit ballot plus a scalar popcount per 64 keys.  A wave
+  // searches two rows at once where registers allow: the two bit searches
+  // are independent chains that overlap each other's latency.
+  constexpr int kPair = KPL <= 8 ? 2 : 1;
+  constexpr int kTopkWaves = kFwdWaves - kOcWaves;
   const int K = g.K;
   const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  for (int rr = wave - kOcWaves; rr < kRows; rr += kFwdWaves - kOcWaves) {
-    if (row0 + rr >= C) break;
-    const float* srow = sc + rr * ldc;
-    uint32_t key[KPL];
+  for (int base = wave - kOcWaves; base < kRows; base += kPair * kTopkWaves) {
+    uint32_t key[kPair][KPL];
+    bool live[kPair];
 #pragma unroll
-    for (int e = 0; e < KPL; ++e) {
-      const int j = e * 64 + lane;
-      key[e] = (j < C) ? score_key(srow[j]) : 0u;  // 0 is below every score key
+    for (int p = 0; p < kPair; ++p) {
+      const int rr = base + p * kTopkWaves;
+      live[p] = rr < kRows && row0 + rr < C;
+      const float* srow = sc + (live[p] ? rr : 0) * ldc;
+#pragma unroll
+      for (int e = 0; e < KPL; ++e) {
+        const int j = e * 64 + lane;
+        key[p][e] = (live[p] && j < C) ? score_key(srow[j]) : 0u;  // 0 is below every score key
+      }
     }
+    if (!live[0]) break;
     // largest threshold t with #{key >= t} >= K, i.e. the K-th largest key
-    uint32_t thr = 0u;
+    uint32_t thr[kPair];
+#pragma unroll
+    for (int p = 0; p < kPair; ++p) thr[p] = 0u;
     for (int bit = 31; bit >= 0; --bit) {
-      const uint32_t cand = thr | (1u << bit);
-      int cnt = 0;
 #pragma unroll
-      for (int e = 0; e < KPL; ++e) cnt += __popcll(__ballot(key[e] >= cand));
-      if (cnt >= K) thr = cand;
+      for (int p = 0; p < kPair; ++p) {
+        const uint32_t cand = thr[p] | (1u << bit);
+        int cnt = 0;
+#pragma unroll
+        for (int e = 0; e < KPL; ++e) cnt += __popcll(__ballot(key[p][e] >= cand));
+        if (cnt >= K) thr[p] = cand;
+      }
     }
-    int gt = 0;
 #pragma unroll
-    for (int e = 0; e < KPL; ++e) gt += __popcll(__ballot(key[e] > thr));
-    const int need = K - gt;  // ties at the threshold to keep, lowest index first
-    int ties_before = 0, sel_before = 0;
-    int32_t* out = idx + (bh * C + row0 + rr) * K;
+    for (int p = 0; p < kPair; ++p) {
+      if (!live[p]) continue;
+      int gt = 0;
 #pragma unroll
-    for (int e = 0; e < KPL; ++e) {
-      const int j = e * 64 + lane;
-      const bool is_gt = (j < C) && key[e] > thr;
-      const bool is_eq = (j < C) && key[e] == thr;
-      const uint64_t eqm = __ballot(is_eq);
-      const int eq_rank = ties_before + __popcll(eqm & lt_mask);
-      const bool take = is_gt || (is_eq && eq_rank < need);
-      const uint64_t takem = __ballot(take);
-      if (take) out[sel_before + __popcll(takem & lt_mask)] = j;
-      ties_before += __popcll(eqm);
-      sel_before += __popcll(takem);
+      for (int e = 0; e < KPL; ++e) gt += __popcll(__ballot(key[p][e] > thr[p]));
+      const int need = K - gt;  // ties at the threshold to keep, lowest index first
+      int ties_before = 0, sel_before = 0;
+      int32_t* out = idx + (bh * C + row0 + base + p * kTopkWaves) * K;
+#pragma unroll
+      for (int e = 0; e < KPL; ++e) {
+        const int j = e * 64 + lane;
+        const bool is_gt = (j < C) && key[p][e] > thr[p];
+        const bool is_eq = (j < C) && key[p][e] == thr[p];
+        const uint64_t eqm = __ballot(is_eq);
+        const int eq_rank = ties_before + __popcll(eqm & lt_mask);
+        const bool take = is_gt || (is_eq && eq_rank < need);
+        const uint64_t takem = __ballot(take);
+        if (take) out[sel_before + __popcll(takem & lt_mask)] = j;
+        ties_before += __popcll(eqm);
+        sel_before += __popcll(takem);
+      }
     }
   }
 }
@@ -376,7 +395,7 @@ __global__ __launch_bounds__(64 * kWaves) void coarse_bwd_rows_kernel(
   const int C = g.C;
   const int64_t bh = blockIdx.y;
   const int row0 = blockIdx.x * kRows;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t hoff = bh * C * D;
   rows_dot<D>(qm + hoff, row0, km + hoff, C, kScale, s1, ldc, wave, lane);
   rows_dot<D>(docs + hoff, row0, vm + hoff, C, 1.f, s2, ldc, wave, lane);
@@ -422,7 +441,7 @@ __global__ __launch_bounds__(64 * kWaves) void coarse_bwd_cols_kernel(
   const int C = g.C;
   const int64_t bh = blockIdx.y;
   const int col0 = blockIdx.x * kRows;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t hoff = bh * C * D;
   rows_dot<D>(km + hoff, col0, qm + hoff, C, kScale, t1, ldc, wave, lane);
   rows_dot<D>(vm + hoff, col0, docs + hoff, C, 1.f, t2, ldc, wave, lane);
