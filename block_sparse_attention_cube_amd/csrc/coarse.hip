@@ -72,16 +72,18 @@ constexpr int kFwdWaves = 16;
 
 // 16x16 fp32 tile out[r][j] = dot(A row r, B row j) over D, with the D/4
 // MFMA steps spread over 4 independent accumulators (short dependency chains).
+// brow is always a real row: callers clamp indices past the last cube, and the
+// tile entries they produce are never consumed.  Unguarded loads keep the
+// compiler from wrapping each one in its own branch.
 template <int D>
 __device__ __forceinline__ f32x4 dot_tile(const float4 (&af)[D / 16],
-                                          const float* __restrict__ brow, bool valid, int lg) {
+                                          const float* __restrict__ brow, int lg) {
   f32x4 acc[4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f},
                   {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
   float4 bf[D / 16];
 #pragma unroll
   for (int kk = 0; kk < D / 16; ++kk)
-    bf[kk] = valid ? *reinterpret_cast<const float4*>(brow + 16 * kk + 4 * lg)
-                   : make_float4(0.f, 0.f, 0.f, 0.f);
+    bf[kk] = *reinterpret_cast<const float4*>(brow + 16 * kk + 4 * lg);
 #pragma unroll
   for (int kk = 0; kk < D / 16; ++kk) {
     acc[0] = __builtin_amdgcn_mfma_f32_16x16x4f32(af[kk].x, bf[kk].x, acc[0], 0, 0, 0);
@@ -127,7 +129,7 @@ __global__ __launch_bounds__(64 * kFwdWaves) void coarse_kernel(const float* __r
 #pragma unroll
     for (int u = 0; u < 16; ++u) {
       const int j = j0 + 16 * (u >> 2) + 4 * lg + (u & 3);
-      b[u] = (j < C) ? vh[(int64_t)j * D + wave * 16 + li] : 0.f;
+      b[u] = vh[(int64_t)min(j, C - 1) * D + wave * 16 + li];   // j >= C: weight 0 below
     }
   };
   if (wave < kOcWaves) load_batch(0);
@@ -154,7 +156,7 @@ __global__ __launch_bounds__(64 * kFwdWaves) void coarse_kernel(const float* __r
   }
   for (int ct = wave; ct < ntile; ct += kFwdWaves) {
     const int col = ct * 16 + li;
-    const f32x4 acc = dot_tile<D>(qf, kh + (int64_t)col * D, col < C, lg);
+    const f32x4 acc = dot_tile<D>(qf, kh + (int64_t)min(col, C - 1) * D, lg);
     // acc[r] is the dot product of query row 4*lg + r with key column col
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -200,7 +202,8 @@ __global__ __launch_bounds__(64 * kFwdWaves) void coarse_kernel(const float* __r
 #pragma unroll
       for (int u = 0; u < 16; ++u) {
         const int j = j0 + 16 * (u >> 2) + 4 * lg + (u & 3);
-        a[u] = (j < C) ? __expf(prow[j] - mrow) * irow : 0.f;
+        const float e = __expf(prow[min(j, C - 1)] - mrow) * irow;
+        a[u] = (j < C) ? e : 0.f;
       }
 #pragma unroll
       for (int u = 0; u < 16; ++u)
@@ -318,7 +321,9 @@ hipError_t launch_typed(const Geo& g, const float* qm, const float* km, const fl
 // dSc column-wise from those statistics.  Both are deterministic.
 
 // out[r][j] = scale * dot(A[r], B[j]) for the 16 rows r of A starting at a0
-// (rows >= C read as zero) and every j < C, into LDS with row stride ldc.
+// and every j of the 16-aligned column range, into LDS with row stride ldc.
+// Rows and columns past the last cube repeat the last one (finite values that
+// no later step consumes).
 template <int D>
 __device__ __forceinline__ void rows_dot(const float* __restrict__ A, int a0,
                                          const float* __restrict__ B, int C, float scale,
@@ -328,12 +333,11 @@ __device__ __forceinline__ void rows_dot(const float* __restrict__ A, int a0,
   const int r = a0 + li;
 #pragma unroll
   for (int kk = 0; kk < D / 16; ++kk)
-    af[kk] = (r < C) ? *reinterpret_cast<const float4*>(A + (int64_t)r * D + 16 * kk + 4 * lg)
-                     : make_float4(0.f, 0.f, 0.f, 0.f);
+    af[kk] = *reinterpret_cast<const float4*>(A + (int64_t)min(r, C - 1) * D + 16 * kk + 4 * lg);
   const int ntile = (C + 15) / 16;
   for (int ct = wave; ct < ntile; ct += kWaves) {
     const int col = ct * 16 + li;
-    const f32x4 acc = dot_tile<D>(af, B + (int64_t)col * D, col < C, lg);
+    const f32x4 acc = dot_tile<D>(af, B + (int64_t)min(col, C - 1) * D, lg);
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr) out[(4 * lg + rr) * ldc + col] = acc[rr] * scale;
   }
@@ -356,7 +360,7 @@ __device__ __forceinline__ void lds_times(const float* T, int ldc, const float* 
 #pragma unroll
       for (int u = 0; u < 16; ++u) {
         const int j = j0 + 16 * (u >> 2) + 4 * lg + (u & 3);
-        b[u] = (j < C) ? Y[(int64_t)j * D + dt * 16 + li] : 0.f;
+        b[u] = Y[(int64_t)min(j, C - 1) * D + dt * 16 + li];   // j >= C: weight 0 below
       }
     };
     load_batch(0);
@@ -368,7 +372,8 @@ __device__ __forceinline__ void lds_times(const float* T, int ldc, const float* 
 #pragma unroll
       for (int u = 0; u < 16; ++u) {
         const int j = j0 + 16 * (u >> 2) + 4 * lg + (u & 3);
-        a[u] = (j < C) ? trow[j] : 0.f;
+        const float t = trow[min(j, C - 1)];
+        a[u] = (j < C) ? t : 0.f;
       }
 #pragma unroll
       for (int u = 0; u < 16; ++u)
