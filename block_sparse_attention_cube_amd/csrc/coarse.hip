@@ -1,19 +1,24 @@
 // Coarse stage of VSA: cube-level attention and the top-K block selection.
 //
 // Input: fp32 means of q, k, v per cube, [B,H,C,D] (written by the reorder).
-// One workgroup (16 waves) owns 16 query-cube rows of one head:
+// Two workgroups (16 waves each) own 16 query-cube rows of one head; both
+// compute
 //   1. Sc[16, C] = Qc Kc^T / sqrt(D) on fp32 MFMA (v_mfma_f32_16x16x4_f32),
 //      kept in LDS (16 x C fp32, C <= 2048) and optionally written out;
+// then the first one does
 //   2. row max and 1/sum(exp) per row (one wave per row, wave reductions);
 //   3. O_coarse[16, D] = softmax(Sc) Vc on fp32 MFMA, probabilities formed on
-//      the fly from the LDS scores (D/16 waves; their Vc loads are issued at
-//      the start so that the latency overlaps phase 1);
-//   4. concurrently on the other waves, top-K per row: the K-th largest
-//      score is found exactly by a 32-step bitwise search over
-//      order-preserving uint32 keys of the fp32 scores, each step counting
-//      with 64-bit wave ballots (no shuffles); then one ordered pass with
-//      ballots emits every index above it plus the lowest-index ties,
-//      already in ascending order.
+//      the fly from the LDS scores, each 16-wide slice of D split over waves
+//      by key batches and summed through LDS (their first Vc loads are issued
+//      at the start so that the latency overlaps phase 1);
+// and the second one
+//   4. the top-K of each row (one row per wave): the K-th largest score is
+//      found exactly by a 32-step bitwise search over order-preserving uint32
+//      keys of the fp32 scores, each step counting with 64-bit wave ballots
+//      (no shuffles); then one ordered pass with ballots emits every index
+//      above it plus the lowest-index ties, already in ascending order.
+// The split costs one more score computation (cheap) and lets the two phases
+// run on separate CUs instead of competing for one CU's issue slots.
 // Everything is fp32 (no bf16 rounding of means or scores), so the selection
 // differs from an exact one only where two scores are within fp32 rounding.
 #include "vsa_internal.h"
@@ -65,9 +70,7 @@ __device__ inline void store_out(uint16_t* p, float x) { *p = f32_to_bf16_rne(x)
 constexpr int kRows = 16;
 
 constexpr int kWaves = 8;   // backward kernels: 512 threads
-// Forward kernel: 1024 threads.  One row of statistics per wave; then the
-// first D/16 waves form O_coarse while the others run the top-K, so the two
-// final phases overlap instead of following each other.
+// Forward kernel: 1024 threads, one statistics / top-K row per wave.
 constexpr int kFwdWaves = 16;
 
 // 16x16 fp32 tile out[r][j] = dot(A row r, B row j) over D, with the D/4
@@ -103,36 +106,40 @@ __global__ __launch_bounds__(64 * kFwdWaves) void coarse_kernel(const float* __r
                                                                int32_t* __restrict__ idx,
                                                                float* __restrict__ scores, Geo g,
                                                                int ldc) {
+  constexpr int kOcWaves = D / 16;                // 16-wide slices of O_coarse
+  constexpr int kHalves = kFwdWaves / kOcWaves;   // waves sharing one slice, over key batches
+  constexpr int kQS = D + 4;                      // padded row stride of qs (floats)
   extern __shared__ float lds[];
   float* sc = lds;                       // [kRows][ldc]
   float* rowmax = lds + kRows * ldc;     // [kRows]
   float* rowinv = rowmax + kRows;        // [kRows]
-  float* qs = rowinv + kRows;            // [kRows][D + 4]: the query rows, loaded once
+  float* qs = rowinv + kRows;            // [kRows][kQS]: the query rows, loaded once
+  float* part = qs + kRows * kQS;        // [kFwdWaves - kOcWaves][64][4]: O_coarse partial sums
 
   constexpr float kScale = (D == 64) ? 0.125f : 0.08838834764831845f;  // 1/sqrt(D)
-  constexpr int kOcWaves = D / 16;       // one 16-wide slice of O_coarse per wave
-  constexpr int kQS = D + 4;             // padded row stride of qs (floats)
   const int C = g.C;
   const int64_t bh = blockIdx.y;
   const int row0 = blockIdx.x * kRows;
+  const bool oc_role = blockIdx.z == 0;  // z = 0: statistics and O_coarse; z = 1: top-K
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int li = lane & 15, lg = lane >> 4;
   const float* qh = qm + bh * C * D;
   const float* kh = km + bh * C * D;
   const float* vh = vm + bh * C * D;
+  const int dt = wave % kOcWaves, half = wave / kOcWaves;
 
-  // Vc operand of the first 64 key cubes for the O_coarse waves, issued now
-  // so that its latency overlaps the score phase.  Lane (li, lg) feeds
-  // B[k=lg][n=li] = Vc[j][16*wave + li] for j = j0 + 16(u/4) + 4lg + u%4.
+  // Vc operand of this wave's first key batch (O_coarse workgroups), issued
+  // now so that its latency overlaps the score phase.  Lane (li, lg) feeds
+  // B[k=lg][n=li] = Vc[j][16*dt + li] for j = j0 + 16(u/4) + 4lg + u%4.
   float b[16];
   auto load_batch = [&](int j0) {
 #pragma unroll
     for (int u = 0; u < 16; ++u) {
       const int j = j0 + 16 * (u >> 2) + 4 * lg + (u & 3);
-      b[u] = vh[(int64_t)min(j, C - 1) * D + wave * 16 + li];   // j >= C: weight 0 below
+      b[u] = vh[(int64_t)min(j, C - 1) * D + dt * 16 + li];   // j >= C: weight 0 below
     }
   };
-  if (wave < kOcWaves) load_batch(0);
+  if (oc_role) load_batch(64 * half);
 
   // -- 1. scores.  Lane (li, lg) feeds A[m=li][k=lg] and B[k=lg][n=li]; the
   // t-th of four MFMAs per 16-wide slice of D uses d = 16*kk + 4*lg + t for
@@ -163,42 +170,42 @@ __global__ __launch_bounds__(64 * kFwdWaves) void coarse_kernel(const float* __r
       const int rr = 4 * lg + r;
       const float s = acc[r] * kScale;
       sc[rr * ldc + col] = s;
-      if (scores != nullptr && row0 + rr < C && col < C)
+      if (oc_role && scores != nullptr && row0 + rr < C && col < C)
         scores[(bh * C + row0 + rr) * C + col] = s;
     }
   }
   __syncthreads();
 
-  // -- 2. softmax statistics, one row per wave
-  for (int rr = wave; rr < kRows; rr += kFwdWaves) {
-    const float* srow = sc + rr * ldc;
-    float m = -INFINITY;
-    for (int j = lane; j < C; j += 64) m = fmaxf(m, srow[j]);
-    m = wave_max(m);
-    float s = 0.f;
-    for (int j = lane; j < C; j += 64) s += __expf(srow[j] - m);
-    s = wave_sum(s);
-    if (lane == 0) {
-      rowmax[rr] = m;
-      rowinv[rr] = 1.f / s;
+  if (oc_role) {
+    // -- 2. softmax statistics, one row per wave
+    for (int rr = wave; rr < kRows; rr += kFwdWaves) {
+      const float* srow = sc + rr * ldc;
+      float m = -INFINITY;
+      for (int j = lane; j < C; j += 64) m = fmaxf(m, srow[j]);
+      m = wave_max(m);
+      float s = 0.f;
+      for (int j = lane; j < C; j += 64) s += __expf(srow[j] - m);
+      s = wave_sum(s);
+      if (lane == 0) {
+        rowmax[rr] = m;
+        rowinv[rr] = 1.f / s;
+      }
     }
-  }
-  __syncthreads();
+    __syncthreads();
 
-  if (wave < kOcWaves) {
     // -- 3. O_coarse = P Vc: A[m=li][k=lg] = P[row li][j], B[k=lg][n=li] = Vc[j][col].
-    // Each batch of 16 Vc loads is issued one batch ahead of its MFMAs; the 16
-    // MFMAs of a batch alternate between 4 accumulators.
+    // The kHalves waves of a slice take every kHalves-th batch of 64 keys;
+    // each batch of 16 Vc loads is issued one batch ahead of its MFMAs, and
+    // the 16 MFMAs of a batch alternate between 4 accumulators.
     const float mrow = rowmax[li], irow = rowinv[li];
     const float* prow = sc + li * ldc;
-    const int dt = wave;
     f32x4 acc[4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f},
                     {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-    for (int j0 = 0; j0 < C; j0 += 64) {
+    for (int j0 = 64 * half; j0 < C; j0 += 64 * kHalves) {
       float bc[16], a[16];
 #pragma unroll
       for (int u = 0; u < 16; ++u) bc[u] = b[u];
-      if (j0 + 64 < C) load_batch(j0 + 64);
+      if (j0 + 64 * kHalves < C) load_batch(j0 + 64 * kHalves);
 #pragma unroll
       for (int u = 0; u < 16; ++u) {
         const int j = j0 + 16 * (u >> 2) + 4 * lg + (u & 3);
@@ -210,74 +217,65 @@ __global__ __launch_bounds__(64 * kFwdWaves) void coarse_kernel(const float* __r
         acc[u & 3] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[u], bc[u], acc[u & 3], 0, 0, 0);
     }
     const f32x4 tot = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+    // the slice's partial sums meet in LDS, added in a fixed order
+    if (half > 0) *reinterpret_cast<f32x4*>(part + ((wave - kOcWaves) * 64 + lane) * 4) = tot;
+    __syncthreads();
+    if (half == 0) {
+      f32x4 sum = tot;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int row = row0 + 4 * lg + r;
-      if (row < C) store_out(oc + (bh * C + row) * D + dt * 16 + li, tot[r]);
+      for (int h = 1; h < kHalves; ++h)
+        sum += *reinterpret_cast<const f32x4*>(part + (((h - 1) * kOcWaves + dt) * 64 + lane) * 4);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = row0 + 4 * lg + r;
+        if (row < C) store_out(oc + (bh * C + row) * D + dt * 16 + li, sum[r]);
+      }
     }
     return;
   }
 
-  // -- 4. top-K per row, on the remaining waves.  Counting a predicate over
-  // the row is one 64-bit ballot plus a scalar popcount per 64 keys.  A wave
-  // searches two rows at once where registers allow: the two bit searches
-  // are independent chains that overlap each other's latency.
-  constexpr int kPair = KPL <= 8 ? 2 : 1;
-  constexpr int kTopkWaves = kFwdWaves - kOcWaves;
+  // -- 4. top-K, one row per wave.  Counting a predicate over the row is one
+  // 64-bit ballot plus a scalar popcount per 64 keys.
+  static_assert(kRows == kFwdWaves, "one top-K row per wave");
+  const int rr = wave;
+  if (row0 + rr >= C) return;
   const int K = g.K;
   const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  for (int base = wave - kOcWaves; base < kRows; base += kPair * kTopkWaves) {
-    uint32_t key[kPair][KPL];
-    bool live[kPair];
+  const float* srow = sc + rr * ldc;
+  uint32_t key[KPL];
 #pragma unroll
-    for (int p = 0; p < kPair; ++p) {
-      const int rr = base + p * kTopkWaves;
-      live[p] = rr < kRows && row0 + rr < C;
-      const float* srow = sc + (live[p] ? rr : 0) * ldc;
+  for (int e = 0; e < KPL; ++e) {
+    const int j = e * 64 + lane;
+    key[e] = (j < C) ? score_key(srow[j]) : 0u;  // 0 is below every score key
+  }
+  // largest threshold t with #{key >= t} >= K, i.e. the K-th largest key
+  uint32_t thr = 0u;
+#pragma unroll 8
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t cand = thr | (1u << bit);
+    int cnt = 0;
 #pragma unroll
-      for (int e = 0; e < KPL; ++e) {
-        const int j = e * 64 + lane;
-        key[p][e] = (live[p] && j < C) ? score_key(srow[j]) : 0u;  // 0 is below every score key
-      }
-    }
-    if (!live[0]) break;
-    // largest threshold t with #{key >= t} >= K, i.e. the K-th largest key
-    uint32_t thr[kPair];
+    for (int e = 0; e < KPL; ++e) cnt += __popcll(__ballot(key[e] >= cand));
+    if (cnt >= K) thr = cand;
+  }
+  int gt = 0;
 #pragma unroll
-    for (int p = 0; p < kPair; ++p) thr[p] = 0u;
-    for (int bit = 31; bit >= 0; --bit) {
+  for (int e = 0; e < KPL; ++e) gt += __popcll(__ballot(key[e] > thr));
+  const int need = K - gt;  // ties at the threshold to keep, lowest index first
+  int ties_before = 0, sel_before = 0;
+  int32_t* out = idx + (bh * C + row0 + rr) * K;
 #pragma unroll
-      for (int p = 0; p < kPair; ++p) {
-        const uint32_t cand = thr[p] | (1u << bit);
-        int cnt = 0;
-#pragma unroll
-        for (int e = 0; e < KPL; ++e) cnt += __popcll(__ballot(key[p][e] >= cand));
-        if (cnt >= K) thr[p] = cand;
-      }
-    }
-#pragma unroll
-    for (int p = 0; p < kPair; ++p) {
-      if (!live[p]) continue;
-      int gt = 0;
-#pragma unroll
-      for (int e = 0; e < KPL; ++e) gt += __popcll(__ballot(key[p][e] > thr[p]));
-      const int need = K - gt;  // ties at the threshold to keep, lowest index first
-      int ties_before = 0, sel_before = 0;
-      int32_t* out = idx + (bh * C + row0 + base + p * kTopkWaves) * K;
-#pragma unroll
-      for (int e = 0; e < KPL; ++e) {
-        const int j = e * 64 + lane;
-        const bool is_gt = (j < C) && key[p][e] > thr[p];
-        const bool is_eq = (j < C) && key[p][e] == thr[p];
-        const uint64_t eqm = __ballot(is_eq);
-        const int eq_rank = ties_before + __popcll(eqm & lt_mask);
-        const bool take = is_gt || (is_eq && eq_rank < need);
-        const uint64_t takem = __ballot(take);
-        if (take) out[sel_before + __popcll(takem & lt_mask)] = j;
-        ties_before += __popcll(eqm);
-        sel_before += __popcll(takem);
-      }
-    }
+  for (int e = 0; e < KPL; ++e) {
+    const int j = e * 64 + lane;
+    const bool is_gt = (j < C) && key[e] > thr;
+    const bool is_eq = (j < C) && key[e] == thr;
+    const uint64_t eqm = __ballot(is_eq);
+    const int eq_rank = ties_before + __popcll(eqm & lt_mask);
+    const bool take = is_gt || (is_eq && eq_rank < need);
+    const uint64_t takem = __ballot(take);
+    if (take) out[sel_before + __popcll(takem & lt_mask)] = j;
+    ties_before += __popcll(eqm);
+    sel_before += __popcll(takem);
   }
 }
 
@@ -286,7 +284,8 @@ hipError_t launch_kpl(const Geo& g, const float* qm, const float* km, const floa
                       int32_t* idx, float* scores, hipStream_t s) {
   const int ntile = (g.C + 15) / 16;
   const int ldc = ntile * 16 + 1;  // odd stride spreads a column over the LDS banks
-  const size_t lds = (size_t)(kRows * ldc + 2 * kRows + kRows * (D + 4)) * sizeof(float);
+  const size_t lds = (size_t)(kRows * ldc + 2 * kRows + kRows * (D + 4) +
+                              (kFwdWaves - D / 16) * 64 * 4) * sizeof(float);
   auto* kern = coarse_kernel<TOut, D, KPL>;
   if (lds > 65536) {
     const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -294,7 +293,7 @@ hipError_t launch_kpl(const Geo& g, const float* qm, const float* km, const floa
                                              static_cast<int>(lds));
     if (e != hipSuccess) return e;
   }
-  return launch_kernel(kern, dim3(ntile, g.B * g.H), dim3(64 * kFwdWaves), lds, s, qm, km, vm,
+  return launch_kernel(kern, dim3(ntile, g.B * g.H, 2), dim3(64 * kFwdWaves), lds, s, qm, km, vm,
                        static_cast<TOut*>(oc), idx, scores, g, ldc);
 }
 
