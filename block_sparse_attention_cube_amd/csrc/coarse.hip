@@ -24,6 +24,7 @@
 #include "vsa_internal.h"
 #include "vsa_bwd.h"
 
+#include <algorithm>
 #include <type_traits>
 
 namespace vsa {
@@ -319,26 +320,48 @@ hipError_t launch_typed(const Geo& g, const float* qm, const float* km, const fl
 // Column pass (16 key cubes per workgroup): dKc and dVc, recomputing Pc and
 // dSc column-wise from those statistics.  Both are deterministic.
 
-// out[r][j] = scale * dot(A[r], B[j]) for the 16 rows r of A starting at a0
-// and every j of the 16-aligned column range, into LDS with row stride ldc.
-// Rows and columns past the last cube repeat the last one (finite values that
-// no later step consumes).
+// out1[r][j] = scale1 * dot(A1[r], B1[j]) and out2[r][j] = dot(A2[r], B2[j])
+// for the 16 rows r starting at a0 and every j of the 16-aligned column
+// range, into LDS with row stride ldc.  The 2 x 16 A rows are read from
+// memory once, coalesced, into `stage` (which may overlap out1/out2: every
+// wave takes its operands into registers before any output is written) —
+// a per-wave load would fetch them once per wave.  Rows and columns past
+// the last cube repeat the last one (finite values no later step consumes).
 template <int D>
-__device__ __forceinline__ void rows_dot(const float* __restrict__ A, int a0,
-                                         const float* __restrict__ B, int C, float scale,
-                                         float* out, int ldc, int wave, int lane) {
+__device__ __forceinline__ void rows_dot2(const float* __restrict__ A1,
+                                          const float* __restrict__ A2, int a0,
+                                          const float* __restrict__ B1,
+                                          const float* __restrict__ B2, int C, float scale1,
+                                          float* out1, float* out2, int ldc, float* stage,
+                                          int wave, int lane) {
+  constexpr int kAS = D + 4;   // padded row stride of the staged rows (floats)
   const int li = lane & 15, lg = lane >> 4;
-  float4 af[D / 16];
-  const int r = a0 + li;
+  for (int e = threadIdx.x; e < 2 * kRows * D / 4; e += 64 * kWaves) {
+    const int t = e / (kRows * D / 4), rem = e % (kRows * D / 4);
+    const int r = rem / (D / 4), c4 = rem % (D / 4);
+    const float* A = t ? A2 : A1;
+    const float4 x = *reinterpret_cast<const float4*>(A + (int64_t)min(a0 + r, C - 1) * D + 4 * c4);
+    *reinterpret_cast<float4*>(stage + (t * kRows + r) * kAS + 4 * c4) = x;
+  }
+  __syncthreads();
+  float4 af1[D / 16], af2[D / 16];
 #pragma unroll
-  for (int kk = 0; kk < D / 16; ++kk)
-    af[kk] = *reinterpret_cast<const float4*>(A + (int64_t)min(r, C - 1) * D + 16 * kk + 4 * lg);
+  for (int kk = 0; kk < D / 16; ++kk) {
+    af1[kk] = *reinterpret_cast<const float4*>(stage + li * kAS + 16 * kk + 4 * lg);
+    af2[kk] = *reinterpret_cast<const float4*>(stage + (kRows + li) * kAS + 16 * kk + 4 * lg);
+  }
+  __syncthreads();
   const int ntile = (C + 15) / 16;
   for (int ct = wave; ct < ntile; ct += kWaves) {
     const int col = ct * 16 + li;
-    const f32x4 acc = dot_tile<D>(af, B + (int64_t)min(col, C - 1) * D, lg);
+    const int64_t cc = min(col, C - 1);
+    const f32x4 acc1 = dot_tile<D>(af1, B1 + cc * D, lg);
+    const f32x4 acc2 = dot_tile<D>(af2, B2 + cc * D, lg);
 #pragma unroll
-    for (int rr = 0; rr < 4; ++rr) out[(4 * lg + rr) * ldc + col] = acc[rr] * scale;
+    for (int rr = 0; rr < 4; ++rr) {
+      out1[(4 * lg + rr) * ldc + col] = acc1[rr] * scale1;
+      out2[(4 * lg + rr) * ldc + col] = acc2[rr];
+    }
   }
 }
 
@@ -401,8 +424,8 @@ __global__ __launch_bounds__(64 * kWaves) void coarse_bwd_rows_kernel(
   const int row0 = blockIdx.x * kRows;
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t hoff = bh * C * D;
-  rows_dot<D>(qm + hoff, row0, km + hoff, C, kScale, s1, ldc, wave, lane);
-  rows_dot<D>(docs + hoff, row0, vm + hoff, C, 1.f, s2, ldc, wave, lane);
+  rows_dot2<D>(qm + hoff, docs + hoff, row0, km + hoff, vm + hoff, C, kScale, s1, s2, ldc, lds,
+               wave, lane);
   __syncthreads();
   for (int rr = wave; rr < kRows; rr += kWaves) {
     float* p = s1 + rr * ldc;
@@ -447,8 +470,8 @@ __global__ __launch_bounds__(64 * kWaves) void coarse_bwd_cols_kernel(
   const int col0 = blockIdx.x * kRows;
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t hoff = bh * C * D;
-  rows_dot<D>(km + hoff, col0, qm + hoff, C, kScale, t1, ldc, wave, lane);
-  rows_dot<D>(vm + hoff, col0, docs + hoff, C, 1.f, t2, ldc, wave, lane);
+  rows_dot2<D>(km + hoff, vm + hoff, col0, qm + hoff, docs + hoff, C, kScale, t1, t2, ldc, lds,
+               wave, lane);
   __syncthreads();
   const int64_t plane = (int64_t)g.B * g.H * C;
   const float* sm = stats + bh * C;
@@ -471,7 +494,8 @@ hipError_t launch_coarse_bwd_typed(const Geo& g, const float* qm, const float* k
                                    float* dqc, float* dkc, float* dvc, hipStream_t s) {
   const int ntile = (g.C + 15) / 16;
   const int ldc = ntile * 16 + 1;
-  const size_t lds = (size_t)(2 * kRows * ldc) * sizeof(float);
+  // two 16 x C score tiles, or the 2 x 16 staged operand rows if larger
+  const size_t lds = (size_t)std::max(2 * kRows * ldc, 2 * kRows * (D + 4)) * sizeof(float);
   auto* rows = coarse_bwd_rows_kernel<D>;
   auto* cols = coarse_bwd_cols_kernel<D>;
   if (lds > 65536) {
