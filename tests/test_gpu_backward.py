@@ -24,6 +24,10 @@ EDGE = [
              structure="field", alpha=0.5, backward=True),
     Workload("bwd-one-token", B=1, H=1, T=1, Hh=1, Ww=1, d=128, dtype="bf16", topk=1,
              structure="offset", alpha=0.5, backward=True),
+    # 552 cubes: above the bitmap limit of the block-list transpose (512), so
+    # the round-by-round transpose runs; ragged last cube column
+    Workload("bwd-many-cubes", B=1, H=1, T=4, Hh=96, Ww=90, d=64, dtype="bf16", topk=3,
+             structure="field", alpha=0.5, backward=True),
 ]
 CASES = list(configs.SWEEP) + EDGE
 ids = [w.name for w in CASES]
