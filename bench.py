@@ -8,11 +8,14 @@ cubes (87.5% sparse), synthetic seeded q/k/v.  A step is one vsa_forward call
 (raster q/k/v in HBM -> O_fine, O_coarse, block indices, LSE); inputs rotate
 over 5 independent sets (268 MB) so calls read HBM rather than a warm cache.
 
-Prints one JSON line.  Besides the headline (ms per forward) it reports the
-fine kernel alone (vsa_fine on cube-order inputs), coarse + fine, and the
-in-repo dense flash attention on the same padded sequence (the fine kernel
-with every cube selected), the fine kernel's MFMA roofline, and the fp64 CPU
-oracle timed on the host cores.
+Prints one JSON line.  Besides the headline (ms per forward, with the median
+and 10th/90th percentile of single calls) it reports the fine kernel alone
+(vsa_fine on cube-order inputs), coarse + fine, the in-repo dense flash
+attention on the same padded sequence (the fine kernel with every cube
+selected) and on the 5824 real tokens, valid x valid ("useful") TFLOPS, the
+forward and fine-stage times of every workload of the pages (tiny fp32,
+410M DiT, Wan-1.3B, Wan-14B), the fine kernel's MFMA roofline, and the fp64
+CPU oracle timed on the host cores.
 """
 from __future__ import annotations
 
@@ -73,6 +76,83 @@ def per_launch(fn, launches, warmup, rotate):
         b.record()
     torch.cuda.synchronize()
     return sum(a.elapsed_time(b) for a, b in pairs) / launches
+
+
+def per_call(fn, calls, warmup, rotate):
+    """Median, 10th and 90th percentile (ms) of single calls, each between its own
+    HIP events on the current stream."""
+    import torch
+    for i in range(warmup):
+        fn(i % rotate)
+    pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+             for _ in range(calls)]
+    torch.cuda.synchronize()
+    for i, (a, b) in enumerate(pairs):
+        a.record()
+        fn(i % rotate)
+        b.record()
+    torch.cuda.synchronize()
+    t = sorted(a.elapsed_time(b) for a, b in pairs)
+    pick = lambda f: t[min(len(t) - 1, int(f * len(t)))]
+    return pick(0.5), pick(0.1), pick(0.9)
+
+
+def valid_counts(w):
+    """Valid slots n_c of every cube of a workload's grid, cube order."""
+    ct, ch, cw = -(-w.T // 4), -(-w.Hh // 4), -(-w.Ww // 4)
+    return [min(4, w.T - 4 * t) * min(4, w.Hh - 4 * h) * min(4, w.Ww - 4 * x)
+            for t in range(ct) for h in range(ch) for x in range(cw)]
+
+
+def graph_timed(fn, steps, warmup):
+    """ms per call of fn() captured once into a HIP graph and replayed: device
+    time without the host cost of each binding call, which dominates for the
+    small workloads."""
+    import torch
+    fn()                                   # allocations and library set-up outside the capture
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        fn()
+    return timed(lambda i: graph.replay(), steps, warmup, 1)
+
+
+def per_config(args, dev):
+    """vsa_forward and the fine stage alone (cube-order inputs) for every workload
+    of the pages: one seeded input set each, computed-sparse and useful TFLOPS.
+    Times are HIP-graph replays (device time per call)."""
+    import torch
+    import block_sparse_attention_cube_amd as vsa
+    from block_sparse_attention_cube_amd import flops
+    from synth import configs, inputs
+    out = []
+    for w in (configs.TINY_F32, configs.DIT_410M, configs.WAN_1_3B, configs.WAN_14B):
+        grid = (w.T, w.Hh, w.Ww)
+        dtype = torch.float32 if w.dtype == "f32" else torch.bfloat16
+        host = inputs.make_inputs(w, seed=0)
+        s = {n: inputs.as_torch(host[n], w.dtype, dev) for n in "qkv"}
+        del host
+        big = w.N * w.H > 1_000_000
+        steps, warm = (10, 2) if big else (max(10, args.steps // 2), max(2, args.warmup // 2))
+        plan = vsa.ForwardPlan(w.B, w.H, grid, w.d, w.topk, dtype, dev)
+        f_ms = graph_timed(lambda: plan.run(s["q"], s["k"], s["v"]), steps, warm)
+        cube = {n: vsa.reorder(s[n], grid) for n in "qkv"}
+        _, idx = vsa.coarse(cube["q"], cube["k"], cube["v"], grid, w.topk)
+        obuf = torch.empty_like(cube["q"])
+        fine_ms = graph_timed(lambda: vsa.fine(cube["q"], cube["k"], cube["v"], idx, grid, out=obuf),
+                              steps, warm)
+        fl = flops.fine_forward_flops(w.B, w.H, w.C, w.topk, w.d)
+        useful = flops.useful_fine_flops(w.B, w.H, w.d, valid_counts(w), idx.cpu().numpy())
+        out.append({"workload": w.name, "dtype": w.dtype, "B": w.B, "H": w.H, "grid": list(grid),
+                    "d": w.d, "cubes": w.C, "topk": w.topk,
+                    "forward_ms": round(f_ms, 5), "fine_ms": round(fine_ms, 5),
+                    "fine_sparse_tflops": round(fl / (fine_ms * 1e-3) / 1e12, 2),
+                    "fine_useful_tflops": round(useful / (fine_ms * 1e-3) / 1e12, 2),
+                    "useful_over_computed": round(useful / fl, 4),
+                    "timing": "hip graph replay"})
+        del s, cube, obuf, idx, plan
+        torch.cuda.empty_cache()
+    return out
 
 
 def traffic_record(kernel_source):
@@ -202,6 +282,7 @@ def main():
         stage_only(args, w, grid, sets, cube_sets, step)
         return
     ms = timed(step, args.steps, args.warmup, N_SETS)
+    med_ms, p10_ms, p90_ms = per_call(step, max(20, args.steps // 2), args.warmup, N_SETS)
     warm_ms = timed(lambda i: step(0), args.steps, args.warmup, 1)
 
     # fine kernel alone and coarse + fine on cube-order inputs
@@ -226,6 +307,19 @@ def main():
     dense_step = lambda i: vsa.fine(cube_sets[i]["q"], cube_sets[i]["k"], cube_sets[i]["v"],
                                     all_idx, grid, out=o_buf)
     dense_ms = timed(dense_step, max(10, args.steps // 8), max(2, args.warmup // 4), N_SETS)
+    # dense attention over the 5824 real tokens only: 5824 = 91 x 64, and dense
+    # attention does not depend on token order, so the raster rows read as the
+    # cube order of a 4 x 4 x 364 grid (91 full cubes), every cube selected
+    real_grid = (4, 4, w.N // 16)
+    real_c = w.N // 64
+    real_idx = torch.arange(real_c, dtype=torch.int32, device=dev).expand(
+        w.B, w.H, real_c, real_c).contiguous()
+    o_real = torch.empty_like(sets[0]["q"])
+    dense_real_ms = timed(lambda i: vsa.fine(sets[i]["q"], sets[i]["k"], sets[i]["v"], real_idx,
+                                             real_grid, out=o_real),
+                          max(10, args.steps // 8), max(2, args.warmup // 4), N_SETS)
+    useful = flops.useful_fine_flops(w.B, w.H, w.d, valid_counts(w), idx_sets[0].cpu().numpy())
+    configs_out = per_config(args, dev)
 
     sweep = sparsity_sweep(args, dev)
 
@@ -264,6 +358,12 @@ def main():
         "speedup_coarse_fine_vs_dense": round(dense_ms / cf_ms, 3),
         "speedup_forward_vs_dense": round(dense_ms / ms, 3),
         "dense_tflops": round(fl_dense / (dense_ms * 1e-3) / 1e12, 2),
+        "dense_real_tokens_ms": round(dense_real_ms, 5),
+        "speedup_forward_vs_dense_real_tokens": round(dense_real_ms / ms, 3),
+        "value_median_ms": round(med_ms, 5), "value_p10_ms": round(p10_ms, 5),
+        "value_p90_ms": round(p90_ms, 5),
+        "fine_useful_tflops": round(useful / (fine_ms * 1e-3) / 1e12, 2),
+        "per_config": configs_out,
         "sweep": sweep,
         "fine_launch_ms": round(fine_launch_ms, 5),
         "roofline": {"bound": "mfma", "kernel": "fine_fwd_bf16_kernel<128,false> (vsa_fine)",

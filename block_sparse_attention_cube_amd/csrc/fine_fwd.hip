@@ -443,16 +443,22 @@ __global__ __launch_bounds__(256, 2) void fine_fwd_bf16_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// fp32: 4 threads per query row, thread owns dims qq + 4*i; 32 keys per step.
+// fp32: 4 threads per query row, thread qq owns the contiguous dims
+// qq*D/4 .. qq*D/4 + D/4 - 1; 32 keys per step, read from LDS 16 bytes at a
+// time and four keys per batch so that the reads of a batch overlap.  Row
+// dot products are summed over the row's 4 lanes with DPP quad permutes;
+// exponentials use the hardware v_exp_f32 (about 1 ulp).
 template <int D, bool RASTER>
 __global__ __launch_bounds__(256) void fine_fwd_f32_kernel(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
     const int32_t* __restrict__ idx, float* __restrict__ o, float* __restrict__ lse,
     const float* __restrict__ oc, float* __restrict__ o_coarse, Geo g) {
-  constexpr int kQ = D / 4;
+  constexpr int kQ = D / 4;       // dims per thread
+  constexpr int kQ4 = kQ / 4;     // float4 per thread
   constexpr int kKeys = 32;
-  __shared__ float ks[kKeys * D];
-  __shared__ float vs[kKeys * D];
+  constexpr int kBatch = 4;
+  __shared__ __attribute__((aligned(16))) float ks[kKeys * D];
+  __shared__ __attribute__((aligned(16))) float vs[kKeys * D];
 
   const int tile = xcd_remap(blockIdx.x, gridDim.x);
   const int64_t bh = tile / g.C;
@@ -461,15 +467,22 @@ __global__ __launch_bounds__(256) void fine_fwd_f32_kernel(
   const int K = g.K;
   const int32_t* __restrict__ sel = idx + static_cast<int64_t>(tile) * K;
   const float c2 = inv_sqrt_d<D>() * kLog2e;
+  const int d0 = qq * kQ;
 
-  float qv[kQ], ov[kQ];
-  const float* qrow = q + (bh * g.Np + static_cast<int64_t>(qc) * 64 + row) * D;
+  float4 qv[kQ4], ov[kQ4];
+  const float* qrow = q + (bh * g.Np + static_cast<int64_t>(qc) * 64 + row) * D + d0;
 #pragma unroll
-  for (int i = 0; i < kQ; ++i) {
-    qv[i] = qrow[qq + 4 * i] * c2;
-    ov[i] = 0.f;
+  for (int i = 0; i < kQ4; ++i) {
+    const float4 x = reinterpret_cast<const float4*>(qrow)[i];
+    qv[i] = make_float4(x.x * c2, x.y * c2, x.z * c2, x.w * c2);
+    ov[i] = make_float4(0.f, 0.f, 0.f, 0.f);
   }
   float m = -INFINITY, l = 0.f;
+  auto quad_sum = [](float x) {
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xf, 0xf, false));
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xf, 0xf, false));
+    return x;
+  };
 
   for (int n = 0; n < K; ++n) {
     const int j = sel[n];
@@ -477,36 +490,65 @@ __global__ __launch_bounds__(256) void fine_fwd_f32_kernel(
     for (int half = 0; half < 2; ++half) {
       __syncthreads();
       const int64_t base = (bh * g.Np + static_cast<int64_t>(j) * 64 + half * kKeys) * D;
-      for (int x = tid; x < kKeys * D; x += 256) {
-        ks[x] = k[base + x];
-        vs[x] = v[base + x];
+#pragma unroll
+      for (int x = tid; x < kKeys * D / 4; x += 256) {
+        reinterpret_cast<float4*>(ks)[x] = reinterpret_cast<const float4*>(k + base)[x];
+        reinterpret_cast<float4*>(vs)[x] = reinterpret_cast<const float4*>(v + base)[x];
       }
       __syncthreads();
       float s[kKeys];
       float mloc = -INFINITY;
 #pragma unroll
-      for (int jj = 0; jj < kKeys; ++jj) {
-        float part = 0.f;
+      for (int j0 = 0; j0 < kKeys; j0 += kBatch) {
+        float4 kr[kBatch][kQ4];
 #pragma unroll
-        for (int i = 0; i < kQ; ++i) part = fmaf(qv[i], ks[jj * D + qq + 4 * i], part);
-        part += __shfl_xor(part, 1);
-        part += __shfl_xor(part, 2);
-        const int slot = half * kKeys + jj;
-        const bool valid = (slot >> 4) < e.nt && ((slot >> 2) & 3) < e.nh && (slot & 3) < e.nw;
-        s[jj] = valid ? part : -INFINITY;
-        mloc = fmaxf(mloc, s[jj]);
+        for (int u = 0; u < kBatch; ++u)
+#pragma unroll
+          for (int i = 0; i < kQ4; ++i)
+            kr[u][i] = *reinterpret_cast<const float4*>(ks + (j0 + u) * D + d0 + 4 * i);
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+          float part = 0.f;
+#pragma unroll
+          for (int i = 0; i < kQ4; ++i) {
+            part = fmaf(qv[i].x, kr[u][i].x, part);
+            part = fmaf(qv[i].y, kr[u][i].y, part);
+            part = fmaf(qv[i].z, kr[u][i].z, part);
+            part = fmaf(qv[i].w, kr[u][i].w, part);
+          }
+          part = quad_sum(part);
+          const int slot = half * kKeys + j0 + u;
+          const bool valid = (slot >> 4) < e.nt && ((slot >> 2) & 3) < e.nh && (slot & 3) < e.nw;
+          s[j0 + u] = valid ? part : -INFINITY;
+          mloc = fmaxf(mloc, s[j0 + u]);
+        }
       }
       const float m_new = fmaxf(m, mloc);   // slot 0 of every cube is valid
-      const float alpha = exp2f(m - m_new);
+      const float alpha = __builtin_amdgcn_exp2f(m - m_new);
       l *= alpha;
 #pragma unroll
-      for (int i = 0; i < kQ; ++i) ov[i] *= alpha;
+      for (int i = 0; i < kQ4; ++i)
+        ov[i] = make_float4(ov[i].x * alpha, ov[i].y * alpha, ov[i].z * alpha, ov[i].w * alpha);
 #pragma unroll
-      for (int jj = 0; jj < kKeys; ++jj) {
-        const float pj = exp2f(s[jj] - m_new);
-        l += pj;
+      for (int j0 = 0; j0 < kKeys; j0 += kBatch) {
+        float4 vr[kBatch][kQ4];
 #pragma unroll
-        for (int i = 0; i < kQ; ++i) ov[i] = fmaf(pj, vs[jj * D + qq + 4 * i], ov[i]);
+        for (int u = 0; u < kBatch; ++u)
+#pragma unroll
+          for (int i = 0; i < kQ4; ++i)
+            vr[u][i] = *reinterpret_cast<const float4*>(vs + (j0 + u) * D + d0 + 4 * i);
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+          const float pj = __builtin_amdgcn_exp2f(s[j0 + u] - m_new);
+          l += pj;
+#pragma unroll
+          for (int i = 0; i < kQ4; ++i) {
+            ov[i].x = fmaf(pj, vr[u][i].x, ov[i].x);
+            ov[i].y = fmaf(pj, vr[u][i].y, ov[i].y);
+            ov[i].z = fmaf(pj, vr[u][i].z, ov[i].z);
+            ov[i].w = fmaf(pj, vr[u][i].w, ov[i].w);
+          }
+        }
       }
       m = m_new;
     }
@@ -515,24 +557,26 @@ __global__ __launch_bounds__(256) void fine_fwd_f32_kernel(
   const float inv = 1.f / l;
   if (lse != nullptr && qq == 0)
     lse[bh * g.Np + static_cast<int64_t>(qc) * 64 + row] = (m + log2f(l)) * kLn2;
+  auto put = [&](float* dst) {
+#pragma unroll
+    for (int i = 0; i < kQ4; ++i)
+      reinterpret_cast<float4*>(dst + d0)[i] =
+          make_float4(ov[i].x * inv, ov[i].y * inv, ov[i].z * inv, ov[i].w * inv);
+  };
   if (RASTER) {
     const CubeExt eq = cube_extent(g, qc);
     const int64_t tok = slot_token(g, eq, row);
     if (tok >= 0) {
-      float* orow = o + (bh * g.N + tok) * D;
-#pragma unroll
-      for (int i = 0; i < kQ; ++i) orow[qq + 4 * i] = ov[i] * inv;
+      put(o + (bh * g.N + tok) * D);
       if (oc != nullptr) {
-        const float* crow = oc + (bh * g.C + qc) * D;
-        float* corow = o_coarse + (bh * g.N + tok) * D;
+        const float4* crow = reinterpret_cast<const float4*>(oc + (bh * g.C + qc) * D + d0);
+        float4* corow = reinterpret_cast<float4*>(o_coarse + (bh * g.N + tok) * D + d0);
 #pragma unroll
-        for (int i = 0; i < kQ; ++i) corow[qq + 4 * i] = crow[qq + 4 * i];
+        for (int i = 0; i < kQ4; ++i) corow[i] = crow[i];
       }
     }
   } else {
-    float* orow = o + (bh * g.Np + static_cast<int64_t>(qc) * 64 + row) * D;
-#pragma unroll
-    for (int i = 0; i < kQ; ++i) orow[qq + 4 * i] = ov[i] * inv;
+    put(o + (bh * g.Np + static_cast<int64_t>(qc) * 64 + row) * D);
   }
 }
 
