@@ -74,6 +74,20 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t head_rsrc(const void* base, ui
                                            0x00020000);  // raw 32-bit data format
 }
 
+// LDS byte address of a pointer into shared memory.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const void*)p));
+}
+
+// The DMA loads below are written as inline assembly so that the compiler
+// does not see LDS writes in flight: it would otherwise wait for every
+// outstanding DMA before each transposed LDS read (it cannot tell that those
+// read another ring slot).  Every consumer of a slot waits for its DMA
+// explicitly (s_waitcnt vmcnt(0) + barrier); M0 (the LDS destination) serves
+// no other purpose in these kernels.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"   // M0 is reserved; it is clobbered on purpose
+
 // DMA of one tile whose first row starts at byte row_bytes of the head:
 // thread t moves physical chunks u*256 + t (byte offsets from that row in
 // off[]); lane l lands at +16*l bytes of the wave-uniform LDS destination.
@@ -81,19 +95,29 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t head_rsrc(const void* base, ui
 template <int D>
 __device__ __forceinline__ void dma_rows(const __amdgpu_buffer_rsrc_t& rs, uint32_t row_bytes,
                                          const uint32_t* off, uint16_t* slot, int wave) {
+  const uint32_t lds = lds_addr(slot);
 #pragma unroll
   for (int u = 0; u < BwdTile<D>::kDma; ++u)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        rs, (__attribute__((address_space(3))) void*)(slot + (u * 256 + wave * 64) * 8), 16, off[u],
-        row_bytes, 0, 0);
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                 :: "s"(lds + (u * 256 + wave * 64) * 16), "v"(off[u]), "s"(rs), "s"(row_bytes)
+                 : "memory", "m0");
 }
 // DMA of 64 fp32 per-slot statistics starting at byte `at` of the head (one
 // wave): lane l's value lands at +4*l bytes.
 __device__ __forceinline__ void dma_stats(const __amdgpu_buffer_rsrc_t& rs, uint32_t at, float* slot,
                                           int lane) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)slot, 4,
-                                           static_cast<uint32_t>(lane) * 4u, at, 0, 0);
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, %3 offen lds"
+               :: "s"(lds_addr(slot)), "v"(static_cast<uint32_t>(lane) * 4u), "s"(rs), "s"(at)
+               : "memory", "m0");
 }
+#pragma clang diagnostic pop
+
+// s_waitcnt vmcnt(0) (gfx9 encoding: vmcnt 0, expcnt 7, lgkmcnt 15) as a
+// builtin, which the compiler's own wait insertion understands: registers
+// loaded before it count as complete, so the loop below them carries no wait
+// for them (such a wait would also cover the DMA loads in flight, which the
+// compiler does not count).
+__device__ __forceinline__ void loads_done() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 // Row read: 8 consecutive dims of tile row r (r & 15 as for its 16-row
 // block), starting at logical chunk c.
@@ -449,6 +473,7 @@ __global__ __launch_bounds__(256, 2) void fine_bwd_dq_kernel(BwdFineArgs a, Geo 
     }
   };
   keys(0);
+  loads_done();
   int ext_cur = -1;
   f32x4 bias = {0.f, 0.f, 0.f, 0.f};   // (ih, iw) mask of S^T, first MFMA of each key tile
   float offk[4];                        // exp2 offset of key tile kb: -lse2, or -inf past nt
@@ -627,21 +652,25 @@ __global__ __launch_bounds__(256, 2) void fine_bwd_dkdv_kernel(BwdFineArgs a, Ge
     dvacc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
+  loads_done();
   const int32_t* off_l = a.offsets + bh * (g.C + 1);
   const int beg = off_l[kc], end = off_l[kc + 1];
   const int32_t* lst = a.list + bh * g.C * g.K;
   // extents (nt | nh << 3 | nw << 6) and first raster rows of the listed
   // query cubes, 64 steps per lane vector
   constexpr int kFull = 4 | (4 << 3) | (4 << 6);
-  int ext_lanes = kFull, row_lanes = 0;
+  int ext_lanes = kFull, row_lanes = 0, cube_lanes = 0;
   auto cubes = [&](int first) {   // list positions beg + first ...
     const int m = beg + first + lane;
     ext_lanes = kFull;
     row_lanes = 0;
+    cube_lanes = 0;
     if (m < end) {
-      const CubeExt e = cube_extent(g, lst[m]);
+      const int c = lst[m];
+      const CubeExt e = cube_extent(g, c);
       ext_lanes = e.nt | (e.nh << 3) | (e.nw << 6);
-      row_lanes = cube_row<true>(g, e, lst[m]);
+      row_lanes = cube_row<true>(g, e, c);
+      cube_lanes = c;
     }
   };
   // stage Q, dO (pad slots of an edge cube read its first row) and the
@@ -664,7 +693,7 @@ __global__ __launch_bounds__(256, 2) void fine_bwd_dkdv_kernel(BwdFineArgs a, Ge
       dma_rows<D>(qrs, row_bytes, eoff, dst, wave);
       dma_rows<D>(ors, row_bytes, eoff, dst + kT, wave);
     }
-    const uint32_t at = static_cast<uint32_t>(lst[beg + i]) * (64 * 4);
+    const uint32_t at = static_cast<uint32_t>(__builtin_amdgcn_readlane(cube_lanes, i & 63)) * (64 * 4);
     if (wave == 0) dma_stats(lrs, at, &stat[slot][0][0], lane);
     if (wave == 1) dma_stats(drs, at, &stat[slot][1][0], lane);
   };

@@ -93,17 +93,28 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t head_rsrc(const uint16_t* base
 
 // Issues the DMA loads of one tile: thread t moves physical chunks u*256 + t
 // from byte offset row_bytes + off[u] of the head.  The LDS destination of a
-// load is wave-uniform; lane l lands at +16*l bytes.  The per-lane offsets
-// stay in registers across tiles and only the scalar row offset changes.
+// load is wave-uniform (M0); lane l lands at +16*l bytes.  The per-lane
+// offsets stay in registers across tiles and only the scalar row offset
+// changes.  The loads are written as inline assembly so that the compiler
+// does not see LDS writes in flight: it would otherwise wait for every
+// outstanding DMA before each transposed LDS read (it cannot tell that those
+// read another ring slot).  Every consumer of a slot waits for its DMA
+// explicitly (s_waitcnt vmcnt(0) + barrier); M0 serves no other purpose in
+// these kernels.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"   // M0 is reserved; it is clobbered on purpose
 template <int D>
 __device__ __forceinline__ void dma_tile(const __amdgpu_buffer_rsrc_t& rs, uint32_t row_bytes,
                                          const uint32_t* off, uint16_t* slot, int wave) {
+  const uint32_t lds = static_cast<uint32_t>(
+      reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) uint16_t*)slot));
 #pragma unroll
   for (int u = 0; u < FineTile<D>::kDma; ++u)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        rs, (__attribute__((address_space(3))) void*)(slot + (u * 256 + wave * 64) * 8), 16, off[u],
-        row_bytes, 0, 0);
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                 :: "s"(lds + (u * 256 + wave * 64) * 16), "v"(off[u]), "s"(rs), "s"(row_bytes)
+                 : "memory", "m0");
 }
+#pragma clang diagnostic pop
 
 // Valid extent of a key cube packed as nt | nh << 3 | nw << 6 (each 1..4);
 // a full cube packs to kFullExt.
