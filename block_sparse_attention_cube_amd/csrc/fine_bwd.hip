@@ -167,10 +167,14 @@ __device__ __forceinline__ void write_cube_rows(const uint16_t* stage, uint16_t*
 
 // ---------------------------------------------------------------------------
 // Preparation: per slot D = rowsum(dO * O) and lse * log2(e) (+inf on pad
-// slots), per cube the means of q, k, v and the sum of dO_coarse.  The
+// slots); when the coarse branch has a gradient, per cube also the means of
+// q, k, v and the sum of dO_coarse (the coarse backward's operands).  The
 // gradient kernels gather q, k, v, dO straight from raster rows.
-template <int D>
-__global__ __launch_bounds__(256) void bwd_prep_kernel(BwdPrepArgs a, Geo g) {
+// Eight workgroups per CU: the C x B*H grid fits one round for the shapes
+// of the pages.  Each tensor is summed in its own phase (four loads in
+// flight per thread) so that the accumulators stay within 64 VGPRs.
+template <int D, bool COARSE>
+__global__ __launch_bounds__(256, 8) void bwd_prep_kernel(BwdPrepArgs a, Geo g) {
   constexpr int kCpr = D / 8;                  // 16-byte chunks per row
   constexpr int kRowsPerPass = 256 / kCpr;
   constexpr int kPasses = kSlots / kRowsPerPass;
@@ -178,68 +182,86 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdPrepArgs a, Geo g) {
   const int64_t bh = blockIdx.y;
   const CubeExt e = cube_extent(g, c);
   const int tid = threadIdx.x, chunk = tid % kCpr, row0 = tid / kCpr;
-  const uint16_t* src[4] = {a.q, a.k, a.v, a.dof};
-  float acc[4][8];
-#pragma unroll
-  for (int t = 0; t < 4; ++t)
-#pragma unroll
-    for (int i = 0; i < 8; ++i) acc[t][i] = 0.f;
-
+  int64_t rrow[kPasses];   // raster row of each pass's slot, -1 for a pad slot
 #pragma unroll
   for (int u = 0; u < kPasses; ++u) {
-    const int s = row0 + u * kRowsPerPass;
-    const int64_t r = slot_token(g, e, s);
-    const int64_t crow = bh * g.Np + static_cast<int64_t>(c) * kSlots + s;
-    const int64_t rrow = bh * g.N + r;
-    u32x4 val[4];
-#pragma unroll
-    for (int t = 0; t < 4; ++t)
-      val[t] = (r >= 0) ? *reinterpret_cast<const u32x4*>(src[t] + rrow * D + chunk * 8)
+    const int64_t r = slot_token(g, e, row0 + u * kRowsPerPass);
+    rrow[u] = r >= 0 ? bh * g.N + r : -1;
+  }
+  auto load = [&](const uint16_t* x, int u) {
+    return rrow[u] >= 0 ? *reinterpret_cast<const u32x4*>(x + rrow[u] * D + chunk * 8)
                         : u32x4{0u, 0u, 0u, 0u};
-    const u32x4 ov = (r >= 0) ? *reinterpret_cast<const u32x4*>(a.o + rrow * D + chunk * 8)
-                              : u32x4{0u, 0u, 0u, 0u};
-    const u32x4 cv = (r >= 0 && a.doc != nullptr)
-                         ? *reinterpret_cast<const u32x4*>(a.doc + rrow * D + chunk * 8)
-                         : u32x4{0u, 0u, 0u, 0u};
-    float dot = 0.f;
+  };
+
+  {
+    u32x4 dv[kPasses], ov[kPasses];
 #pragma unroll
-    for (int h = 0; h < 4; ++h) {
-      dot = fmaf(bf16_lo(val[3][h]), bf16_lo(ov[h]), dot);
-      dot = fmaf(bf16_hi(val[3][h]), bf16_hi(ov[h]), dot);
-#pragma unroll
-      for (int t = 0; t < 3; ++t) {
-        acc[t][2 * h] += bf16_lo(val[t][h]);
-        acc[t][2 * h + 1] += bf16_hi(val[t][h]);
-      }
-      acc[3][2 * h] += bf16_lo(cv[h]);
-      acc[3][2 * h + 1] += bf16_hi(cv[h]);
+    for (int u = 0; u < kPasses; ++u) {
+      dv[u] = load(a.dof, u);
+      ov[u] = load(a.o, u);
     }
 #pragma unroll
-    for (int o = kCpr / 2; o >= 1; o >>= 1) dot += __shfl_xor(dot, o);
-    if (chunk == 0) {
-      a.delta[crow] = dot;
-      a.lse2[crow] = r >= 0 ? a.lse[crow] * kLog2e : INFINITY;
+    for (int u = 0; u < kPasses; ++u) {
+      float dot = 0.f;
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        dot = fmaf(bf16_lo(dv[u][h]), bf16_lo(ov[u][h]), dot);
+        dot = fmaf(bf16_hi(dv[u][h]), bf16_hi(ov[u][h]), dot);
+      }
+#pragma unroll
+      for (int o = kCpr / 2; o >= 1; o >>= 1) dot += __shfl_xor(dot, o);
+      if (chunk == 0) {
+        const int64_t crow = bh * g.Np + static_cast<int64_t>(c) * kSlots + row0 + u * kRowsPerPass;
+        a.delta[crow] = dot;
+        a.lse2[crow] = rrow[u] >= 0 ? a.lse[crow] * kLog2e : INFINITY;
+      }
     }
   }
-
-  __shared__ float red[4][kRowsPerPass][D];
+  if constexpr (COARSE) {
+    // Column sums of the cube per tensor: the rows of one wave meet by lane
+    // shuffles (lanes l, l + kCpr, ... hold the same chunk), the four waves
+    // in LDS.
+    const int lane = tid & 63, wave = tid >> 6;
+    __shared__ float red[4][4][D];   // [wave][tensor][dim]
+    const uint16_t* const src[4] = {a.q, a.k, a.v, a.doc};
 #pragma unroll
-  for (int t = 0; t < 4; ++t)
+    for (int t = 0; t < 4; ++t) {
+      u32x4 val[kPasses];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) red[t][row0][chunk * 8 + i] = acc[t][i];
-  __syncthreads();
-  if (tid < D) {
-    const float inv_n = 1.f / static_cast<float>(e.nt * e.nh * e.nw);
-    float sum[4] = {0.f, 0.f, 0.f, 0.f};
+      for (int u = 0; u < kPasses; ++u) val[u] = load(src[t], u);
+      float acc[8];
 #pragma unroll
-    for (int rr = 0; rr < kRowsPerPass; ++rr)
+      for (int i = 0; i < 8; ++i) acc[i] = 0.f;
 #pragma unroll
-      for (int t = 0; t < 4; ++t) sum[t] += red[t][rr][tid];
-    const int64_t m = (bh * g.C + c) * D + tid;
-    a.qm[m] = sum[0] * inv_n;
-    a.km[m] = sum[1] * inv_n;
-    a.vm[m] = sum[2] * inv_n;
-    a.docs[m] = sum[3];
+      for (int u = 0; u < kPasses; ++u)
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+          acc[2 * h] += bf16_lo(val[u][h]);
+          acc[2 * h + 1] += bf16_hi(val[u][h]);
+        }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+#pragma unroll
+        for (int o = kCpr; o < 64; o <<= 1) acc[i] += __shfl_xor(acc[i], o);
+      }
+      if (lane < kCpr) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) red[wave][t][chunk * 8 + i] = acc[i];
+      }
+    }
+    __syncthreads();
+    if (tid < D) {
+      const float inv_n = 1.f / static_cast<float>(e.nt * e.nh * e.nw);
+      float sum[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+        sum[t] = (red[0][t][tid] + red[1][t][tid]) + (red[2][t][tid] + red[3][t][tid]);
+      const int64_t m = (bh * g.C + c) * D + tid;
+      a.qm[m] = sum[0] * inv_n;
+      a.km[m] = sum[1] * inv_n;
+      a.vm[m] = sum[2] * inv_n;
+      a.docs[m] = sum[3];
+    }
   }
 }
 
@@ -797,8 +819,11 @@ __global__ __launch_bounds__(256, 2) void fine_bwd_dkdv_kernel(BwdFineArgs a, Ge
 
 hipError_t launch_bwd_prep(const Geo& g, const BwdPrepArgs& a, hipStream_t s) {
   const dim3 grid(g.C, g.B * g.H), block(256);
-  return g.D == 128 ? launch_kernel(bwd_prep_kernel<128>, grid, block, 0, s, a, g)
-                    : launch_kernel(bwd_prep_kernel<64>, grid, block, 0, s, a, g);
+  if (a.doc != nullptr)
+    return g.D == 128 ? launch_kernel(bwd_prep_kernel<128, true>, grid, block, 0, s, a, g)
+                      : launch_kernel(bwd_prep_kernel<64, true>, grid, block, 0, s, a, g);
+  return g.D == 128 ? launch_kernel(bwd_prep_kernel<128, false>, grid, block, 0, s, a, g)
+                    : launch_kernel(bwd_prep_kernel<64, false>, grid, block, 0, s, a, g);
 }
 
 hipError_t launch_idx_transpose(const Geo& g, const int32_t* idx, int32_t* offsets,
