@@ -22,7 +22,7 @@ What VSA computes, and where the pages state it
 * At 87.5% sparsity attention FLOPs drop 8x (same results section, the
   410M scaling experiment), i.e. sparsity = 1 - K/C over C key blocks.
 
-Readings where the pages are silent (each listed in the design doc):
+Readings where the pages are silent:
 * a 64-token block of a video token grid is a 4x4x4 cube; cubes are taken in
   raster order of the cube grid and slots inside a cube in raster order of
   (t, y, x); each axis is padded at its high end to a multiple of 4, pad

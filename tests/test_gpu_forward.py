@@ -115,7 +115,7 @@ def test_forward_end_to_end(w, cache):
     torch.cuda.synchronize()
     gidx = idx.cpu().numpy()
     near = check_idx(gidx, ref["idx"], ref["scores"], w.topk)
-    # judge the fine stage on the mask the GPU chose (identical unless near ties)
+    # check the fine stage on the mask the GPU chose (identical unless near ties)
     ref_g = ref if near == 0 else vo.forward(x["q"], x["k"], x["v"], w.T, w.Hh, w.Ww, w.topk,
                                              idx=gidx)
     assert_close(host(o_fine), ref_g["o_fine"], w.dtype, "O_fine raster")
