@@ -275,12 +275,13 @@ constexpr int kBitmapCubes = 512;
 constexpr int kBitmapThreads = 1024;
 __global__ __launch_bounds__(kBitmapThreads) void idx_transpose_bitmap_kernel(
     const int32_t* __restrict__ idx, int32_t* __restrict__ offsets, int32_t* __restrict__ list,
-    Geo g) {
+    int32_t* __restrict__ order, Geo g) {
   extern __shared__ uint32_t bmp[];
   constexpr int kNT = kBitmapThreads, kBatch = 4;
   const int C = g.C, K = g.K, W = (C + 31) / 32;
   uint32_t* bits = bmp;                                        // [C][W]
   int32_t* start = reinterpret_cast<int32_t*>(bmp + C * W);    // [C]: counts, then offsets
+  int32_t* cnt = start + C;                                     // [C]: counts
   const int64_t bh = blockIdx.x;
   const int tid = threadIdx.x;
   const int n = C * K;
@@ -303,6 +304,7 @@ __global__ __launch_bounds__(kBitmapThreads) void idx_transpose_bitmap_kernel(
     int c = 0;
     for (int w = 0; w < W; ++w) c += __popc(bits[jj * W + w]);
     start[jj] = c;
+    cnt[jj] = c;
   }
   __syncthreads();
   // exclusive scan of the C <= 512 counts on wave 0: 8 per lane, then the lanes
@@ -334,6 +336,16 @@ __global__ __launch_bounds__(kBitmapThreads) void idx_transpose_bitmap_kernel(
     if (tid == 0) off[C] = n;
   }
   __syncthreads();
+  // key cubes by descending count, ties by index (heaviest dK/dV work first)
+  for (int jj = tid; jj < C; jj += kNT) {
+    const int cj = cnt[jj];
+    int rank = 0;
+    for (int t = 0; t < C; ++t) {
+      const int ct = cnt[t];
+      rank += (ct > cj) | ((ct == cj) & (t < jj));
+    }
+    order[bh * C + rank] = jj;
+  }
   int32_t* out = list + bh * n;
   for (int e0 = tid; e0 < n; e0 += kBatch * kNT) {
     int j[kBatch];
@@ -358,9 +370,11 @@ __global__ __launch_bounds__(kBitmapThreads) void idx_transpose_bitmap_kernel(
 // entry sets its row's bit in a per-key mask (atomicOr, order-free), and its
 // position is the key's cursor plus the number of earlier rows of the step
 // that hold the same key -- deterministic, no ordering by atomics.
+// The dK/dV order of the key cubes stays the identity here.
 __global__ __launch_bounds__(256) void idx_transpose_kernel(const int32_t* __restrict__ idx,
                                                             int32_t* __restrict__ offsets,
-                                                            int32_t* __restrict__ list, Geo g) {
+                                                            int32_t* __restrict__ list,
+                                                            int32_t* __restrict__ order, Geo g) {
   extern __shared__ int32_t shared[];
   int32_t* cursor = shared;                                   // [C] counts, then cursors
   uint32_t* mask = reinterpret_cast<uint32_t*>(shared + g.C);  // [C] rows of this step
@@ -371,6 +385,7 @@ __global__ __launch_bounds__(256) void idx_transpose_kernel(const int32_t* __res
   for (int j = tid; j < C; j += 256) {
     cursor[j] = 0;
     mask[j] = 0u;
+    order[bh * C + j] = j;
   }
   __syncthreads();
   for (int e = tid; e < C * K; e += 256) atomicAdd(&cursor[rows[e]], 1);
@@ -620,9 +635,11 @@ __global__ __launch_bounds__(256, 2) void fine_bwd_dkdv_kernel(BwdFineArgs a, Ge
   __shared__ __attribute__((aligned(16))) uint16_t smem[4 * kT];   // [2 slots][Q | dO]
   __shared__ __attribute__((aligned(16))) float stat[2][2][64];    // [slot][lse2 | delta][q]
 
+  // key cubes in descending order of their selection counts within each
+  // head, so that the longest lists start first and short ones fill the tail
   const int tile = xcd_remap(blockIdx.x, gridDim.x);
   const int64_t bh = tile / g.C;
-  const int kc = tile % g.C;
+  const int kc = __builtin_amdgcn_readfirstlane(a.order[bh * g.C + tile % g.C]);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int li = lane & 15, lg = lane >> 4;
@@ -827,14 +844,15 @@ hipError_t launch_bwd_prep(const Geo& g, const BwdPrepArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_idx_transpose(const Geo& g, const int32_t* idx, int32_t* offsets,
-                                int32_t* list, hipStream_t s) {
+                                int32_t* list, int32_t* order, hipStream_t s) {
   if (g.C <= kBitmapCubes) {
-    const size_t words = static_cast<size_t>(g.C) * ((g.C + 31) / 32) + g.C;
+    const size_t words = static_cast<size_t>(g.C) * ((g.C + 31) / 32) + 2 * g.C;
     return launch_kernel(idx_transpose_bitmap_kernel, dim3(g.B * g.H), dim3(kBitmapThreads),
-                         words * sizeof(uint32_t), s, idx, offsets, list, g);
+                         words * sizeof(uint32_t), s, idx, offsets, list, order, g);
   }
   return launch_kernel(idx_transpose_kernel, dim3(g.B * g.H), dim3(256),
-                       2 * static_cast<size_t>(g.C) * sizeof(int32_t), s, idx, offsets, list, g);
+                       2 * static_cast<size_t>(g.C) * sizeof(int32_t), s, idx, offsets, list,
+                       order, g);
 }
 
 hipError_t launch_bwd_fine(const Geo& g, const BwdFineArgs& a, hipStream_t s) {

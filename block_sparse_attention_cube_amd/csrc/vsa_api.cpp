@@ -90,7 +90,7 @@ struct BwdWs {
   float* qm; float* km; float* vm; float* docs;
   float* stats;
   float* dqc; float* dkc; float* dvc;
-  int32_t* offsets; int32_t* list;
+  int32_t* offsets; int32_t* list; int32_t* order;
 };
 BwdWs carve_backward(const vsa_problem* p, void* ws, size_t* total) {
   const Geo g = geometry(p);
@@ -110,6 +110,7 @@ BwdWs carve_backward(const vsa_problem* p, void* ws, size_t* total) {
   w.dvc = static_cast<float*>(c.take(mean));
   w.offsets = static_cast<int32_t*>(c.take(bh * (g.C + 1) * sizeof(int32_t)));
   w.list = static_cast<int32_t*>(c.take(bh * size_t(g.C) * g.K * sizeof(int32_t)));
+  w.order = static_cast<int32_t*>(c.take(bh * size_t(g.C) * sizeof(int32_t)));
   if (total) *total = c.off;
   return w;
 }
@@ -290,12 +291,12 @@ vsa_status vsa_backward(const vsa_problem* p, const void* q, const void* k, cons
   if (e == hipSuccess && coarse)
     e = vsa::launch_coarse_bwd(g, w.qm, w.km, w.vm, w.docs, w.stats, w.dqc, w.dkc, w.dvc,
                                stream);
-  if (e == hipSuccess) e = vsa::launch_idx_transpose(g, idx, w.offsets, w.list, stream);
+  if (e == hipSuccess) e = vsa::launch_idx_transpose(g, idx, w.offsets, w.list, w.order, stream);
   if (e == hipSuccess) {
     vsa::BwdFineArgs fa;
     fa.q = b16(q); fa.k = b16(k); fa.v = b16(v); fa.dof = b16(do_fine);
     fa.lse2 = w.lse2; fa.delta = w.delta; fa.idx = idx;
-    fa.offsets = w.offsets; fa.list = w.list;
+    fa.offsets = w.offsets; fa.list = w.list; fa.order = w.order;
     fa.dqc = coarse ? w.dqc : nullptr;
     fa.dkc = coarse ? w.dkc : nullptr;
     fa.dvc = coarse ? w.dvc : nullptr;

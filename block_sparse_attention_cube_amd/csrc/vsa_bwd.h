@@ -25,16 +25,18 @@ hipError_t launch_coarse_bwd(const Geo& g, const float* qm, const float* km, con
                              const float* docs, float* stats, float* dqc, float* dkc,
                              float* dvc, hipStream_t s);
 
-// offsets [B,H,C+1], list [B,H,C*K]: query cubes selecting each key cube.
+// offsets [B,H,C+1], list [B,H,C*K]: query cubes selecting each key cube;
+// order [B,H,C]: the key cubes of each head by descending selection count
+// (ties by index), the order the dK/dV workgroups take them in.
 hipError_t launch_idx_transpose(const Geo& g, const int32_t* idx, int32_t* offsets,
-                                int32_t* list, hipStream_t s);
+                                int32_t* list, int32_t* order, hipStream_t s);
 
 struct BwdFineArgs {
   const uint16_t* q; const uint16_t* k; const uint16_t* v; const uint16_t* dof;   // raster
   const float* lse2;     // [B,H,Np] lse * log2(e), +inf on pad slots
   const float* delta;    // [B,H,Np]
   const int32_t* idx;    // [B,H,C,K]
-  const int32_t* offsets; const int32_t* list;
+  const int32_t* offsets; const int32_t* list; const int32_t* order;
   const float* dqc; const float* dkc; const float* dvc;   // coarse gradients or nullptr
   uint16_t* dq; uint16_t* dk; uint16_t* dv;               // raster out
 };
