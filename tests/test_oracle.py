@@ -257,6 +257,24 @@ def test_forward_selection_follows_pooled_scores():
     np.testing.assert_allclose(out["o_coarse"], sdpa(qm, km, vm)[..., ids, :], atol=1e-12)
 
 
+def test_shared_cube_offset_puts_the_own_cube_first():
+    """The tiny fp32 workload adds one N(0,1) offset vector per cube to both q
+    and k (the write-up's per-cube shared offset): the pooled score of a cube
+    with itself is then about |o|^2 = d, far above its scores with other
+    cubes (about N(0, d)), so every row's top-K holds its own cube and its
+    O_coarse leans on its own mean.  A transposed or shifted score matrix in
+    the pooling/top-K chain breaks this."""
+    from synth import configs, inputs
+    w = configs.TINY_F32
+    x = inputs.make_inputs(w, seed=0)
+    out = vo.forward(x["q"], x["k"], x["v"], w.T, w.Hh, w.Ww, w.topk)
+    C = w.C
+    for h in range(w.H):
+        for i in range(C):
+            assert i in out["idx"][0, h, i], (h, i, out["idx"][0, h, i])
+            assert int(np.argmax(out["scores"][0, h, i])) == i
+
+
 # --- backward -----------------------------------------------------------
 
 def _loss(q, k, v, gf, gc, T, Hh, Ww, idx):
