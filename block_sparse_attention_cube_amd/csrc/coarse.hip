@@ -17,8 +17,10 @@
 //      keys of the fp32 scores, each step counting with 64-bit wave ballots
 //      (no shuffles); then one ordered pass with ballots emits every index
 //      above it plus the lowest-index ties, already in ascending order.
-// The split costs one more score computation (cheap) and lets the two phases
-// run on separate CUs instead of competing for one CU's issue slots.
+// The split costs one more score computation and lets the two phases run on
+// separate CUs instead of competing for one CU's issue slots; it pays while
+// the grid leaves CUs idle (small C).  For larger problems one workgroup runs
+// both phases on one copy of the scores (grid z = 1).
 // Everything is fp32 (no bf16 rounding of means or scores), so the selection
 // differs from an exact one only where two scores are within fp32 rounding.
 #include "vsa_internal.h"
@@ -69,6 +71,9 @@ __device__ inline void store_out(float* p, float x) { *p = x; }
 __device__ inline void store_out(uint16_t* p, float x) { *p = f32_to_bf16_rne(x); }
 
 constexpr int kRows = 16;
+// Row tiles up to which the forward splits O_coarse and top-K into separate
+// workgroups: the CU count of an MI355X.
+constexpr int kSplitTiles = 256;
 
 constexpr int kWaves = 8;   // backward kernels: 512 threads
 // Forward kernel: 1024 threads, one statistics / top-K row per wave.
@@ -121,7 +126,9 @@ __global__ __launch_bounds__(64 * kFwdWaves) void coarse_kernel(const float* __r
   const int C = g.C;
   const int64_t bh = blockIdx.y;
   const int row0 = blockIdx.x * kRows;
-  const bool oc_role = blockIdx.z == 0;  // z = 0: statistics and O_coarse; z = 1: top-K
+  // split grid: z = 0 statistics and O_coarse, z = 1 top-K; otherwise both
+  const bool both = gridDim.z == 1;
+  const bool oc_role = blockIdx.z == 0;
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int li = lane & 15, lg = lane >> 4;
   const float* qh = qm + bh * C * D;
@@ -232,7 +239,7 @@ __global__ __launch_bounds__(64 * kFwdWaves) void coarse_kernel(const float* __r
         if (row < C) store_out(oc + (bh * C + row) * D + dt * 16 + li, sum[r]);
       }
     }
-    return;
+    if (!both) return;
   }
 
   // -- 4. top-K, one row per wave.  Counting a predicate over the row is one
@@ -294,8 +301,10 @@ hipError_t launch_kpl(const Geo& g, const float* qm, const float* km, const floa
                                              static_cast<int>(lds));
     if (e != hipSuccess) return e;
   }
-  return launch_kernel(kern, dim3(ntile, g.B * g.H, 2), dim3(64 * kFwdWaves), lds, s, qm, km, vm,
-                       static_cast<TOut*>(oc), idx, scores, g, ldc);
+  // two workgroups per row tile while one per tile leaves CUs idle
+  const int roles = int64_t(ntile) * g.B * g.H <= kSplitTiles ? 2 : 1;
+  return launch_kernel(kern, dim3(ntile, g.B * g.H, roles), dim3(64 * kFwdWaves), lds, s, qm, km,
+                       vm, static_cast<TOut*>(oc), idx, scores, g, ldc);
 }
 
 template <typename TOut, int D>

@@ -134,6 +134,43 @@ def test_forward_is_deterministic(w, cache):
         assert torch.equal(s, t)
 
 
+def _forward_sampled(w):
+    """vsa_forward at full size on the GPU against the oracle on sampled heads
+    (whole coarse stage) and sampled query cubes of each."""
+    x = inputs.make_inputs(w, seed=0)
+    q, k, v = (dev(x[n], w) for n in "qkv")
+    o_fine, o_coarse, idx, lse = vsa.forward(q, k, v, grid(w), w.topk)
+    torch.cuda.synchronize()
+    heads, qcubes = inputs.sample_plan(w)
+    hs = torch.tensor(heads, device=DEV)
+    sub = {n: x[n][:, heads] for n in "qkv"}
+    del x
+    gidx = idx[:, hs].cpu().numpy()
+    ref = vo.forward(sub["q"], sub["k"], sub["v"], w.T, w.Hh, w.Ww, w.topk, qcubes=qcubes,
+                     idx=None)
+    check_idx(gidx, ref["idx"], ref["scores"], w.topk)
+    ref_g = vo.forward(sub["q"], sub["k"], sub["v"], w.T, w.Hh, w.Ww, w.topk, qcubes=qcubes,
+                       idx=gidx)
+    g = ref_g["geometry"]
+    pos = np.concatenate([np.arange(64 * c, 64 * c + 64) for c in qcubes])
+    pos = pos[g["valid"][pos]]
+    toks = g["token"][pos]
+    assert_close(host(o_fine[:, hs])[:, :, toks], ref_g["o_fine"][:, :, toks], w.dtype,
+                 "O_fine sampled")
+    assert_close(host(o_coarse[:, hs]), ref["o_coarse"], w.dtype, "O_coarse sampled heads")
+    assert_close(lse[:, hs].cpu().numpy()[..., pos, None], ref_g["lse_cube"][..., pos, None],
+                 w.dtype, "LSE sampled")
+
+
+def test_forward_one_coarse_workgroup_per_row_tile():
+    """384 row tiles of 16 query cubes (16 per head x 24 heads): above the CU
+    count, so one coarse workgroup per row tile computes O_coarse and the
+    top-K from one copy of the scores (the small shapes split them)."""
+    w = Workload("coarse-fused", B=1, H=24, T=16, Hh=32, Ww=32, d=64, dtype="bf16", topk=24,
+                 structure="field", alpha=0.5)
+    _forward_sampled(w)
+
+
 def test_forward_wan14b_sampled():
     """Wan-14B 720p shape at full size on the GPU; the oracle checks 4 sampled
     heads (full coarse stage) and 16 query cubes of each of them."""
