@@ -560,16 +560,26 @@ __global__ __launch_bounds__(256, 2) void fine_bwd_dq_kernel(BwdFineArgs a, Geo 
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) offk[kb] = kb < nt ? -lse2 : -INFINITY;
     }
-    // S^T and dP^T: lane holds (key = 16kb + 4lg + r, q = li)
+    // S^T first, then dP^T: the exp2 of P runs beside the dP^T MFMAs
     f32x4 sacc[4], pacc[4];
 #pragma unroll
     for (int ks = 0; ks < kKS; ++ks)
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
         const u32x4 kf = *reinterpret_cast<const u32x4*>(k_t + rro[ks] + kb * 16 * D);
-        const u32x4 vf = *reinterpret_cast<const u32x4*>(v_t + rro[ks] + kb * 16 * D);
         sacc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
             as_bf16x8(kf), as_bf16x8(qf[ks]), ks == 0 ? bias : sacc[kb], 0, 0, 0);
+      }
+    float pp[16];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) pp[kb * 4 + r] = __builtin_amdgcn_exp2f(fmaf(sacc[kb][r], c2, offk[kb]));
+#pragma unroll
+    for (int ks = 0; ks < kKS; ++ks)
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        const u32x4 vf = *reinterpret_cast<const u32x4*>(v_t + rro[ks] + kb * 16 * D);
         pacc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
             as_bf16x8(vf), as_bf16x8(df[ks]), ks == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : pacc[kb], 0, 0, 0);
       }
@@ -581,7 +591,7 @@ __global__ __launch_bounds__(256, 2) void fine_bwd_dq_kernel(BwdFineArgs a, Geo 
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const int kb = 2 * s + (i >> 2), r = i & 3;
-        const float p = __builtin_amdgcn_exp2f(fmaf(sacc[kb][r], c2, offk[kb]));
+        const float p = pp[kb * 4 + r];
         ds[i] = p * (pacc[kb][r] - delta);
       }
       dsf[s] = u32x4{pack_bf16x2(ds[0], ds[1]), pack_bf16x2(ds[2], ds[3]),
@@ -754,50 +764,65 @@ __global__ __launch_bounds__(256, 2) void fine_bwd_dkdv_kernel(BwdFineArgs a, Ge
     const uint16_t* q_t = smem + slot * 2 * kT;
     const uint16_t* o_t = q_t + kT;
 
-    // S and dP: lane holds (q = 16qb + 4lg + r, key = 16w + li)
+    // S and dP: lane holds (q = 16qb + 4lg + r, key = 16w + li).  S first:
+    // the exp2 of P runs beside the dP MFMAs, dS beside the dV MFMAs.
     f32x4 sacc[4], pacc[4];
 #pragma unroll
     for (int ks = 0; ks < kKS; ++ks)
 #pragma unroll
       for (int qb = 0; qb < 4; ++qb) {
         const u32x4 qa = *reinterpret_cast<const u32x4*>(q_t + rro[ks] + qb * 16 * D);
-        const u32x4 oa = *reinterpret_cast<const u32x4*>(o_t + rro[ks] + qb * 16 * D);
         sacc[qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
             as_bf16x8(qa), as_bf16x8(kf[ks]), ks == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : sacc[qb], 0, 0, 0);
-        pacc[qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-            as_bf16x8(oa), as_bf16x8(vf[ks]), ks == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : pacc[qb], 0, 0, 0);
       }
     // P^T and dS^T as A operands: k-step s covers q = 32s + 16(i/4) + 4lg + (i%4)
     u32x4 pf[2], dsf[2];
+    float p[16];
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      float p[8], ds[8];
+    for (int qb = 0; qb < 4; ++qb) {
+      const f32x4 l2 = *reinterpret_cast<const f32x4*>(&stat[slot][0][16 * qb + 4 * lg]);
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int qb = 2 * s + h;
-        const f32x4 l2 = *reinterpret_cast<const f32x4*>(&stat[slot][0][16 * qb + 4 * lg]);
-        const f32x4 dl = *reinterpret_cast<const f32x4*>(&stat[slot][1][16 * qb + 4 * lg]);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          p[4 * h + r] = __builtin_amdgcn_exp2f(fmaf(sacc[qb][r], c2, -l2[r]));
-          ds[4 * h + r] = p[4 * h + r] * (pacc[qb][r] - dl[r]);
-        }
-      }
-      pf[s] = u32x4{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
-                    pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7])};
-      dsf[s] = u32x4{pack_bf16x2(ds[0], ds[1]), pack_bf16x2(ds[2], ds[3]),
-                     pack_bf16x2(ds[4], ds[5]), pack_bf16x2(ds[6], ds[7])};
+      for (int r = 0; r < 4; ++r) p[4 * qb + r] = __builtin_amdgcn_exp2f(fmaf(sacc[qb][r], c2, -l2[r]));
     }
-    // dV[key][d] += P^T[key][q] dO[q][d];  dK[key][d] += dS^T[key][q] Q[q][d]
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+      pf[s] = u32x4{pack_bf16x2(p[8 * s + 0], p[8 * s + 1]), pack_bf16x2(p[8 * s + 2], p[8 * s + 3]),
+                    pack_bf16x2(p[8 * s + 4], p[8 * s + 5]), pack_bf16x2(p[8 * s + 6], p[8 * s + 7])};
+#pragma unroll
+    for (int ks = 0; ks < kKS; ++ks)
+#pragma unroll
+      for (int qb = 0; qb < 4; ++qb) {
+        const u32x4 oa = *reinterpret_cast<const u32x4*>(o_t + rro[ks] + qb * 16 * D);
+        pacc[qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            as_bf16x8(oa), as_bf16x8(vf[ks]), ks == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : pacc[qb], 0, 0, 0);
+      }
+    // dV[key][d] += P^T[key][q] dO[q][d]
 #pragma unroll
     for (int s = 0; s < 2; ++s)
 #pragma unroll
-      for (int dt = 0; dt < kDT; ++dt) {
+      for (int dt = 0; dt < kDT; ++dt)
         dvacc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
             as_bf16x8(pf[s]), as_bf16x8(tok_read<D>(o_t, tro[dt], s)), dvacc[dt], 0, 0, 0);
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      float ds[8];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int qb = 2 * s + h;
+        const f32x4 dl = *reinterpret_cast<const f32x4*>(&stat[slot][1][16 * qb + 4 * lg]);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) ds[4 * h + r] = p[4 * qb + r] * (pacc[qb][r] - dl[r]);
+      }
+      dsf[s] = u32x4{pack_bf16x2(ds[0], ds[1]), pack_bf16x2(ds[2], ds[3]),
+                     pack_bf16x2(ds[4], ds[5]), pack_bf16x2(ds[6], ds[7])};
+    }
+    // dK[key][d] += dS^T[key][q] Q[q][d]
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+      for (int dt = 0; dt < kDT; ++dt)
         dkacc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
             as_bf16x8(dsf[s]), as_bf16x8(tok_read<D>(q_t, tro[dt], s)), dkacc[dt], 0, 0, 0);
-      }
   };
   for (int i = 0; beg + i < end; i += 2) {
     step(std::integral_constant<int, 0>{}, i);
