@@ -583,8 +583,9 @@ __global__ __launch_bounds__(256, 2) void fine_bwd_dq_kernel(BwdFineArgs a, Geo 
         pacc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
             as_bf16x8(vf), as_bf16x8(df[ks]), ks == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : pacc[kb], 0, 0, 0);
       }
-    // dS^T as the B operand: k-step s covers keys 32s + 16(i/4) + 4lg + (i%4)
-    u32x4 dsf[2];
+    // dS^T as the B operand: k-step s covers keys 32s + 16(i/4) + 4lg + (i%4);
+    // dQ^T[d][q] += K^T[d][keys] dS^T[keys][q], the second half of dS
+    // formed beside the MFMAs of the first
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       float ds[8];
@@ -594,16 +595,13 @@ __global__ __launch_bounds__(256, 2) void fine_bwd_dq_kernel(BwdFineArgs a, Geo 
         const float p = pp[kb * 4 + r];
         ds[i] = p * (pacc[kb][r] - delta);
       }
-      dsf[s] = u32x4{pack_bf16x2(ds[0], ds[1]), pack_bf16x2(ds[2], ds[3]),
-                     pack_bf16x2(ds[4], ds[5]), pack_bf16x2(ds[6], ds[7])};
-    }
-    // dQ^T[d][q] += K^T[d][keys] dS^T[keys][q]
-#pragma unroll
-    for (int s = 0; s < 2; ++s)
+      const u32x4 dsf = {pack_bf16x2(ds[0], ds[1]), pack_bf16x2(ds[2], ds[3]),
+                         pack_bf16x2(ds[4], ds[5]), pack_bf16x2(ds[6], ds[7])};
 #pragma unroll
       for (int dt = 0; dt < kDT; ++dt)
         dacc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(tok_read<D>(k_t, tro[dt], s)),
-                                                           as_bf16x8(dsf[s]), dacc[dt], 0, 0, 0);
+                                                           as_bf16x8(dsf), dacc[dt], 0, 0, 0);
+    }
   };
   for (int n = 0; n < K; n += 2) {
     step(std::integral_constant<int, 0>{}, n);
@@ -803,6 +801,8 @@ __global__ __launch_bounds__(256, 2) void fine_bwd_dkdv_kernel(BwdFineArgs a, Ge
       for (int dt = 0; dt < kDT; ++dt)
         dvacc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
             as_bf16x8(pf[s]), as_bf16x8(tok_read<D>(o_t, tro[dt], s)), dvacc[dt], 0, 0, 0);
+    // dK[key][d] += dS^T[key][q] Q[q][d], the second half of dS formed beside
+    // the MFMAs of the first
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       float ds[8];
@@ -815,14 +815,11 @@ __global__ __launch_bounds__(256, 2) void fine_bwd_dkdv_kernel(BwdFineArgs a, Ge
       }
       dsf[s] = u32x4{pack_bf16x2(ds[0], ds[1]), pack_bf16x2(ds[2], ds[3]),
                      pack_bf16x2(ds[4], ds[5]), pack_bf16x2(ds[6], ds[7])};
-    }
-    // dK[key][d] += dS^T[key][q] Q[q][d]
-#pragma unroll
-    for (int s = 0; s < 2; ++s)
 #pragma unroll
       for (int dt = 0; dt < kDT; ++dt)
         dkacc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
             as_bf16x8(dsf[s]), as_bf16x8(tok_read<D>(q_t, tro[dt], s)), dkacc[dt], 0, 0, 0);
+    }
   };
   for (int i = 0; beg + i < end; i += 2) {
     step(std::integral_constant<int, 0>{}, i);
