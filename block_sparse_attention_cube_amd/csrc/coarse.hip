@@ -75,7 +75,7 @@ constexpr int kRows = 16;
 // workgroups: the CU count of an MI355X.
 constexpr int kSplitTiles = 256;
 
-constexpr int kWaves = 8;   // backward kernels: 512 threads
+constexpr int kWaves = 16;  // backward kernels: 1024 threads (<= 128 VGPRs)
 // Forward kernel: 1024 threads, one statistics / top-K row per wave.
 constexpr int kFwdWaves = 16;
 
@@ -353,24 +353,23 @@ __device__ __forceinline__ void rows_dot2(const float* __restrict__ A1,
     *reinterpret_cast<float4*>(stage + (t * kRows + r) * kAS + 4 * c4) = x;
   }
   __syncthreads();
-  float4 af1[D / 16], af2[D / 16];
+  // task = (product, column tile): even waves take product 1, odd waves 2
+  const int prod = wave & 1;
+  float4 af[D / 16];
 #pragma unroll
-  for (int kk = 0; kk < D / 16; ++kk) {
-    af1[kk] = *reinterpret_cast<const float4*>(stage + li * kAS + 16 * kk + 4 * lg);
-    af2[kk] = *reinterpret_cast<const float4*>(stage + (kRows + li) * kAS + 16 * kk + 4 * lg);
-  }
+  for (int kk = 0; kk < D / 16; ++kk)
+    af[kk] = *reinterpret_cast<const float4*>(stage + (prod * kRows + li) * kAS + 16 * kk + 4 * lg);
   __syncthreads();
   const int ntile = (C + 15) / 16;
-  for (int ct = wave; ct < ntile; ct += kWaves) {
+  const float* const B = prod ? B2 : B1;
+  float* const out = prod ? out2 : out1;
+  const float scale = prod ? 1.f : scale1;
+  for (int ct = wave >> 1; ct < ntile; ct += kWaves / 2) {
     const int col = ct * 16 + li;
     const int64_t cc = min(col, C - 1);
-    const f32x4 acc1 = dot_tile<D>(af1, B1 + cc * D, lg);
-    const f32x4 acc2 = dot_tile<D>(af2, B2 + cc * D, lg);
+    const f32x4 acc = dot_tile<D>(af, B + cc * D, lg);
 #pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-      out1[(4 * lg + rr) * ldc + col] = acc1[rr] * scale1;
-      out2[(4 * lg + rr) * ldc + col] = acc2[rr];
-    }
+    for (int rr = 0; rr < 4; ++rr) out[(4 * lg + rr) * ldc + col] = acc[rr] * scale;
   }
 }
 
@@ -379,10 +378,10 @@ __device__ __forceinline__ void rows_dot2(const float* __restrict__ A1,
 template <int D>
 __device__ __forceinline__ void lds_times(const float* T, int ldc, const float* __restrict__ Y,
                                           int C, float scale, float* __restrict__ out, int o0,
-                                          int wave, int lane) {
+                                          int wave, int lane, int nwaves) {
   const int li = lane & 15, lg = lane >> 4;
   const float* trow = T + li * ldc;
-  for (int dt = wave; dt < D / 16; dt += kWaves) {
+  for (int dt = wave; dt < D / 16; dt += nwaves) {
     f32x4 acc[4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f},
                     {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
     // each batch of 16 Y loads is issued one batch ahead of its MFMAs
@@ -462,7 +461,7 @@ __global__ __launch_bounds__(64 * kWaves) void coarse_bwd_rows_kernel(
     }
   }
   __syncthreads();
-  lds_times<D>(s2, ldc, km + hoff, C, kScale, dqc + hoff, row0, wave, lane);
+  lds_times<D>(s2, ldc, km + hoff, C, kScale, dqc + hoff, row0, wave, lane, kWaves);
 }
 
 template <int D>
@@ -493,8 +492,10 @@ __global__ __launch_bounds__(64 * kWaves) void coarse_bwd_cols_kernel(
     t2[jj * ldc + i] = p * (t2[jj * ldc + i] - sr[i]);
   }
   __syncthreads();
-  lds_times<D>(t2, ldc, qm + hoff, C, kScale, dkc + hoff, col0, wave, lane);
-  lds_times<D>(t1, ldc, docs + hoff, C, 1.f, dvc + hoff, col0, wave, lane);
+  // dKc on one half of the waves, dVc on the other
+  constexpr int kHalf = kWaves / 2;
+  if (wave < kHalf) lds_times<D>(t2, ldc, qm + hoff, C, kScale, dkc + hoff, col0, wave, lane, kHalf);
+  else lds_times<D>(t1, ldc, docs + hoff, C, 1.f, dvc + hoff, col0, wave - kHalf, lane, kHalf);
 }
 
 template <int D>
