@@ -25,6 +25,7 @@
 // differs from an exact one only where two scores are within fp32 rounding.
 #include "vsa_internal.h"
 #include "vsa_bwd.h"
+#include "block_lists.h"
 
 #include <algorithm>
 #include <type_traits>
@@ -418,12 +419,24 @@ __device__ __forceinline__ void lds_times(const float* T, int ldc, const float* 
   }
 }
 
+// With lists.idx set, the last workgroup column builds the transposed block
+// lists of its head instead (spare workgroups of this small grid).
+struct ListArgs {
+  const int32_t* idx; int32_t* offsets; int32_t* list; int32_t* order;
+};
+static_assert(64 * kWaves == kBitmapThreads, "block-list workgroups have the row kernel's size");
+
 template <int D>
 __global__ __launch_bounds__(64 * kWaves) void coarse_bwd_rows_kernel(
     const float* __restrict__ qm, const float* __restrict__ km, const float* __restrict__ vm,
     const float* __restrict__ docs, float* __restrict__ stats, float* __restrict__ dqc, Geo g,
-    int ldc) {
+    int ldc, ListArgs lists) {
   extern __shared__ float lds[];
+  if (lists.idx != nullptr && blockIdx.x == gridDim.x - 1) {
+    idx_transpose_bitmap(lists.idx, lists.offsets, lists.list, lists.order, g, blockIdx.y,
+                         reinterpret_cast<uint32_t*>(lds));
+    return;
+  }
   float* s1 = lds;                 // scores, then probabilities
   float* s2 = lds + kRows * ldc;   // dPc, then dSc
   constexpr float kScale = (D == 64) ? 0.125f : 0.08838834764831845f;
@@ -501,11 +514,13 @@ __global__ __launch_bounds__(64 * kWaves) void coarse_bwd_cols_kernel(
 template <int D>
 hipError_t launch_coarse_bwd_typed(const Geo& g, const float* qm, const float* km,
                                    const float* vm, const float* docs, float* stats,
-                                   float* dqc, float* dkc, float* dvc, hipStream_t s) {
+                                   float* dqc, float* dkc, float* dvc, const ListArgs& lists,
+                                   hipStream_t s) {
   const int ntile = (g.C + 15) / 16;
   const int ldc = ntile * 16 + 1;
   // two 16 x C score tiles, or the 2 x 16 staged operand rows if larger
-  const size_t lds = (size_t)std::max(2 * kRows * ldc, 2 * kRows * (D + 4)) * sizeof(float);
+  size_t lds = (size_t)std::max(2 * kRows * ldc, 2 * kRows * (D + 4)) * sizeof(float);
+  if (lists.idx != nullptr) lds = std::max(lds, bitmap_words(g.C) * sizeof(uint32_t));
   auto* rows = coarse_bwd_rows_kernel<D>;
   auto* cols = coarse_bwd_cols_kernel<D>;
   if (lds > 65536) {
@@ -517,7 +532,9 @@ hipError_t launch_coarse_bwd_typed(const Geo& g, const float* qm, const float* k
     if (e != hipSuccess) return e;
   }
   const dim3 grid(ntile, g.B * g.H), block(64 * kWaves);
-  hipError_t e = launch_kernel(rows, grid, block, lds, s, qm, km, vm, docs, stats, dqc, g, ldc);
+  const dim3 rows_grid(ntile + (lists.idx != nullptr ? 1 : 0), g.B * g.H);
+  hipError_t e = launch_kernel(rows, rows_grid, block, lds, s, qm, km, vm, docs, stats, dqc, g,
+                               ldc, lists);
   if (e != hipSuccess) return e;
   return launch_kernel(cols, grid, block, lds, s, qm, km, vm, docs,
                        static_cast<const float*>(stats), dkc, dvc, g, ldc);
@@ -541,10 +558,12 @@ namespace vsa {
 
 hipError_t launch_coarse_bwd(const Geo& g, const float* qm, const float* km, const float* vm,
                              const float* docs, float* stats, float* dqc, float* dkc,
-                             float* dvc, hipStream_t s) {
+                             float* dvc, const int32_t* idx, int32_t* offsets, int32_t* list,
+                             int32_t* order, hipStream_t s) {
+  const ListArgs lists = {g.C <= kBitmapCubes ? idx : nullptr, offsets, list, order};
   return g.D == 128
-             ? launch_coarse_bwd_typed<128>(g, qm, km, vm, docs, stats, dqc, dkc, dvc, s)
-             : launch_coarse_bwd_typed<64>(g, qm, km, vm, docs, stats, dqc, dkc, dvc, s);
+             ? launch_coarse_bwd_typed<128>(g, qm, km, vm, docs, stats, dqc, dkc, dvc, lists, s)
+             : launch_coarse_bwd_typed<64>(g, qm, km, vm, docs, stats, dqc, dkc, dvc, lists, s);
 }
 
 }  // namespace vsa

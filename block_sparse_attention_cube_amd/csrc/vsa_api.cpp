@@ -288,10 +288,12 @@ vsa_status vsa_backward(const vsa_problem* p, const void* q, const void* k, cons
   pa.qm = w.qm; pa.km = w.km; pa.vm = w.vm; pa.docs = w.docs;
   hipError_t e = vsa::launch_bwd_prep(g, pa, stream);
   const bool coarse = do_coarse != nullptr;
+  // the coarse backward builds the block lists in spare workgroups when it runs
   if (e == hipSuccess && coarse)
-    e = vsa::launch_coarse_bwd(g, w.qm, w.km, w.vm, w.docs, w.stats, w.dqc, w.dkc, w.dvc,
-                               stream);
-  if (e == hipSuccess) e = vsa::launch_idx_transpose(g, idx, w.offsets, w.list, w.order, stream);
+    e = vsa::launch_coarse_bwd(g, w.qm, w.km, w.vm, w.docs, w.stats, w.dqc, w.dkc, w.dvc, idx,
+                               w.offsets, w.list, w.order, stream);
+  if (e == hipSuccess && !(coarse && vsa::coarse_bwd_builds_lists(g)))
+    e = vsa::launch_idx_transpose(g, idx, w.offsets, w.list, w.order, stream);
   if (e == hipSuccess) {
     vsa::BwdFineArgs fa;
     fa.q = b16(q); fa.k = b16(k); fa.v = b16(v); fa.dof = b16(do_fine);

@@ -21,9 +21,16 @@ hipError_t launch_bwd_prep(const Geo& g, const BwdPrepArgs& a, hipStream_t s);
 
 // Coarse-stage gradients from the means (fp32): dqc/dkc/dvc [B,H,C,D] and row
 // statistics stats [3][B,H,C] (row max, row sum of exp, rowsum(P * dP)).
+// With idx set and C <= 512 it also builds the transposed block lists (as
+// launch_idx_transpose) in spare workgroups of its first kernel.
 hipError_t launch_coarse_bwd(const Geo& g, const float* qm, const float* km, const float* vm,
                              const float* docs, float* stats, float* dqc, float* dkc,
-                             float* dvc, hipStream_t s);
+                             float* dvc, const int32_t* idx, int32_t* offsets, int32_t* list,
+                             int32_t* order, hipStream_t s);
+// Cube counts up to which the block lists come from a bit matrix in LDS (one
+// 1024-thread workgroup per head); launch_coarse_bwd builds them then.
+constexpr int kBitmapCubes = 512;
+inline bool coarse_bwd_builds_lists(const Geo& g) { return g.C <= kBitmapCubes; }
 
 // offsets [B,H,C+1], list [B,H,C*K]: query cubes selecting each key cube;
 // order [B,H,C]: the key cubes of each head by descending selection count
