@@ -4,10 +4,12 @@ The computation lives in libvsa.so (include/vsa.h); this package is its
 PyTorch binding.  Importing it does not load the library; the first call does,
 and fails loudly if the library is missing.
 """
-from .binding import (BackwardPlan, ForwardPlan, VSAFunction, backward, check_problem, coarse, cube_counts,
-                      fine, forward, make_problem, reorder, vsa_attention, workspace_bytes)
+from .binding import (BackwardPlan, ForwardFp8Plan, ForwardPlan, VSAFunction, backward, check_problem,
+                      coarse, cube_counts, fine, fine_fp8, forward, forward_fp8, make_problem,
+                      quantize_fp8, reorder, vsa_attention, workspace_bytes)
 from ._lib import VSAError, LIB_PATH
 
-__all__ = ["BackwardPlan", "ForwardPlan", "VSAFunction", "VSAError", "LIB_PATH", "backward", "check_problem",
-           "coarse", "cube_counts", "fine", "forward", "make_problem", "reorder",
-           "vsa_attention", "workspace_bytes"]
+__all__ = ["BackwardPlan", "ForwardFp8Plan", "ForwardPlan", "VSAFunction", "VSAError", "LIB_PATH",
+           "backward", "check_problem", "coarse", "cube_counts", "fine", "fine_fp8", "forward",
+           "forward_fp8", "make_problem", "quantize_fp8", "reorder", "vsa_attention",
+           "workspace_bytes"]

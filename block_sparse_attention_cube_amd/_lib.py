@@ -25,9 +25,11 @@ VSA_OP_FORWARD = 0
 VSA_OP_BACKWARD = 1
 VSA_OP_COARSE = 2
 VSA_OP_FINE = 3
+VSA_OP_FORWARD_FP8 = 4
 
 EXPORTS = ("vsa_workspace_bytes", "vsa_check_problem", "vsa_reorder", "vsa_coarse",
-           "vsa_fine", "vsa_forward", "vsa_backward", "vsa_status_string")
+           "vsa_fine", "vsa_forward", "vsa_backward", "vsa_quantize_fp8", "vsa_fine_fp8",
+           "vsa_forward_fp8", "vsa_status_string")
 
 
 class VSAProblem(ctypes.Structure):
@@ -57,6 +59,9 @@ _SIG = {
     "vsa_forward": (ctypes.c_int, [_P, _V, _V, _V, _V, _V, _V, _V, _V, ctypes.c_size_t, _V]),
     "vsa_backward": (ctypes.c_int, [_P, _V, _V, _V, _V, _V, _V, _V, _V, _V, _V, _V, _V,
                                     ctypes.c_size_t, _V]),
+    "vsa_quantize_fp8": (ctypes.c_int, [_P, _V, _V, _V, _V, _V, _V, _V, _V]),
+    "vsa_fine_fp8": (ctypes.c_int, [_P, _V, _V, _V, _V, _V, _V, _V, _V]),
+    "vsa_forward_fp8": (ctypes.c_int, [_P, _V, _V, _V, _V, _V, _V, _V, _V, ctypes.c_size_t, _V]),
     "vsa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
 }
 

@@ -248,6 +248,81 @@ def backward(q, k, v, o_fine, lse, idx, do_fine, do_coarse, grid: Grid):
     return dq, dk, dv
 
 
+def quantize_fp8(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, grid: Grid):
+    """E4M3 copies of bf16 raster q, k, v (d = 128) for fine_fp8.
+
+    Returns (q8, k8, vt8, exps): q8, k8 uint8 [B,H,Np,128] cube order, vt8
+    uint8 [B,H,C,128,64] (per-cube transposed V tiles), exps int32 [3,B,H,C].
+    """
+    B, H, N, d = _raster_inputs(q, k, v, grid)
+    C, Np = cube_counts(grid)
+    prob = make_problem(B, H, grid, d, 1, q.dtype)
+    dev = q.device
+    q8 = torch.empty((B, H, Np, d), dtype=torch.uint8, device=dev)
+    k8 = torch.empty_like(q8)
+    vt8 = torch.empty((B, H, C, d, 64), dtype=torch.uint8, device=dev)
+    exps = torch.empty((3, B, H, C), dtype=torch.int32, device=dev)
+    L.check(L.lib().vsa_quantize_fp8(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(q8),
+                                     _ptr(k8), _ptr(vt8), _ptr(exps), _stream(dev)),
+            "vsa_quantize_fp8")
+    return q8, k8, vt8, exps
+
+
+def fine_fp8(q8: torch.Tensor, k8: torch.Tensor, vt8: torch.Tensor, exps: torch.Tensor,
+             idx: torch.Tensor, grid: Grid, return_lse: bool = True,
+             out: Optional[torch.Tensor] = None):
+    """FP8 fine stage: (o_fine bf16 cube order [B,H,Np,128], lse [B,H,Np])."""
+    _device_tensor(q8, "q8")
+    B, H, Np_in, d = q8.shape
+    C, Np = cube_counts(grid)
+    if Np_in != Np:
+        raise ValueError(f"q8 has {Np_in} rows, expected {Np}")
+    _expect(k8, q8.shape, torch.uint8, "k8")
+    _expect(vt8, (B, H, C, d, 64), torch.uint8, "vt8")
+    _expect(exps, (3, B, H, C), torch.int32, "exps")
+    _device_tensor(idx, "idx")
+    if idx.dtype != torch.int32 or idx.dim() != 4 or tuple(idx.shape[:3]) != (B, H, C):
+        raise ValueError(f"idx must be int32 [B,H,C,K], got {idx.dtype} {tuple(idx.shape)}")
+    prob = make_problem(B, H, grid, d, idx.shape[3], torch.bfloat16)
+    dev = q8.device
+    o = out if out is not None else torch.empty((B, H, Np, d), dtype=torch.bfloat16, device=dev)
+    _expect(o, (B, H, Np, d), torch.bfloat16, "out")
+    lse = torch.empty((B, H, Np), dtype=torch.float32, device=dev) if return_lse else None
+    L.check(L.lib().vsa_fine_fp8(ctypes.byref(prob), _ptr(q8), _ptr(k8), _ptr(vt8), _ptr(exps),
+                                 _ptr(idx), _ptr(o), _ptr(lse), _stream(dev)), "vsa_fine_fp8")
+    return o, lse
+
+
+class ForwardFp8Plan(ForwardPlan):
+    """Preallocated outputs and workspace for repeated vsa_forward_fp8 calls."""
+
+    def __init__(self, B: int, H: int, grid: Grid, d: int, topk: int, device,
+                 return_lse: bool = True):
+        super().__init__(B, H, grid, d, topk, torch.bfloat16, device, return_lse)
+        self.ws, self.nws = _workspace(self.prob, L.VSA_OP_FORWARD_FP8, device)
+        if self.ws is None:
+            L.check(L.VSA_ERR_UNSUPPORTED, "vsa_forward_fp8")
+
+    def run(self, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor):
+        for t, n in ((q, "q"), (k, "k"), (v, "v")):
+            _expect(t, self.shape, self.dtype, n)
+        L.check(L.lib().vsa_forward_fp8(ctypes.byref(self.prob), _ptr(q), _ptr(k), _ptr(v),
+                                        _ptr(self.o_fine), _ptr(self.o_coarse), _ptr(self.idx),
+                                        _ptr(self.lse), _ptr(self.ws), self.nws,
+                                        _stream(self.device)), "vsa_forward_fp8")
+        return self.o_fine, self.o_coarse, self.idx, self.lse
+
+
+def forward_fp8(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, grid: Grid, topk: int,
+                return_lse: bool = True):
+    """VSA forward with the FP8 fine stage (bf16 raster in, d = 128)."""
+    B, H, N, d = _raster_inputs(q, k, v, grid)
+    if q.dtype != torch.bfloat16:
+        raise TypeError("forward_fp8 takes bfloat16 q, k, v")
+    plan = ForwardFp8Plan(B, H, grid, d, topk, q.device, return_lse)
+    return plan.run(q, k, v)
+
+
 class VSAFunction(torch.autograd.Function):
     """Trainable VSA: (o_fine, o_coarse) = VSA(q, k, v); the selection is constant."""
 

@@ -21,7 +21,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libvsa.so")
 
-SOURCES = ["vsa_api.cpp", "reorder.hip", "coarse.hip", "fine_fwd.hip", "fine_bwd.hip"]
+SOURCES = ["vsa_api.cpp", "reorder.hip", "coarse.hip", "fine_fwd.hip", "fine_bwd.hip",
+           "quant_fp8.hip", "fine_fp8.hip"]
 ARCH = "gfx950"
 FLAGS = ["-x", "hip", f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
          "-Wall", "-Wno-unused-function",

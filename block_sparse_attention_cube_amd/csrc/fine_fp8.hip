@@ -1,0 +1,423 @@
+// FP8 fine stage: exact softmax attention of each 64-token query cube over
+// its K selected key cubes, with q, k, v held as E4M3 codes with per-cube
+// power-of-two scales (written by quant_fp8.hip).  The format is this
+// library's own; the pages only note that sparse and low-bit attention stack
+// (TurboDiffusion write-up, section "主要技术").
+//
+// One workgroup = 4 waves = one query cube, wave w owns query slots
+// 16w..16w+15.  A step covers TWO selected key cubes (128 keys), the
+// contraction length of gfx950's v_mfma_f32_16x16x128_f8f6f4:
+//   * S^T = K Q^T: one MFMA per 16 keys (d = 128 in a single instruction).
+//     Lane (li, lg) then holds, for query li, keys 16(b%4) + 4lg + j of
+//     cube b/4 in block b, j = 0..3.
+//   * Scores go to exp2 units with the per-cube factor
+//     2^(eq + ek) log2(e) / sqrt(d); the probabilities P = exp2(t - m) are
+//     rounded to E4M3 (v_cvt_pk_fp8_f32) straight into the B operand of
+//     O^T += V^T P^T: byte 4b + j of lane (li, lg) is the key of score block
+//     b, element j.  The V tile is stored transposed with that key order
+//     (byte 16g + 4b + j of row d = key 16b + 4g + j), so the A operand of
+//     lane (d row, lg) is one 16-byte read per cube.
+//   * The V exponent of each cube is applied by the MFMA itself through its
+//     E8M0 operand scales.  The instruction splits the 128-long contraction
+//     into 4 blocks of 32: block beta is bytes 16(beta / 2) .. +15 of lane
+//     groups 2(beta % 2) and 2(beta % 2) + 1, scaled by the scale operand of
+//     lane group beta.  With cube 0 in bytes 0..15 and cube 1 in bytes
+//     16..31 every block belongs to one cube: lane groups 0-1 pass cube 0's
+//     exponent, 2-3 cube 1's.  Row sums come from one unscaled MFMA of P
+//     against ones.
+//   * The running max is raised lazily, as in the bf16 kernel: P <= 2^8,
+//     well inside E4M3's 448.
+//   * K and V^T tiles (8 KB per cube) are staged by buffer_load ... lds DMA
+//     into two-slot rings of cube pairs (64 KB), K one step ahead of V.
+#include <type_traits>
+
+#include "vsa_internal.h"
+
+namespace vsa {
+namespace {
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kD = 128;
+constexpr int kTile = 64 * kD;        // bytes of one cube's K tile or V^T tile
+constexpr int kPair = 2 * kTile;      // one step: two cubes
+constexpr int kDma = kTile / (256 * 16);   // 16-byte DMA loads per thread per tile
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kTau = 8.0f;          // lazy rescale threshold (exp2 units)
+
+static_assert(int64_t(kMaxCubes) * kTile < (int64_t(1) << 32), "32-bit head offsets");
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc8(const uint8_t* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), 0, static_cast<int>(bytes),
+                                           0x00020000);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  const f32x2 f = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2));
+}
+
+__device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
+  const int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  return static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true));
+}
+
+__device__ __forceinline__ f32x4 mfma_fp8(const i32x8& a, const i32x8& b, const f32x4& c) {
+  // format 0 (E4M3) for both operands, no block scales
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
+// DMA of one cube tile: thread t moves physical chunks 256u + t from byte
+// offset cube_bytes + off[u] of the head into `slot`; lane l of a wave lands
+// at +16 l bytes of the wave's M0 base.  Inline assembly so that the compiler
+// does not see the LDS writes (it would otherwise wait for every DMA before
+// each LDS read); every consumer waits explicitly (vmcnt(0) + barrier).
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"   // M0 is reserved; it is clobbered on purpose
+__device__ __forceinline__ void dma_cube(const __amdgpu_buffer_rsrc_t& rs, uint32_t cube_bytes,
+                                         const uint32_t* off, uint8_t* slot, int wave) {
+  const uint32_t lds = static_cast<uint32_t>(
+      reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) uint8_t*)slot));
+#pragma unroll
+  for (int u = 0; u < kDma; ++u)
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                 :: "s"(lds + (u * 256 + wave * 64) * 16), "v"(off[u]), "s"(rs), "s"(cube_bytes)
+                 : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// Masking of pad key slots inside a cube: element j of lane group lg in
+// score block b is key slot (it, ih, iw) = (b % 4, lg, j).  The (ih, iw)
+// part is an accumulator init (0 valid, -inf pad); the it part is a -inf
+// exp2 offset for blocks b % 4 >= nt.
+__device__ __forceinline__ f32x4 hw_bias(int ext, int lg) {
+  const int nh = (ext >> 3) & 7, nw = ext >> 6;
+  const float vl = lg < nh ? 0.f : -INFINITY;
+  return f32x4{nw > 0 ? vl : -INFINITY, nw > 1 ? vl : -INFINITY, nw > 2 ? vl : -INFINITY,
+               nw > 3 ? vl : -INFINITY};
+}
+
+__device__ __forceinline__ float max3f(float a, float b, float c) { return fmaxf(a, fmaxf(b, c)); }
+
+__device__ __forceinline__ float lane_max(const f32x4* t) {
+  float x = -INFINITY;
+#pragma unroll
+  for (int b = 0; b < 8; ++b) x = max3f(x, fmaxf(t[b][0], t[b][1]), fmaxf(t[b][2], t[b][3]));
+  return x;
+}
+
+// Row max over the 4 lanes l, l^16, l^32, l^48 holding the same query.
+__device__ __forceinline__ float row_max(const f32x4* t) {
+  float x = lane_max(t);
+  const uint32_t u = __float_as_uint(x);
+  const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const uint32_t w = __float_as_uint(x);
+  const auto b = __builtin_amdgcn_permlane32_swap(w, w, false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+// Per-step key data, one step per lane: cubes c0 | c1 << 16 and, per cube,
+// ext | (ek + 128) << 9 | (ev + 128) << 17.  A missing second cube (odd K)
+// repeats the first with extent 0: every key of it is masked.
+__device__ __forceinline__ uint32_t cube_info(const Geo& g, int c, const int32_t* ek,
+                                              const int32_t* ev, bool real) {
+  if (!real) return (128u << 9) | (128u << 17);
+  const CubeExt e = cube_extent(g, c);
+  return static_cast<uint32_t>(e.nt | (e.nh << 3) | (e.nw << 6)) |
+         (static_cast<uint32_t>(ek[c] + 128) << 9) | (static_cast<uint32_t>(ev[c] + 128) << 17);
+}
+
+__device__ __forceinline__ void lane_steps(const Geo& g, const int32_t* __restrict__ sel,
+                                           const int32_t* ek, const int32_t* ev, int first,
+                                           int lane, uint32_t& tc, uint32_t& ta, uint32_t& tb) {
+  tc = 0; ta = 0; tb = 0;
+  const int m0 = 2 * (first + lane), m1 = m0 + 1;
+  if (m0 < g.K) {
+    const int c0 = min(max(sel[m0], 0), g.C - 1);
+    const int c1 = m1 < g.K ? min(max(sel[m1], 0), g.C - 1) : c0;
+    tc = static_cast<uint32_t>(c0) | (static_cast<uint32_t>(c1) << 16);
+    ta = cube_info(g, c0, ek, ev, true);
+    tb = cube_info(g, c1, ek, ev, m1 < g.K);
+  }
+}
+
+struct StepKeys {
+  int ext[2];
+  float c2[2];     // score factor 2^(eq + ek) log2(e) / sqrt(d)
+  int vscale;      // E8M0 code of 2^ev of the cube whose PV blocks this lane scales
+};
+
+__device__ __forceinline__ StepKeys step_keys(uint32_t a, uint32_t b, float cq, int lg) {
+  StepKeys s;
+  const uint32_t x[2] = {a, b};
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    s.ext[h] = static_cast<int>(x[h] & 511u);
+    const int ek = static_cast<int>((x[h] >> 9) & 255u) - 128;
+    // the product of two tiny scales may leave the fp32 range: keep it normal
+    s.c2[h] = fmaxf(__builtin_ldexpf(cq, ek), 1.17549435e-38f);
+  }
+  s.vscale = static_cast<int>((lg < 2 ? a : b) >> 17) - 128 + 127;
+  return s;
+}
+
+// S^T blocks of one cube pair: t[b] for keys 16(b%4).. of cube b/4.
+// kro[i]: LDS offset of this lane's i-th 16-byte K chunk in block 0.
+__device__ __forceinline__ void scores(const uint8_t* k_lds, const int* kro, const i32x8& qf,
+                                       const f32x4* bias, f32x4* t) {
+#pragma unroll
+  for (int b = 0; b < 8; ++b) {
+    const uint8_t* base = k_lds + (b >> 2) * kTile + (b & 3) * 16 * kD;
+    const u32x4 lo = *reinterpret_cast<const u32x4*>(base + kro[0]);
+    const u32x4 hi = *reinterpret_cast<const u32x4*>(base + kro[1]);
+    const i32x8 kf = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                      (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+    t[b] = mfma_fp8(kf, qf, bias[b >> 2]);
+  }
+}
+
+// P^T as the B operand: byte 4b + j = exp2(t[b][j]) in E4M3.
+__device__ __forceinline__ i32x8 probabilities(const f32x4* t) {
+  i32x8 pf;
+#pragma unroll
+  for (int b = 0; b < 8; ++b)
+    pf[b] = static_cast<int>(e4m3x4(__builtin_amdgcn_exp2f(t[b][0]), __builtin_amdgcn_exp2f(t[b][1]),
+                                    __builtin_amdgcn_exp2f(t[b][2]), __builtin_amdgcn_exp2f(t[b][3])));
+  return pf;
+}
+
+// O^T[d][q] += 2^ev V^T[d][keys] P^T[keys][q] over the pair (the V
+// exponents as MFMA block scales, E8M0 127 = 1 for P), and the row sums of P
+// (every row of lacc).
+__device__ __forceinline__ void pv(const uint8_t* v_lds, int vro, const i32x8& pf,
+                                   const i32x8& ones, int vscale, f32x4* oacc, f32x4& lacc) {
+  lacc = mfma_fp8(ones, pf, lacc);
+#pragma unroll
+  for (int e = 0; e < kD / 16; ++e) {
+    const u32x4 lo = *reinterpret_cast<const u32x4*>(v_lds + e * 16 * 64 + vro);
+    const u32x4 hi = *reinterpret_cast<const u32x4*>(v_lds + kTile + e * 16 * 64 + vro);
+    const i32x8 vf = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                      (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+    oacc[e] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(vf, pf, oacc[e], 0, 0, 0, vscale,
+                                                               0, 127);
+  }
+}
+
+// RASTER: o (and o_coarse) are raster [B,H,N,D]; otherwise o is cube order.
+template <bool RASTER>
+__global__ __launch_bounds__(256, 2) void fine_fwd_fp8_kernel(
+    const uint8_t* __restrict__ q8, const uint8_t* __restrict__ k8,
+    const uint8_t* __restrict__ vt8, const int32_t* __restrict__ exps,
+    const int32_t* __restrict__ idx, uint16_t* __restrict__ o, float* __restrict__ lse,
+    const uint16_t* __restrict__ oc, uint16_t* __restrict__ o_coarse, Geo g) {
+  constexpr int kKC = kD / 8;               // 16-byte chunks of a bf16 output row
+  constexpr int kOutReg = 64 * kKC / 256;
+  constexpr int kOS = kD + 8;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[4 * kPair];   // K ring (2), V ring (2)
+  uint8_t* const kring = smem;
+  uint8_t* const vring = smem + 2 * kPair;
+
+  const int tile = xcd_remap(blockIdx.x, gridDim.x);
+  const int64_t bh = tile / g.C;
+  const int qc = tile % g.C;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int li = lane & 15, lg = lane >> 4;
+  const int K = g.K;
+  const int ns = (K + 1) >> 1;
+  const int32_t* __restrict__ sel = idx + static_cast<int64_t>(tile) * K;
+  const int64_t nbhc = static_cast<int64_t>(g.B) * g.H * g.C;
+  const int32_t* ek_head = exps + nbhc + bh * g.C;
+  const int32_t* ev_head = exps + 2 * nbhc + bh * g.C;
+  const float cq = __builtin_ldexpf(0.08838834764831845f * kLog2e, exps[bh * g.C + qc]);
+  const int64_t head0 = bh * g.Np * kD;     // byte offset of this head (all three tensors)
+  const uint32_t head_bytes = static_cast<uint32_t>(g.Np * kD);
+  const __amdgpu_buffer_rsrc_t krs = rsrc8(k8 + head0, head_bytes);
+  const __amdgpu_buffer_rsrc_t vrs = rsrc8(vt8 + head0, head_bytes);
+
+  // DMA byte offsets inside a cube tile.  K: row r = P / 8 holds logical
+  // chunk (P % 8) ^ ((r >> 1) & 7); V^T: row d = P / 4 holds logical chunk
+  // (P % 4) ^ ((d >> 2) & 3).  Both put the 16 lanes of one operand read on
+  // distinct bank positions.
+  uint32_t koff[kDma], voff[kDma];
+#pragma unroll
+  for (int u = 0; u < kDma; ++u) {
+    const int P = u * 256 + tid;
+    const int r = P >> 3, d = P >> 2;
+    koff[u] = r * kD + (((P & 7) ^ ((r >> 1) & 7)) * 16);
+    voff[u] = d * 64 + (((P & 3) ^ ((d >> 2) & 3)) * 16);
+  }
+  auto stage = [&](const __amdgpu_buffer_rsrc_t& rs, const uint32_t* off, uint32_t cubes,
+                   uint8_t* slot) {
+    dma_cube(rs, (cubes & 0xffffu) * static_cast<uint32_t>(kTile), off, slot, wave);
+    dma_cube(rs, (cubes >> 16) * static_cast<uint32_t>(kTile), off, slot + kTile, wave);
+  };
+
+  // Q fragment (B operand of S^T): Q8[slot 16w + li][32lg .. 32lg + 31]
+  i32x8 qf;
+  {
+    const uint8_t* qrow = q8 + head0 + (static_cast<int64_t>(qc) * 64 + wave * 16 + li) * kD + 32 * lg;
+    const u32x4 lo = *reinterpret_cast<const u32x4*>(qrow);
+    const u32x4 hi = *reinterpret_cast<const u32x4*>(qrow + 16);
+    qf = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+  }
+  // operand read offsets (loop invariant)
+  int kro[2];
+  kro[0] = li * kD + (((2 * lg) ^ ((li >> 1) & 7)) * 16);
+  kro[1] = li * kD + (((2 * lg + 1) ^ ((li >> 1) & 7)) * 16);
+  const int vro = li * 64 + ((lg ^ ((li >> 2) & 3)) * 16);
+  const int one4 = 0x38383838;   // E4M3 1.0 x 4
+  const i32x8 ones = {one4, one4, one4, one4, one4, one4, one4, one4};
+
+  f32x4 oacc[kD / 16];
+#pragma unroll
+  for (int e = 0; e < kD / 16; ++e) oacc[e] = f32x4{0.f, 0.f, 0.f, 0.f};
+  f32x4 lacc = {0.f, 0.f, 0.f, 0.f};
+
+  uint32_t tab_c, tab_a, tab_b;
+  lane_steps(g, sel, ek_head, ev_head, 0, lane, tab_c, tab_a, tab_b);
+  auto key_c = [&](int n) { return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(tab_c), n & 63)); };
+  auto key_a = [&](int n) { return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(tab_a), n & 63)); };
+  auto key_b = [&](int n) { return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(tab_b), n & 63)); };
+
+  // prologue: K(0), V(0), K(1) in flight together
+  const StepKeys s0 = step_keys(key_a(0), key_b(0), cq, lg);
+  stage(krs, koff, key_c(0), kring);
+  stage(vrs, voff, key_c(0), vring);
+  if (ns > 1) stage(krs, koff, key_c(1), kring + kPair);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  int ext_cur[2] = {s0.ext[0], s0.ext[1]};
+  f32x4 bias[2] = {hw_bias(s0.ext[0], lg), hw_bias(s0.ext[1], lg)};
+  f32x4 tcur[8];
+  scores(kring, kro, qf, bias, tcur);
+#pragma unroll
+  for (int b = 0; b < 8; ++b) {
+    const int h = b >> 2;
+    const float off = (b & 3) < (s0.ext[h] & 7) ? 0.f : -INFINITY;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) tcur[b][j] = fmaf(tcur[b][j], s0.c2[h], off);
+  }
+  float mb = row_max(tcur);
+#pragma unroll
+  for (int b = 0; b < 8; ++b) tcur[b] = tcur[b] - mb;
+  int vscale = s0.vscale;
+
+  auto step = [&](auto p0c, int n) {
+    constexpr int P0 = decltype(p0c)::value, P1 = P0 ^ 1;
+    // K(n+1) and V(n) have landed for every wave; slots of K(n), V(n-1) are free
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    const uint32_t c_next = key_c(n + 1);
+    const StepKeys sn = step_keys(key_a(n + 1), key_b(n + 1), cq, lg);
+    stage(vrs, voff, c_next, vring + P1 * kPair);
+    if (n + 2 < ns) {
+      if (((n + 2) & 63) == 0) lane_steps(g, sel, ek_head, ev_head, n + 2, lane, tab_c, tab_a, tab_b);
+      stage(krs, koff, key_c(n + 2), kring + P0 * kPair);
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+      if ((sn.ext[h] >> 3) != (ext_cur[h] >> 3)) {
+        ext_cur[h] = sn.ext[h];
+        bias[h] = hw_bias(sn.ext[h], lg);
+      }
+    // S(n+1) on the matrix cores while exp2 of step n runs on the VALU
+    f32x4 tnext[8];
+    scores(kring + P1 * kPair, kro, qf, bias, tnext);
+    const i32x8 pf = probabilities(tcur);
+    pv(vring + P0 * kPair, vro, pf, ones, vscale, oacc, lacc);
+    // S(n+1) into exp2 units (relative to the running max)
+#pragma unroll
+    for (int b = 0; b < 8; ++b) {
+      const int h = b >> 2;
+      const float off = (b & 3) < (sn.ext[h] & 7) ? -mb : -INFINITY;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) tnext[b][j] = fmaf(tnext[b][j], sn.c2[h], off);
+    }
+    if (__ballot(lane_max(tnext) > kTau) != 0ull) {
+      const float mt = row_max(tnext);
+      const float delta = mt > kTau ? mt : 0.f;
+      const float alpha = __builtin_amdgcn_exp2f(-delta);
+#pragma unroll
+      for (int e = 0; e < kD / 16; ++e) oacc[e] *= alpha;
+      lacc *= alpha;
+      mb += delta;
+#pragma unroll
+      for (int b = 0; b < 8; ++b) tnext[b] = tnext[b] - delta;
+    }
+#pragma unroll
+    for (int b = 0; b < 8; ++b) tcur[b] = tnext[b];
+    vscale = sn.vscale;
+  };
+  for (int n = 0; n + 1 < ns; n += 2) {
+    step(std::integral_constant<int, 0>{}, n);
+    if (n + 2 >= ns) break;
+    step(std::integral_constant<int, 1>{}, n + 1);
+  }
+  {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    const i32x8 pf = probabilities(tcur);
+    if ((ns - 1) & 1) pv(vring + kPair, vro, pf, ones, vscale, oacc, lacc);
+    else pv(vring, vro, pf, ones, vscale, oacc, lacc);
+  }
+  __syncthreads();   // every wave is done with the rings: reuse them for O
+
+  const float l = lacc[0];   // every row of lacc holds the row sum
+  const float inv = 1.f / l;
+  if (lse != nullptr && lg == 0)
+    lse[bh * g.Np + static_cast<int64_t>(qc) * 64 + wave * 16 + li] = (mb + log2f(l)) * kLn2;
+
+  uint16_t* const o_lds = reinterpret_cast<uint16_t*>(smem);  // [64][kOS]
+#pragma unroll
+  for (int e = 0; e < kD / 16; ++e) {
+    // lane holds O[q = 16w + li][d = 16e + 4lg + j], j = 0..3
+    const u32x2 w = {pack_bf16x2(oacc[e][0] * inv, oacc[e][1] * inv),
+                     pack_bf16x2(oacc[e][2] * inv, oacc[e][3] * inv)};
+    *reinterpret_cast<u32x2*>(o_lds + (wave * 16 + li) * kOS + 16 * e + 4 * lg) = w;
+  }
+  __syncthreads();
+  const CubeExt eq = cube_extent(g, qc);
+#pragma unroll
+  for (int u = 0; u < kOutReg; ++u) {
+    const int ch = tid + 256 * u, row = ch / kKC, c = ch % kKC;
+    const u32x4 val = *reinterpret_cast<const u32x4*>(o_lds + row * kOS + 8 * c);
+    if (RASTER) {
+      const int64_t tok = slot_token(g, eq, row);
+      if (tok >= 0) {
+        *reinterpret_cast<u32x4*>(o + (bh * g.N + tok) * kD + 8 * c) = val;
+        if (oc != nullptr)
+          *reinterpret_cast<u32x4*>(o_coarse + (bh * g.N + tok) * kD + 8 * c) =
+              *reinterpret_cast<const u32x4*>(oc + (bh * g.C + qc) * kD + 8 * c);
+      }
+    } else {
+      *reinterpret_cast<u32x4*>(o + (bh * g.Np + static_cast<int64_t>(qc) * 64 + row) * kD + 8 * c) = val;
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_fine_fp8(const Geo& g, const void* q8, const void* k8, const void* vt8,
+                           const int32_t* exps, const int32_t* idx, void* o, float* lse,
+                           bool raster_out, const void* oc, void* o_coarse, hipStream_t s) {
+  if (g.D != kD) return hipErrorInvalidValue;
+  const dim3 grid(g.B * g.H * g.C), block(256);
+  auto u8 = [](const void* p) { return static_cast<const uint8_t*>(p); };
+  if (raster_out)
+    return launch_kernel(fine_fwd_fp8_kernel<true>, grid, block, 0, s, u8(q8), u8(k8), u8(vt8),
+                         exps, idx, static_cast<uint16_t*>(o), lse,
+                         static_cast<const uint16_t*>(oc), static_cast<uint16_t*>(o_coarse), g);
+  return launch_kernel(fine_fwd_fp8_kernel<false>, grid, block, 0, s, u8(q8), u8(k8), u8(vt8), exps,
+                       idx, static_cast<uint16_t*>(o), lse, static_cast<const uint16_t*>(oc),
+                       static_cast<uint16_t*>(o_coarse), g);
+}
+
+}  // namespace vsa

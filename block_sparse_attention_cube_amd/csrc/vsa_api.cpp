@@ -137,6 +137,36 @@ CoarseWs carve_coarse(const vsa_problem* p, void* ws, size_t* total) {
   return w;
 }
 
+// FP8 path: bf16 inputs with d = 128 only.
+vsa_status check_fp8(const vsa_problem* p) {
+  const vsa_status st = check(p);
+  if (st != VSA_OK) return st;
+  if (p->dtype != VSA_BF16 || p->d != 128) return VSA_ERR_UNSUPPORTED;
+  return VSA_OK;
+}
+
+struct Fp8Ws {
+  void* q8; void* k8; void* vt8; int32_t* exps;
+  float* qm; float* km; float* vm;
+  void* oc;
+};
+Fp8Ws carve_forward_fp8(const vsa_problem* p, void* ws, size_t* total) {
+  const Geo g = geometry(p);
+  const size_t bhc = size_t(g.B) * g.H * g.C;
+  const size_t codes = bhc * 64 * g.D;   // one byte per element
+  const size_t mean = bhc * g.D * sizeof(float);
+  Carver c(ws);
+  Fp8Ws w;
+  w.q8 = c.take(codes); w.k8 = c.take(codes); w.vt8 = c.take(codes);
+  w.exps = static_cast<int32_t*>(c.take(3 * bhc * sizeof(int32_t)));
+  w.qm = static_cast<float*>(c.take(mean));
+  w.km = static_cast<float*>(c.take(mean));
+  w.vm = static_cast<float*>(c.take(mean));
+  w.oc = c.take(bhc * g.D * 2);
+  if (total) *total = c.off;
+  return w;
+}
+
 bool misaligned(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) != 0; }
 
 vsa_status pointers(std::initializer_list<const void*> required,
@@ -174,6 +204,10 @@ size_t vsa_workspace_bytes(const vsa_problem* p, int op) {
     case VSA_OP_FORWARD: carve_forward(p, nullptr, &total); return total;
     case VSA_OP_COARSE: carve_coarse(p, nullptr, &total); return total;
     case VSA_OP_FINE: return 0;
+    case VSA_OP_FORWARD_FP8:
+      if (check_fp8(p) != VSA_OK) return 0;
+      carve_forward_fp8(p, nullptr, &total);
+      return total;
     case VSA_OP_BACKWARD:
       if (check_backward(p) != VSA_OK) return 0;
       carve_backward(p, nullptr, &total);
@@ -307,6 +341,51 @@ vsa_status vsa_backward(const vsa_problem* p, const void* q, const void* k, cons
     fa.dv = static_cast<uint16_t*>(dv);
     e = vsa::launch_bwd_fine(g, fa, stream);
   }
+  return launched(e);
+}
+
+vsa_status vsa_quantize_fp8(const vsa_problem* p, const void* q, const void* k, const void* v,
+                            void* q8, void* k8, void* vt8, int32_t* exps, hipStream_t stream) {
+  vsa_status st = check_fp8(p);
+  if (st != VSA_OK) return st;
+  if ((st = pointers({q, k, v, q8, k8, vt8, exps}, {})) != VSA_OK) return st;
+  vsa::Fp8Batch b = {};
+  b.x[0] = q; b.x[1] = k; b.x[2] = v;
+  b.y[0] = q8; b.y[1] = k8; b.y[2] = vt8;
+  b.exps = exps;
+  return launched(vsa::launch_quant_fp8(geometry(p), b, stream));
+}
+
+vsa_status vsa_fine_fp8(const vsa_problem* p, const void* q8, const void* k8, const void* vt8,
+                        const int32_t* exps, const int32_t* idx, void* o_fine, float* lse,
+                        hipStream_t stream) {
+  vsa_status st = check_fp8(p);
+  if (st != VSA_OK) return st;
+  if ((st = pointers({q8, k8, vt8, exps, idx, o_fine}, {lse})) != VSA_OK) return st;
+  return launched(vsa::launch_fine_fp8(geometry(p), q8, k8, vt8, exps, idx, o_fine, lse,
+                                       /*raster=*/false, nullptr, nullptr, stream));
+}
+
+vsa_status vsa_forward_fp8(const vsa_problem* p, const void* q, const void* k, const void* v,
+                           void* o_fine, void* o_coarse, int32_t* idx, float* lse, void* ws,
+                           size_t ws_bytes, hipStream_t stream) {
+  vsa_status st = check_fp8(p);
+  if (st != VSA_OK) return st;
+  if ((st = pointers({q, k, v, o_fine, o_coarse, idx}, {lse})) != VSA_OK) return st;
+  if ((st = workspace(p, VSA_OP_FORWARD_FP8, ws, ws_bytes)) != VSA_OK) return st;
+  const Geo g = geometry(p);
+  const Fp8Ws w = carve_forward_fp8(p, ws, nullptr);
+  vsa::Fp8Batch b = {};
+  b.x[0] = q; b.x[1] = k; b.x[2] = v;
+  b.y[0] = w.q8; b.y[1] = w.k8; b.y[2] = w.vt8;
+  b.mean[0] = w.qm; b.mean[1] = w.km; b.mean[2] = w.vm;
+  b.exps = w.exps;
+  hipError_t e = vsa::launch_quant_fp8(g, b, stream);
+  if (e == hipSuccess)
+    e = vsa::launch_coarse(g, p->dtype, w.qm, w.km, w.vm, w.oc, idx, nullptr, stream);
+  if (e == hipSuccess)
+    e = vsa::launch_fine_fp8(g, w.q8, w.k8, w.vt8, w.exps, idx, o_fine, lse, /*raster=*/true,
+                             w.oc, o_coarse, stream);
   return launched(e);
 }
 

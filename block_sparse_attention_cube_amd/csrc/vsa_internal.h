@@ -133,4 +133,22 @@ hipError_t launch_fine(const Geo& g, int dtype, const void* q, const void* k, co
                        const int32_t* idx, void* o, float* lse, bool raster,
                        const void* oc, void* o_coarse, hipStream_t s);
 
+// FP8 (E4M3) copies of bf16 raster q, k, v (D = 128): x[i] raster in,
+// y[0], y[1] cube order [B,H,Np,D] bytes (q, k), y[2] per-cube transposed
+// V tiles [B,H,C,D,64] bytes, exps int32 [3][B*H*C] (per-cube exponents of
+// q, k, v), mean[i] optional fp32 per-cube means [B,H,C,D].
+struct Fp8Batch {
+  const void* x[3];
+  void* y[3];
+  float* mean[3];
+  int32_t* exps;
+};
+hipError_t launch_quant_fp8(const Geo& g, const Fp8Batch& b, hipStream_t s);
+
+// FP8 fine stage on the copies above (D = 128); o bf16 in cube order, or
+// raster (+ O_coarse broadcast from oc when non-null) for raster = true.
+hipError_t launch_fine_fp8(const Geo& g, const void* q8, const void* k8, const void* vt8,
+                           const int32_t* exps, const int32_t* idx, void* o, float* lse,
+                           bool raster, const void* oc, void* o_coarse, hipStream_t s);
+
 }  // namespace vsa

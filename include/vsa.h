@@ -81,11 +81,13 @@ typedef struct {
   int32_t dtype;             /* vsa_dtype of q, k, v and of every output tensor  */
 } vsa_problem;
 
-enum { VSA_OP_FORWARD = 0, VSA_OP_BACKWARD = 1, VSA_OP_COARSE = 2, VSA_OP_FINE = 3 };
+enum { VSA_OP_FORWARD = 0, VSA_OP_BACKWARD = 1, VSA_OP_COARSE = 2, VSA_OP_FINE = 3,
+       VSA_OP_FORWARD_FP8 = 4 };
 
 /* Bytes of device workspace the entry point `op` needs for problem `p`
  * (VSA_OP_FORWARD: vsa_forward, VSA_OP_BACKWARD: vsa_backward,
- * VSA_OP_COARSE: vsa_coarse, VSA_OP_FINE: vsa_fine).  Returns 0 if `p` is
+ * VSA_OP_COARSE: vsa_coarse, VSA_OP_FINE: vsa_fine,
+ * VSA_OP_FORWARD_FP8: vsa_forward_fp8).  Returns 0 if `p` is
  * invalid (see vsa_check_problem) or `op` unknown; a valid problem may also
  * need 0 bytes (then ws may be NULL).  Host-only, never touches the GPU. */
 size_t vsa_workspace_bytes(const vsa_problem* p, int op);
@@ -173,6 +175,48 @@ vsa_status vsa_backward(const vsa_problem* p, const void* q, const void* k, cons
                         const void* do_fine, const void* do_coarse,
                         void* dq, void* dk, void* dv,
                         void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* ---- FP8 fine stage ----------------------------------------------------
+ * The pages note that sparse attention and low-bit attention are orthogonal
+ * and stack (TurboDiffusion write-up on qq8o.cn, section "主要技术"); they
+ * give no FP8 scheme for VSA.  The one below is this library's own, for
+ * inference with bf16 q, k, v and d = 128 (other problems return
+ * VSA_ERR_UNSUPPORTED).
+ *   Codes: OCP E4M3 (bias 7, largest finite 448), round to nearest even.
+ *   Scales: every (batch, head, cube) of each of q, k, v has an exponent e,
+ *     the smallest integer with amax <= 448 * 2^e (amax = largest |x| over
+ *     the cube's valid slots), floored at -120; the code stores x * 2^-e.
+ *   Fine stage: S from the codes times 2^(eq + ek) / sqrt(d) (fp32),
+ *     P = exp(S - running max) rounded to E4M3, O = sum P 2^ev V_code / sum P
+ *     with fp32 accumulation; the only rounding beyond the input codes is
+ *     that of P (3 mantissa bits). */
+
+/* Quantizes bf16 raster q, k, v [B,H,N,128] into the FP8 layout:
+ *   q8, k8 : [B,H,Np,128] bytes, cube order, pad slots 0.
+ *   vt8    : [B,H,C,128,64] bytes: per cube the transposed V tile; byte
+ *            16g + 4b + j of row dd holds key slot 16b + 4g + j of the cube
+ *            (g, b, j in 0..3), the operand order of the fine kernel.
+ *   exps   : int32 [3][B,H,C], the exponents e of q, k and v.
+ * Bit-exact (integer exponent logic and round-to-nearest-even codes). */
+vsa_status vsa_quantize_fp8(const vsa_problem* p, const void* q, const void* k, const void* v,
+                            void* q8, void* k8, void* vt8, int32_t* exps, hipStream_t stream);
+
+/* Fine stage on the FP8 layout of vsa_quantize_fp8 (the fine block-sparse
+ * kernel of the FastWan re-post's results section, on E4M3 operands).
+ *   idx    : [B,H,C,topk] int32, each in [0, C), distinct per row.
+ *   o_fine : [B,H,Np,128] bf16 out, cube order (pad rows unspecified).
+ *   lse    : [B,H,Np] fp32 out (natural log), or NULL. */
+vsa_status vsa_fine_fp8(const vsa_problem* p, const void* q8, const void* k8, const void* vt8,
+                        const int32_t* exps, const int32_t* idx, void* o_fine, float* lse,
+                        hipStream_t stream);
+
+/* Whole forward with the FP8 fine stage: one pass quantizes q, k, v and
+ * pools the fp32 cube means, the coarse stage and the selection are those of
+ * vsa_forward (fp32, exact top-K), and the fine stage runs on E4M3.
+ * Arguments as vsa_forward; ws of vsa_workspace_bytes(p, VSA_OP_FORWARD_FP8). */
+vsa_status vsa_forward_fp8(const vsa_problem* p, const void* q, const void* k, const void* v,
+                           void* o_fine, void* o_coarse, int32_t* idx, float* lse,
+                           void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* Static string naming a status. */
 const char* vsa_status_string(vsa_status s);

@@ -256,3 +256,106 @@ def backward(q, k, v, do_fine, do_coarse, T: int, Hh: int, Ww: int, idx: np.ndar
     dk += per_slot(dkc)
     dv += per_slot(dvc)
     return inverse_reorder(dq, g), inverse_reorder(dk, g), inverse_reorder(dv, g)
+
+
+# ----------------------------------------------------------------------------
+# FP8 fine stage (a design of this library, not of the pages)
+# ----------------------------------------------------------------------------
+# The TurboDiffusion write-up (qq8o.cn, section "方法", "主要技术") notes that
+# sparse attention and low-bit attention are orthogonal and stack.  The pages
+# give no FP8 scheme for VSA; the one modelled here is this library's own:
+#   * q, k, v are stored in cube order as OCP E4M3 codes (1 sign bit,
+#     4 exponent bits with bias 7, 3 mantissa bits; largest finite 448,
+#     subnormal step 2^-9), rounded to nearest, ties to even;
+#   * every (batch, head, cube) of each tensor carries its own power-of-two
+#     scale 2^e: the smallest e with amax <= 448 * 2^e, where amax is the
+#     largest |x| over the cube's valid slots, and never below 2^-120;
+#   * the fine stage is exact softmax attention over the dequantized values
+#     (code * 2^e).  The kernel additionally rounds its probabilities to E4M3;
+#     that rounding is not modelled here (it depends on the kernel's running
+#     maximum) and is covered by a tolerance instead.
+
+E4M3_MAX = 448.0
+E4M3_MIN_EXP = -120
+
+
+def e4m3_round(x: np.ndarray) -> np.ndarray:
+    """Round float64 values to the nearest E4M3 value, ties to even.
+
+    Normal values (|x| >= 2^-6) keep 3 mantissa bits, i.e. a quantum of
+    2^(E-3) for |x| in [2^E, 2^(E+1)); below 2^-6 the quantum is the subnormal
+    step 2^-9.  Values that would round beyond 448 are an error: the scales
+    above keep every scaled value within range.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    _, p = np.frexp(x)                 # |x| = m 2^p, m in [0.5, 1)
+    expo = np.maximum(p - 1, -6)       # E, floored at the smallest normal exponent
+    quantum = np.ldexp(1.0, expo - 3)
+    y = np.round(x / quantum) * quantum   # np.round rounds halves to even
+    if np.any(np.abs(y) > E4M3_MAX):
+        raise ValueError("value outside the E4M3 range")
+    return y
+
+
+def e4m3_encode(y: np.ndarray) -> np.ndarray:
+    """Bit pattern (uint8) of values that are already E4M3 values."""
+    y = np.asarray(y, dtype=np.float64)
+    sign = (np.signbit(y)).astype(np.uint8) << 7
+    a = np.abs(y)
+    _, p = np.frexp(a)
+    e = p - 1                                          # a in [2^e, 2^(e+1))
+    normal = a >= 2.0 ** -6
+    exp_field = np.where(normal, e + 7, 0)
+    mant = np.where(normal, a / np.ldexp(1.0, e) - 1.0, a / 2.0 ** -9 / 8.0) * 8.0
+    mant = np.where(a == 0, 0, mant)
+    exp_field = np.where(a == 0, 0, exp_field)
+    code = (exp_field.astype(np.int64) << 3) | np.rint(mant).astype(np.int64)
+    return sign | code.astype(np.uint8)
+
+
+def e4m3_decode(code: np.ndarray) -> np.ndarray:
+    """Value of E4M3 bit patterns (the all-ones exponent/mantissa pattern is NaN)."""
+    c = np.asarray(code, dtype=np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    ef, mf = (c >> 3) & 15, c & 7
+    mag = np.where(ef == 0, mf * 2.0 ** -9, np.ldexp(1.0 + mf / 8.0, ef - 7))
+    mag = np.where((ef == 15) & (mf == 7), np.nan, mag)
+    return sign * mag
+
+
+def fp8_scale_exponent(amax: np.ndarray) -> np.ndarray:
+    """Smallest integer e with amax <= 448 * 2^e, floored at -120."""
+    a = np.asarray(amax, dtype=np.float64)
+    m, p = np.frexp(a)                  # a = m 2^p; 448 = 1.75 * 2^8
+    f, big_e = 2.0 * m, p - 1          # a = f 2^E, f in [1, 2)
+    e = np.where(f <= 1.75, big_e - 8, big_e - 7)
+    e = np.where(a == 0, E4M3_MIN_EXP, e)
+    return np.maximum(e, E4M3_MIN_EXP).astype(np.int64)
+
+
+def quantize_cubes_fp8(xc: np.ndarray, g):
+    """Per-cube E4M3 quantization of a cube-order tensor (..., Np, d).
+
+    Returns (codes uint8 (..., Np, d), exponents int64 (..., C), dequantized
+    float64 (..., Np, d)).  Pad slots are zero in all three.
+    """
+    xc = np.asarray(xc, dtype=np.float64)
+    lead, Np, d = xc.shape[:-2], xc.shape[-2], xc.shape[-1]
+    cubes = xc.reshape(*lead, Np // SLOTS, SLOTS, d)
+    valid = g["valid"].reshape(Np // SLOTS, SLOTS)[..., None]
+    amax = np.abs(np.where(valid, cubes, 0.0)).max(axis=(-2, -1))
+    e = fp8_scale_exponent(amax)
+    scale = np.ldexp(1.0, e)[..., None, None]
+    y = e4m3_round(np.where(valid, cubes, 0.0) / scale)
+    deq = (y * scale).reshape(xc.shape)
+    return e4m3_encode(y).reshape(xc.shape), e, deq
+
+
+def fine_fp8(qc: np.ndarray, kc: np.ndarray, vc: np.ndarray, idx: np.ndarray, g,
+             qcubes: Optional[Iterable[int]] = None):
+    """Fine stage on E4M3-quantized q, k, v (cube order): exact attention over
+    the dequantized values.  Returns o, lse and the per-tensor
+    (codes, exponents) of the quantization."""
+    quant = [quantize_cubes_fp8(x, g) for x in (qc, kc, vc)]
+    o, lse = fine(quant[0][2], quant[1][2], quant[2][2], idx, g, qcubes)
+    return o, lse, [(c, e) for c, e, _ in quant]

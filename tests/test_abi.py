@@ -22,7 +22,7 @@ MISALIGNED = ctypes.c_void_p(0x1008)
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(vsa_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(vsa_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_header_and_library_agree():
@@ -124,3 +124,28 @@ def test_status_strings():
     for s in range(7):
         assert L.status_string(s).startswith("VSA_")
     assert "unknown" in L.status_string(42)
+
+
+def test_fp8_entry_points_validate_before_launching():
+    lib = L.lib()
+    p = prob()
+    # FP8: bf16 and d = 128 only
+    for bad in (prob(dtype=L.VSA_F32), prob(d=64)):
+        assert lib.vsa_quantize_fp8(ctypes.byref(bad), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                    None) == L.VSA_ERR_UNSUPPORTED
+        assert lib.vsa_fine_fp8(ctypes.byref(bad), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None,
+                                None) == L.VSA_ERR_UNSUPPORTED
+        assert lib.vsa_workspace_bytes(ctypes.byref(bad), L.VSA_OP_FORWARD_FP8) == 0
+    assert lib.vsa_quantize_fp8(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE,
+                                None) == L.VSA_ERR_NULL
+    assert lib.vsa_fine_fp8(ctypes.byref(p), FAKE, FAKE, FAKE, MISALIGNED, FAKE, FAKE, None,
+                            None) == L.VSA_ERR_ALIGN
+    assert lib.vsa_fine_fp8(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, MISALIGNED,
+                            None) == L.VSA_ERR_ALIGN
+    ws = lib.vsa_workspace_bytes(ctypes.byref(p), L.VSA_OP_FORWARD_FP8)
+    # three byte copies of q, k, v, the exponents, fp32 means and O_coarse
+    assert ws >= 3 * 12 * 7168 * 128 + 3 * 12 * 112 * 4 + 3 * 12 * 112 * 128 * 4 + 12 * 112 * 128 * 2
+    assert lib.vsa_forward_fp8(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE,
+                               ws - 1, None) == L.VSA_ERR_WORKSPACE
+    assert lib.vsa_forward_fp8(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None,
+                               ws, None) == L.VSA_ERR_NULL
