@@ -15,7 +15,10 @@ attention on the same padded sequence (the fine kernel with every cube
 selected) and on the 5824 real tokens, valid x valid ("useful") TFLOPS, the
 forward and fine-stage times of every workload of the pages (tiny fp32,
 410M DiT, Wan-1.3B, Wan-14B), the fine kernel's MFMA roofline, and the fp64
-CPU oracle timed on the host cores.
+CPU oracle timed on the host cores.  An "fp8" object reports the same shape
+through the FP8 path (E4M3 q/k/v with per-cube scales): the quantization
+pass, the FP8 fine kernel with its roofline against the FP8 MFMA peak, and
+the whole FP8 forward.
 """
 from __future__ import annotations
 
@@ -39,7 +42,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-reps", type=int, default=5)
-    ap.add_argument("--stage", choices=["all", "forward", "fine", "coarse", "reorder", "backward"],
+    ap.add_argument("--stage", choices=["all", "forward", "fine", "coarse", "reorder", "backward",
+                                        "fine_fp8", "forward_fp8", "quantize_fp8"],
                     default="all",
                     help="time one stage only (for profiler runs); prints a short JSON line")
     return ap.parse_args()
@@ -143,23 +147,38 @@ def per_config(args, dev):
                               steps, warm)
         fl = flops.fine_forward_flops(w.B, w.H, w.C, w.topk, w.d)
         useful = flops.useful_fine_flops(w.B, w.H, w.d, valid_counts(w), idx.cpu().numpy())
-        out.append({"workload": w.name, "dtype": w.dtype, "B": w.B, "H": w.H, "grid": list(grid),
-                    "d": w.d, "cubes": w.C, "topk": w.topk,
-                    "forward_ms": round(f_ms, 5), "fine_ms": round(fine_ms, 5),
-                    "fine_sparse_tflops": round(fl / (fine_ms * 1e-3) / 1e12, 2),
-                    "fine_useful_tflops": round(useful / (fine_ms * 1e-3) / 1e12, 2),
-                    "useful_over_computed": round(useful / fl, 4),
-                    "timing": "hip graph replay"})
+        rec = {"workload": w.name, "dtype": w.dtype, "B": w.B, "H": w.H, "grid": list(grid),
+               "d": w.d, "cubes": w.C, "topk": w.topk,
+               "forward_ms": round(f_ms, 5), "fine_ms": round(fine_ms, 5),
+               "fine_sparse_tflops": round(fl / (fine_ms * 1e-3) / 1e12, 2),
+               "fine_useful_tflops": round(useful / (fine_ms * 1e-3) / 1e12, 2),
+               "useful_over_computed": round(useful / fl, 4),
+               "timing": "hip graph replay"}
+        if w.dtype == "bf16" and w.d == 128:
+            del cube, obuf
+            p8 = vsa.ForwardFp8Plan(w.B, w.H, grid, w.d, w.topk, dev)
+            rec["fp8_forward_ms"] = round(graph_timed(lambda: p8.run(s["q"], s["k"], s["v"]),
+                                                      steps, warm), 5)
+            del p8
+            q8 = vsa.quantize_fp8(s["q"], s["k"], s["v"], grid)
+            obuf = torch.empty((w.B, w.H, w.Np, w.d), dtype=torch.bfloat16, device=dev)
+            f8 = graph_timed(lambda: vsa.fine_fp8(*q8, idx, grid, return_lse=False, out=obuf),
+                             steps, warm)
+            rec["fp8_fine_ms"] = round(f8, 5)
+            rec["fp8_fine_sparse_tflops"] = round(fl / (f8 * 1e-3) / 1e12, 2)
+            del q8
+            cube = None
+        out.append(rec)
         del s, cube, obuf, idx, plan
         torch.cuda.empty_cache()
     return out
 
 
-def traffic_record(kernel_source):
+def traffic_record(kernel_source, record="fine_fwd_wan1.3b_traffic.json"):
     """HBM bytes per launch from the committed counter record, if it was taken
     on the current kernel source (else None)."""
     import hashlib
-    path = os.path.join(ROOT, "profiles", "fine_fwd_wan1.3b_traffic.json")
+    path = os.path.join(ROOT, "profiles", record)
     try:
         rec = json.load(open(path))
         src = open(os.path.join(ROOT, kernel_source), "rb").read()
@@ -217,6 +236,47 @@ def sparsity_sweep(args, dev):
     return out
 
 
+def fp8_section(args, w, grid, sets, idx_sets, dev):
+    """The Wan-1.3B shape through the FP8 path: quantization, the FP8 fine
+    kernel (cube-order output, the block indices of the bf16 coarse stage)
+    and the whole FP8 forward, inputs rotated as for the headline."""
+    import torch
+    import block_sparse_attention_cube_amd as vsa
+    from block_sparse_attention_cube_amd import flops
+    n = len(sets)
+    q8s = [vsa.quantize_fp8(s["q"], s["k"], s["v"], grid) for s in sets]
+    obuf = torch.empty((w.B, w.H, w.Np, w.d), dtype=torch.bfloat16, device=dev)
+    quant = lambda i: vsa.quantize_fp8(sets[i]["q"], sets[i]["k"], sets[i]["v"], grid)
+    fine8 = lambda i: vsa.fine_fp8(*q8s[i], idx_sets[i], grid, return_lse=False, out=obuf)
+    plan = vsa.ForwardFp8Plan(w.B, w.H, grid, w.d, w.topk, dev)
+    fwd8 = lambda i: plan.run(sets[i]["q"], sets[i]["k"], sets[i]["v"])
+    quant_ms = timed(quant, args.steps, args.warmup, n)
+    fine_ms = timed(fine8, args.steps, args.warmup, n)
+    launch_ms = per_launch(fine8, args.steps, args.warmup, n)
+    fwd_ms = timed(fwd8, args.steps, args.warmup, n)
+    fl = flops.fine_forward_flops(w.B, w.H, w.C, w.topk, w.d)
+    code_bytes = 3 * w.B * w.H * w.Np * w.d
+    raster_bytes = 3 * w.B * w.H * w.N * w.d * 2
+    achieved = fl / (launch_ms * 1e-3) / 1e12
+    return {
+        "scheme": "E4M3 q, k, v with per-cube power-of-two scales; P rounded to E4M3; "
+                  "fp32 accumulation; coarse stage and top-K as the bf16 path",
+        "quantize_ms": round(quant_ms, 5),
+        "quantize_gbps": round((raster_bytes + code_bytes) / (quant_ms * 1e-3) / 1e9, 1),
+        "fine_ms": round(fine_ms, 5),
+        "fine_launch_ms": round(launch_ms, 5),
+        "fine_tflops": round(fl / (fine_ms * 1e-3) / 1e12, 2),
+        "forward_ms": round(fwd_ms, 5),
+        "speedup_fine_vs_bf16": None,
+        "roofline": {"bound": "mfma", "kernel": "fine_fwd_fp8_kernel<false> (vsa_fine_fp8)",
+                     "achieved": round(achieved, 2), "peak": flops.PEAK_FP8_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / flops.PEAK_FP8_TFLOPS, 4),
+                     "traffic": traffic_record("block_sparse_attention_cube_amd/csrc/fine_fp8.hip",
+                                               "fine_fp8_wan1.3b_traffic.json"),
+                     "flops_per_launch": fl, "launch_ms": round(launch_ms, 5)},
+    }
+
+
 CAL_BYTES = 256 << 20
 
 
@@ -240,6 +300,16 @@ def stage_only(args, w, grid, sets, cube_sets, step):
         return
     elif args.stage == "reorder":
         fn = lambda i: [vsa.reorder(sets[i][t], grid) for t in "qkv"]
+    elif args.stage == "quantize_fp8":
+        fn = lambda i: vsa.quantize_fp8(sets[i]["q"], sets[i]["k"], sets[i]["v"], grid)
+    elif args.stage == "forward_fp8":
+        plan8 = vsa.ForwardFp8Plan(w.B, w.H, grid, w.d, w.topk, sets[0]["q"].device)
+        fn = lambda i: plan8.run(sets[i]["q"], sets[i]["k"], sets[i]["v"])
+    elif args.stage == "fine_fp8":
+        idx = [vsa.coarse(c["q"], c["k"], c["v"], grid, w.topk)[1] for c in cube_sets]
+        q8s = [vsa.quantize_fp8(s["q"], s["k"], s["v"], grid) for s in sets]
+        out = torch.empty_like(cube_sets[0]["q"])
+        fn = lambda i: vsa.fine_fp8(*q8s[i], idx[i], grid, return_lse=False, out=out)
     else:
         idx = [vsa.coarse(c["q"], c["k"], c["v"], grid, w.topk)[1] for c in cube_sets]
         out = torch.empty_like(cube_sets[0]["q"])
@@ -319,6 +389,8 @@ def main():
                                              real_grid, out=o_real),
                           max(10, args.steps // 8), max(2, args.warmup // 4), N_SETS)
     useful = flops.useful_fine_flops(w.B, w.H, w.d, valid_counts(w), idx_sets[0].cpu().numpy())
+    fp8 = fp8_section(args, w, grid, sets, idx_sets, dev)
+    fp8["speedup_fine_vs_bf16"] = round(fine_launch_ms / fp8["fine_launch_ms"], 3)
     configs_out = per_config(args, dev)
 
     sweep = sparsity_sweep(args, dev)
@@ -364,6 +436,7 @@ def main():
         "value_p90_ms": round(p90_ms, 5),
         "fine_useful_tflops": round(useful / (fine_ms * 1e-3) / 1e12, 2),
         "per_config": configs_out,
+        "fp8": fp8,
         "sweep": sweep,
         "fine_launch_ms": round(fine_launch_ms, 5),
         "roofline": {"bound": "mfma", "kernel": "fine_fwd_bf16_kernel<128,false> (vsa_fine)",

@@ -94,8 +94,8 @@ __device__ __forceinline__ void dma_cube(const __amdgpu_buffer_rsrc_t& rs, uint3
 
 // Masking of pad key slots inside a cube: element j of lane group lg in
 // score block b is key slot (it, ih, iw) = (b % 4, lg, j).  The (ih, iw)
-// part is an accumulator init (0 valid, -inf pad); the it part is a -inf
-// exp2 offset for blocks b % 4 >= nt.
+// part is the accumulator init of the score MFMA (0 valid, -inf pad); the it
+// part is a -inf exp2 offset for blocks b % 4 >= nt.
 __device__ __forceinline__ f32x4 hw_bias(int ext, int lg) {
   const int nh = (ext >> 3) & 7, nw = ext >> 6;
   const float vl = lg < nh ? 0.f : -INFINITY;
@@ -123,29 +123,33 @@ __device__ __forceinline__ float row_max(const f32x4* t) {
   return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
-// Per-step key data, one step per lane: cubes c0 | c1 << 16 and, per cube,
-// ext | (ek + 128) << 9 | (ev + 128) << 17.  A missing second cube (odd K)
-// repeats the first with extent 0: every key of it is masked.
-__device__ __forceinline__ uint32_t cube_info(const Geo& g, int c, const int32_t* ek,
-                                              const int32_t* ev, bool real) {
-  if (!real) return (128u << 9) | (128u << 17);
-  const CubeExt e = cube_extent(g, c);
-  return static_cast<uint32_t>(e.nt | (e.nh << 3) | (e.nw << 6)) |
-         (static_cast<uint32_t>(ek[c] + 128) << 9) | (static_cast<uint32_t>(ev[c] + 128) << 17);
+// Per-step key data, one step per lane, in two tables: cubes and extents
+// (tc = c0 | c1 << 16, tx = ext0 | ext1 << 16), and the exponents
+// (te = ek0 | ev0 << 8 | ek1 << 16 | ev1 << 24, each + 128).  A missing
+// second cube (odd K) repeats the first with extent 0: every key of it is
+// masked.  The loads are issued without branches (a lane past the list
+// reads entry 0), and the exponents are loaded separately so that the tile
+// DMA, which needs only the cube indices, need not wait for them.
+__device__ __forceinline__ void lane_cubes(const Geo& g, const int32_t* __restrict__ sel,
+                                           int first, int lane, uint32_t& tc, uint32_t& tx) {
+  const int m0 = 2 * (first + lane), m1 = m0 + 1;
+  const bool r0 = m0 < g.K, r1 = m1 < g.K;
+  const int s0 = sel[r0 ? m0 : 0], s1 = sel[r1 ? m1 : 0];
+  const int c0 = min(max(s0, 0), g.C - 1);
+  const int c1 = r1 ? min(max(s1, 0), g.C - 1) : c0;
+  auto ext = [&](int c, bool real) -> uint32_t {
+    if (!real) return 0u;
+    const CubeExt e = cube_extent(g, c);
+    return static_cast<uint32_t>(e.nt | (e.nh << 3) | (e.nw << 6));
+  };
+  tc = static_cast<uint32_t>(c0) | (static_cast<uint32_t>(c1) << 16);
+  tx = ext(c0, r0) | (ext(c1, r1) << 16);
 }
 
-__device__ __forceinline__ void lane_steps(const Geo& g, const int32_t* __restrict__ sel,
-                                           const int32_t* ek, const int32_t* ev, int first,
-                                           int lane, uint32_t& tc, uint32_t& ta, uint32_t& tb) {
-  tc = 0; ta = 0; tb = 0;
-  const int m0 = 2 * (first + lane), m1 = m0 + 1;
-  if (m0 < g.K) {
-    const int c0 = min(max(sel[m0], 0), g.C - 1);
-    const int c1 = m1 < g.K ? min(max(sel[m1], 0), g.C - 1) : c0;
-    tc = static_cast<uint32_t>(c0) | (static_cast<uint32_t>(c1) << 16);
-    ta = cube_info(g, c0, ek, ev, true);
-    tb = cube_info(g, c1, ek, ev, m1 < g.K);
-  }
+__device__ __forceinline__ uint32_t lane_exps(const int32_t* ek, const int32_t* ev, uint32_t tc) {
+  const int c0 = static_cast<int>(tc & 0xffffu), c1 = static_cast<int>(tc >> 16);
+  return static_cast<uint32_t>(ek[c0] + 128) | (static_cast<uint32_t>(ev[c0] + 128) << 8) |
+         (static_cast<uint32_t>(ek[c1] + 128) << 16) | (static_cast<uint32_t>(ev[c1] + 128) << 24);
 }
 
 struct StepKeys {
@@ -154,17 +158,16 @@ struct StepKeys {
   int vscale;      // E8M0 code of 2^ev of the cube whose PV blocks this lane scales
 };
 
-__device__ __forceinline__ StepKeys step_keys(uint32_t a, uint32_t b, float cq, int lg) {
+__device__ __forceinline__ StepKeys step_keys(uint32_t x, uint32_t e, float cq, int lg) {
   StepKeys s;
-  const uint32_t x[2] = {a, b};
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
-    s.ext[h] = static_cast<int>(x[h] & 511u);
-    const int ek = static_cast<int>((x[h] >> 9) & 255u) - 128;
+    s.ext[h] = static_cast<int>((x >> (16 * h)) & 511u);
+    const int ek = static_cast<int>((e >> (16 * h)) & 255u) - 128;
     // the product of two tiny scales may leave the fp32 range: keep it normal
     s.c2[h] = fmaxf(__builtin_ldexpf(cq, ek), 1.17549435e-38f);
   }
-  s.vscale = static_cast<int>((lg < 2 ? a : b) >> 17) - 128 + 127;
+  s.vscale = static_cast<int>((e >> (lg < 2 ? 8 : 24)) & 255u) - 128 + 127;
   return s;
 }
 
@@ -243,16 +246,20 @@ __global__ __launch_bounds__(256, 2) void fine_fwd_fp8_kernel(
   const __amdgpu_buffer_rsrc_t vrs = rsrc8(vt8 + head0, head_bytes);
 
   // DMA byte offsets inside a cube tile.  K: row r = P / 8 holds logical
-  // chunk (P % 8) ^ ((r >> 1) & 7); V^T: row d = P / 4 holds logical chunk
-  // (P % 4) ^ ((d >> 2) & 3).  Both put the 16 lanes of one operand read on
-  // distinct bank positions.
+  // chunk (P % 8) ^ ksw(r); V^T: row d = P / 4 holds logical chunk
+  // (P % 4) ^ vsw(d).  A 16-byte LDS read is served 8 lanes (128 bytes) at a
+  // time: the swizzles put every 8 consecutive lanes of an operand read (and
+  // every 16) on distinct 16-byte bank positions.  Both use only the low 4
+  // row bits, so the per-lane read offsets hold for every 16-row block.
+  auto ksw = [](int r) { return (r & 7) ^ ((r >> 3) & 1); };
+  auto vsw = [](int d) { return ((d >> 1) & 3) ^ ((d >> 3) & 1); };
   uint32_t koff[kDma], voff[kDma];
 #pragma unroll
   for (int u = 0; u < kDma; ++u) {
     const int P = u * 256 + tid;
     const int r = P >> 3, d = P >> 2;
-    koff[u] = r * kD + (((P & 7) ^ ((r >> 1) & 7)) * 16);
-    voff[u] = d * 64 + (((P & 3) ^ ((d >> 2) & 3)) * 16);
+    koff[u] = r * kD + (((P & 7) ^ ksw(r)) * 16);
+    voff[u] = d * 64 + (((P & 3) ^ vsw(d)) * 16);
   }
   auto stage = [&](const __amdgpu_buffer_rsrc_t& rs, const uint32_t* off, uint32_t cubes,
                    uint8_t* slot) {
@@ -270,9 +277,9 @@ __global__ __launch_bounds__(256, 2) void fine_fwd_fp8_kernel(
   }
   // operand read offsets (loop invariant)
   int kro[2];
-  kro[0] = li * kD + (((2 * lg) ^ ((li >> 1) & 7)) * 16);
-  kro[1] = li * kD + (((2 * lg + 1) ^ ((li >> 1) & 7)) * 16);
-  const int vro = li * 64 + ((lg ^ ((li >> 2) & 3)) * 16);
+  kro[0] = li * kD + (((2 * lg) ^ ksw(li)) * 16);
+  kro[1] = li * kD + (((2 * lg + 1) ^ ksw(li)) * 16);
+  const int vro = li * 64 + ((lg ^ vsw(li)) * 16);
   const int one4 = 0x38383838;   // E4M3 1.0 x 4
   const i32x8 ones = {one4, one4, one4, one4, one4, one4, one4, one4};
 
@@ -281,17 +288,20 @@ __global__ __launch_bounds__(256, 2) void fine_fwd_fp8_kernel(
   for (int e = 0; e < kD / 16; ++e) oacc[e] = f32x4{0.f, 0.f, 0.f, 0.f};
   f32x4 lacc = {0.f, 0.f, 0.f, 0.f};
 
-  uint32_t tab_c, tab_a, tab_b;
-  lane_steps(g, sel, ek_head, ev_head, 0, lane, tab_c, tab_a, tab_b);
-  auto key_c = [&](int n) { return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(tab_c), n & 63)); };
-  auto key_a = [&](int n) { return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(tab_a), n & 63)); };
-  auto key_b = [&](int n) { return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(tab_b), n & 63)); };
+  uint32_t tab_c, tab_x, tab_e;
+  lane_cubes(g, sel, 0, lane, tab_c, tab_x);
+  auto rl = [](uint32_t t, int n) {
+    return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(t), n & 63));
+  };
 
-  // prologue: K(0), V(0), K(1) in flight together
-  const StepKeys s0 = step_keys(key_a(0), key_b(0), cq, lg);
-  stage(krs, koff, key_c(0), kring);
-  stage(vrs, voff, key_c(0), vring);
-  if (ns > 1) stage(krs, koff, key_c(1), kring + kPair);
+  // prologue: K(0), V(0), K(1) in flight together.  The staging needs only
+  // the cube indices; the exponent loads (which depend on them) are issued
+  // after it and complete under the DMA.
+  stage(krs, koff, rl(tab_c, 0), kring);
+  stage(vrs, voff, rl(tab_c, 0), vring);
+  if (ns > 1) stage(krs, koff, rl(tab_c, 1), kring + kPair);
+  tab_e = lane_exps(ek_head, ev_head, tab_c);
+  const StepKeys s0 = step_keys(rl(tab_x, 0), rl(tab_e, 0), cq, lg);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   int ext_cur[2] = {s0.ext[0], s0.ext[1]};
@@ -315,12 +325,16 @@ __global__ __launch_bounds__(256, 2) void fine_fwd_fp8_kernel(
     // K(n+1) and V(n) have landed for every wave; slots of K(n), V(n-1) are free
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    const uint32_t c_next = key_c(n + 1);
-    const StepKeys sn = step_keys(key_a(n + 1), key_b(n + 1), cq, lg);
-    stage(vrs, voff, c_next, vring + P1 * kPair);
+    const StepKeys sn = step_keys(rl(tab_x, n + 1), rl(tab_e, n + 1), cq, lg);
+    stage(vrs, voff, rl(tab_c, n + 1), vring + P1 * kPair);
     if (n + 2 < ns) {
-      if (((n + 2) & 63) == 0) lane_steps(g, sel, ek_head, ev_head, n + 2, lane, tab_c, tab_a, tab_b);
-      stage(krs, koff, key_c(n + 2), kring + P0 * kPair);
+      if (((n + 2) & 63) == 0) {
+        lane_cubes(g, sel, n + 2, lane, tab_c, tab_x);
+        stage(krs, koff, rl(tab_c, n + 2), kring + P0 * kPair);
+        tab_e = lane_exps(ek_head, ev_head, tab_c);
+      } else {
+        stage(krs, koff, rl(tab_c, n + 2), kring + P0 * kPair);
+      }
     }
 #pragma unroll
     for (int h = 0; h < 2; ++h)
@@ -333,7 +347,7 @@ __global__ __launch_bounds__(256, 2) void fine_fwd_fp8_kernel(
     scores(kring + P1 * kPair, kro, qf, bias, tnext);
     const i32x8 pf = probabilities(tcur);
     pv(vring + P0 * kPair, vro, pf, ones, vscale, oacc, lacc);
-    // S(n+1) into exp2 units (relative to the running max)
+    // S(n+1) into exp2 units (relative to the running max), pads to -inf
 #pragma unroll
     for (int b = 0; b < 8; ++b) {
       const int h = b >> 2;

@@ -13,6 +13,7 @@ BLOCK = 64
 
 # MI355X published dense peaks (no structured sparsity)
 PEAK_BF16_TFLOPS = 2516.6      # 256 CU x 2.4 GHz x 4096 FLOP/clk
+PEAK_FP8_TFLOPS = 5033.2       # 256 CU x 2.4 GHz x 8192 FLOP/clk
 PEAK_FP32_MFMA_TFLOPS = 157.3
 PEAK_HBM_GBPS = 8000.0
 
