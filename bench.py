@@ -39,7 +39,8 @@ def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    # the GPU clock takes a few hundred calls to settle; untimed
+    ap.add_argument("--warmup", type=int, default=400)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-reps", type=int, default=5)
     ap.add_argument("--stage", choices=["all", "forward", "fine", "coarse", "reorder", "backward",
