@@ -155,24 +155,29 @@ def per_config(args, dev):
                "fine_useful_tflops": round(useful / (fine_ms * 1e-3) / 1e12, 2),
                "useful_over_computed": round(useful / fl, 4),
                "timing": "hip graph replay"}
+        del cube, obuf, plan      # the cube-order copies are not needed below
         if w.dtype == "bf16" and w.d == 128:
-            del cube, obuf
-            p8 = vsa.ForwardFp8Plan(w.B, w.H, grid, w.d, w.topk, dev)
-            rec["fp8_forward_ms"] = round(graph_timed(lambda: p8.run(s["q"], s["k"], s["v"]),
-                                                      steps, warm), 5)
-            del p8
-            q8 = vsa.quantize_fp8(s["q"], s["k"], s["v"], grid)
-            obuf = torch.empty((w.B, w.H, w.Np, w.d), dtype=torch.bfloat16, device=dev)
-            f8 = graph_timed(lambda: vsa.fine_fp8(*q8, idx, grid, return_lse=False, out=obuf),
-                             steps, warm)
-            rec["fp8_fine_ms"] = round(f8, 5)
-            rec["fp8_fine_sparse_tflops"] = round(fl / (f8 * 1e-3) / 1e12, 2)
-            del q8
-            cube = None
+            rec.update(fp8_config(w, grid, s, idx, fl, steps, warm, dev))
         out.append(rec)
-        del s, cube, obuf, idx, plan
+        del s, idx
         torch.cuda.empty_cache()
     return out
+
+
+def fp8_config(w, grid, s, idx, fl, steps, warm, dev):
+    """The FP8 forward and FP8 fine stage of one d = 128 workload (HIP-graph
+    replays; the fine stage uses the bf16 path's block indices)."""
+    import torch
+    import block_sparse_attention_cube_amd as vsa
+    plan = vsa.ForwardFp8Plan(w.B, w.H, grid, w.d, w.topk, dev)
+    fwd_ms = graph_timed(lambda: plan.run(s["q"], s["k"], s["v"]), steps, warm)
+    del plan
+    q8 = vsa.quantize_fp8(s["q"], s["k"], s["v"], grid)
+    obuf = torch.empty((w.B, w.H, w.Np, w.d), dtype=torch.bfloat16, device=dev)
+    fine_ms = graph_timed(lambda: vsa.fine_fp8(*q8, idx, grid, return_lse=False, out=obuf),
+                          steps, warm)
+    return {"fp8_forward_ms": round(fwd_ms, 5), "fp8_fine_ms": round(fine_ms, 5),
+            "fp8_fine_sparse_tflops": round(fl / (fine_ms * 1e-3) / 1e12, 2)}
 
 
 def traffic_record(kernel_source, record="fine_fwd_wan1.3b_traffic.json"):
