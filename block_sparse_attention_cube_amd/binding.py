@@ -159,7 +159,7 @@ class ForwardPlan:
     """Preallocated outputs and workspace for repeated vsa_forward calls on one shape."""
 
     def __init__(self, B: int, H: int, grid: Grid, d: int, topk: int, dtype: torch.dtype,
-                 device, return_lse: bool = True):
+                 device, return_lse: bool = True, op: int = L.VSA_OP_FORWARD):
         self.prob = make_problem(B, H, grid, d, topk, dtype)
         L.check(L.lib().vsa_check_problem(ctypes.byref(self.prob)), "vsa_forward")
         C, Np = cube_counts(grid)
@@ -171,7 +171,7 @@ class ForwardPlan:
         self.o_coarse = torch.empty(self.shape, dtype=dtype, device=device)
         self.idx = torch.empty((B, H, C, topk), dtype=torch.int32, device=device)
         self.lse = torch.empty((B, H, Np), dtype=torch.float32, device=device) if return_lse else None
-        self.ws, self.nws = _workspace(self.prob, L.VSA_OP_FORWARD, device)
+        self.ws, self.nws = _workspace(self.prob, op, device)
 
     def run(self, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor):
         for t, n in ((q, "q"), (k, "k"), (v, "v")):
@@ -298,10 +298,11 @@ class ForwardFp8Plan(ForwardPlan):
 
     def __init__(self, B: int, H: int, grid: Grid, d: int, topk: int, device,
                  return_lse: bool = True):
-        super().__init__(B, H, grid, d, topk, torch.bfloat16, device, return_lse)
-        self.ws, self.nws = _workspace(self.prob, L.VSA_OP_FORWARD_FP8, device)
-        if self.ws is None:
-            L.check(L.VSA_ERR_UNSUPPORTED, "vsa_forward_fp8")
+        prob = make_problem(B, H, grid, d, topk, torch.bfloat16)
+        if L.lib().vsa_workspace_bytes(ctypes.byref(prob), L.VSA_OP_FORWARD_FP8) == 0:
+            L.check(L.VSA_ERR_UNSUPPORTED, "vsa_forward_fp8")   # d != 128 or invalid
+        super().__init__(B, H, grid, d, topk, torch.bfloat16, device, return_lse,
+                         op=L.VSA_OP_FORWARD_FP8)
 
     def run(self, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor):
         for t, n in ((q, "q"), (k, "k"), (v, "v")):
