@@ -348,7 +348,8 @@ __global__ __launch_bounds__(256) void idx_transpose_kernel(const int32_t* __res
 }
 
 // ---------------------------------------------------------------------------
-// dQ: one workgroup per query cube, 4 waves x 16 query slots (as the forward).
+// dQ: one workgroup per query cube, 4 waves x 16 query slots (wave w owns
+// row ih = w of the cube, as the forward).
 // Per selected key cube the K and V tiles go from cube order straight into
 // a 2-slot LDS ring by DMA; K^T comes from transposed reads of the K tile.
 // Pad key slots get P = 0 as in the forward: a -inf accumulator init for the
@@ -369,7 +370,13 @@ __global__ __launch_bounds__(256, 2) void fine_bwd_dq_kernel(BwdFineArgs a, Geo 
   const int K = g.K;
   const int32_t* __restrict__ sel = a.idx + static_cast<int64_t>(tile) * K;
   const float c2 = inv_sqrt_d<D>() * kLog2e;
-  const int64_t qrow = bh * g.Np + static_cast<int64_t>(qc) * 64 + wave * 16 + li;   // cube-order stats
+  // wave w owns the 16 query slots of row ih = w of the cube: slot
+  // qslot = 16 (li / 4) + 4 w + li % 4; a wave whose row lies past the grid
+  // has no valid query and only stages tiles and meets barriers
+  const CubeExt eq = cube_extent(g, qc);
+  const int qslot = 16 * (li >> 2) + 4 * wave + (li & 3);
+  const bool active = wave < eq.nh;   // wave-uniform
+  const int64_t qrow = bh * g.Np + static_cast<int64_t>(qc) * 64 + qslot;   // cube-order stats
   const int64_t head0 = bh * g.N * D;   // raster q, k, v, dO of this head
 
   // DMA byte offsets (from a key cube's first raster row) of this thread's
@@ -395,8 +402,7 @@ __global__ __launch_bounds__(256, 2) void fine_bwd_dq_kernel(BwdFineArgs a, Geo 
 
   u32x4 qf[kKS], df[kKS];
   {
-    const CubeExt eq = cube_extent(g, qc);
-    const int it = wave, ih = li >> 2, iw = li & 3;
+    const int it = li >> 2, ih = wave, iw = li & 3;
     const bool valid = it < eq.nt && ih < eq.nh && iw < eq.nw;   // pad rows: P = 0 via lse2
     const int64_t row = cube_row<true>(g, eq, qc) + (valid ? slot_row<true>(g, it, ih, iw) : 0);
 #pragma unroll
@@ -462,6 +468,7 @@ __global__ __launch_bounds__(256, 2) void fine_bwd_dq_kernel(BwdFineArgs a, Geo 
       if (((n + 1) & 63) == 0) keys(n + 1);
       stage(n + 1, smem + (SLOT ^ 1) * 2 * kT);
     }
+    if (!active) return;   // staging only
     const uint16_t* k_t = smem + SLOT * 2 * kT;
     const uint16_t* v_t = k_t + kT;
     if (ext != ext_cur) {
@@ -523,8 +530,7 @@ __global__ __launch_bounds__(256, 2) void fine_bwd_dq_kernel(BwdFineArgs a, Geo 
   __syncthreads();   // every wave is done with the ring
 
   // epilogue: dq[q][d] = scale * acc + dQc[qc][d] / n_qc
-  uint16_t* const stage_o = smem;
-  const CubeExt eq = cube_extent(g, qc);
+  uint16_t* const stage_o = smem;   // rows of skipped waves are pad slots, never written out
   const float inv_n = 1.f / static_cast<float>(eq.nt * eq.nh * eq.nw);
   const float* cq = a.dqc == nullptr ? nullptr : a.dqc + (bh * g.C + qc) * D;
 #pragma unroll
@@ -536,7 +542,7 @@ __global__ __launch_bounds__(256, 2) void fine_bwd_dq_kernel(BwdFineArgs a, Geo 
       x[r] = dacc[dt][r] * inv_sqrt_d<D>() + (cq ? cq[d] * inv_n : 0.f);
     }
     const u32x2 w = {pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3])};
-    *reinterpret_cast<u32x2*>(stage_o + (wave * 16 + li) * kOS + 16 * dt + 4 * lg) = w;
+    if (active) *reinterpret_cast<u32x2*>(stage_o + qslot * kOS + 16 * dt + 4 * lg) = w;
   }
   __syncthreads();
   write_cube_rows<D>(stage_o, a.dq, g, bh, qc, tid);
