@@ -2,8 +2,7 @@
 // its K selected 64-token key cubes (64x64 blocks).
 //
 // bf16 path (the hot loop), one workgroup = 4 waves = one query cube; wave w
-// owns the 16 query slots of row ih = w of the cube and keeps their Q
-// fragment in VGPRs (a wave whose row is past the grid computes nothing).
+// owns query slots 16w..16w+15 and keeps its Q fragment in VGPRs.
 //   * Gather: q, k, v are read either in cube order (64 rows per cube) or
 //     straight from raster order, where slot (it, ih, iw) of a cube is row
 //     base(cube) + (it*Hh + ih)*Ww + iw, so no reordered copy is needed.
@@ -294,18 +293,11 @@ __global__ __launch_bounds__(256, 2) void fine_fwd_bf16_kernel(
     }
   };
 
-  // Q fragment: B operand of S^T.  Wave w owns the 16 query slots of row
-  // ih = w of the cube, lane li the slot (it, iw) = (li / 4, li % 4), i.e.
-  // slot qslot = 16 (li / 4) + 4 w + li % 4; the lane holds
-  // Q[qslot][32ks + 8lg .. +7].  A wave whose row lies past the grid's Hh
-  // extent (edge cubes) has no valid query and skips all compute; it still
-  // stages its share of every tile and meets every barrier.
+  // Q fragment: B operand of S^T, lane holds Q[slot 16w+li][32ks + 8lg .. +7]
   u32x4 qf[kKS];
   const CubeExt eq = cube_extent(g, qc);
-  const int qslot = 16 * (li >> 2) + 4 * wave + (li & 3);
-  const bool active = wave < eq.nh;   // wave-uniform
   {
-    const int it = li >> 2, ih = wave, iw = li & 3;
+    const int it = wave, ih = li >> 2, iw = li & 3;
     const bool valid = !RASTER || (it < eq.nt && ih < eq.nh && iw < eq.nw);
     const int row = cube_row<RASTER>(g, eq, qc) + (valid ? slot_row<RASTER>(g, it, ih, iw) : 0);
     const uint16_t* qrow = q + head0 + static_cast<int64_t>(row) * D;
@@ -344,20 +336,19 @@ __global__ __launch_bounds__(256, 2) void fine_fwd_bf16_kernel(
   // the masks follow the key cube's extent and are rebuilt only when it changes
   int hw_cur = ext0 >> 3, nt_cur = ext0 & 7;
   f32x4 bias = hw_bias(ext0, lg);
-  f32x4 tcur[4] = {};
-  float mb = 0.f;  // running row max, exp2 units
-  float mbk[4];    // exp2 offset of key tile kb: -mb, or -inf for tiles past the cube's t extent
-  if (active) {
-    score_tile<D>(kring, kro, qf, bias, tcur);
+  f32x4 tcur[4];
+  score_tile<D>(kring, kro, qf, bias, tcur);
+  float mb;     // running row max, exp2 units
+  float mbk[4]; // exp2 offset of key tile kb: -mb, or -inf for tiles past the cube's t extent
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
-      tcur[kb] = kb < nt_cur ? tcur[kb] * c2 : f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-    mb = row_max(tcur);
+  for (int kb = 0; kb < 4; ++kb)
+    tcur[kb] = kb < nt_cur ? tcur[kb] * c2 : f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+  mb = row_max(tcur);
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) tcur[kb] = tcur[kb] - mb;
+  for (int kb = 0; kb < 4; ++kb) {
+    tcur[kb] = tcur[kb] - mb;
+    mbk[kb] = kb < nt_cur ? -mb : -INFINITY;
   }
-#pragma unroll
-  for (int kb = 0; kb < 4; ++kb) mbk[kb] = kb < nt_cur ? -mb : -INFINITY;
 
   // One step per selected key cube.  The loop is unrolled by two so that the
   // ring slots (P0 = n & 1) are constants and every LDS address is a
@@ -373,7 +364,6 @@ __global__ __launch_bounds__(256, 2) void fine_fwd_bf16_kernel(
       if (((n + 2) & 63) == 0) lane_keys<RASTER>(g, sel, n + 2, K, lane, ext_lanes, row_lanes);
       stage(krs, koff, kalt, key_row(n + 2), key_ext(n + 2), kring + P0 * kT);
     }
-    if (!active) return;   // no valid query row in this wave: staging only
     if ((ext >> 3) != hw_cur) {
       hw_cur = ext >> 3;
       bias = hw_bias(ext, lg);
@@ -423,30 +413,26 @@ __global__ __launch_bounds__(256, 2) void fine_fwd_bf16_kernel(
   {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    if (active) {
-      u32x4 pf[2];
-      probabilities(tcur, pf);
-      if ((K - 1) & 1) pv_tile<D>(vring + kT, vtr, pf, oacc, lacc);
-      else pv_tile<D>(vring, vtr, pf, oacc, lacc);
-    }
+    u32x4 pf[2];
+    probabilities(tcur, pf);
+    if ((K - 1) & 1) pv_tile<D>(vring + kT, vtr, pf, oacc, lacc);
+    else pv_tile<D>(vring, vtr, pf, oacc, lacc);
   }
   __syncthreads();   // every wave is done with the rings: reuse them for O
 
   // ---- epilogue: l is the same in every accumulator row of lacc
   const float l = lacc[0];
   const float inv = 1.f / l;
-  if (active && lse != nullptr && lg == 0)
-    lse[bh * g.Np + static_cast<int64_t>(qc) * 64 + qslot] = (mb + log2f(l)) * kLn2;
+  if (lse != nullptr && lg == 0)
+    lse[bh * g.Np + static_cast<int64_t>(qc) * 64 + wave * 16 + li] = (mb + log2f(l)) * kLn2;
 
-  uint16_t* const o_lds = smem;  // [64][kOS]; rows of skipped waves are pad slots
-  if (active) {
+  uint16_t* const o_lds = smem;  // [64][kOS]
 #pragma unroll
-    for (int dt = 0; dt < kDT; ++dt) {
-      // lane holds O[qslot][d = 16dt + 4lg + r], r = 0..3
-      const u32x2 w = {pack_bf16x2(oacc[dt][0] * inv, oacc[dt][1] * inv),
-                       pack_bf16x2(oacc[dt][2] * inv, oacc[dt][3] * inv)};
-      *reinterpret_cast<u32x2*>(o_lds + qslot * kOS + 16 * dt + 4 * lg) = w;
-    }
+  for (int dt = 0; dt < kDT; ++dt) {
+    // lane holds O[q = 16w+li][d = 16dt + 4lg + r], r = 0..3
+    const u32x2 w = {pack_bf16x2(oacc[dt][0] * inv, oacc[dt][1] * inv),
+                     pack_bf16x2(oacc[dt][2] * inv, oacc[dt][3] * inv)};
+    *reinterpret_cast<u32x2*>(o_lds + (wave * 16 + li) * kOS + 16 * dt + 4 * lg) = w;
   }
   __syncthreads();
 #pragma unroll
