@@ -6,7 +6,7 @@ import torch
 
 import block_sparse_attention_cube_amd as vsa
 from oracle import vsa_oracle as vo
-from parity import assert_close
+from parity import assert_close, check_idx
 from synth import configs, inputs
 from synth.configs import Workload
 
@@ -47,10 +47,32 @@ def run(w, with_coarse=True):
     return x, t, (o_fine, o_coarse, idx, lse), (dq, dk, dv)
 
 
+def check_forward(w, x, outs):
+    """The forward that feeds the backward, against the oracle: the selection
+    by the near-tie rule, then O_fine (on the GPU's own selection), O_coarse
+    and LSE element by element."""
+    o_fine, o_coarse, idx, lse = outs
+    gidx = idx.cpu().numpy()
+    ref = vo.forward(x["q"], x["k"], x["v"], w.T, w.Hh, w.Ww, w.topk)
+    near = check_idx(gidx, ref["idx"], ref["scores"], w.topk)
+    ref_g = ref if near == 0 else vo.forward(x["q"], x["k"], x["v"], w.T, w.Hh, w.Ww, w.topk,
+                                             idx=gidx)
+    errs = {
+        "o_fine": assert_close(o_fine.float().cpu().numpy(), ref_g["o_fine"], w.dtype, "O_fine"),
+        "o_coarse": assert_close(o_coarse.float().cpu().numpy(), ref["o_coarse"], w.dtype,
+                                 "O_coarse"),
+        "lse": assert_close(lse.cpu().numpy()[..., None], ref_g["lse_cube"][..., None], w.dtype,
+                            "LSE", rows=ref_g["geometry"]["valid"]),
+    }
+    print(f"{w.name}: near-tie rows {near}; max/mean |err| " +
+          ", ".join(f"{k} {a:.2e}/{b:.2e}" for k, (a, b) in errs.items()))
+
+
 @pytest.mark.parametrize("w", CASES, ids=ids)
 def test_backward_matches_oracle(w):
-    x, _, (_, _, idx, _), grads = run(w)
-    gidx = idx.cpu().numpy()
+    x, _, outs, grads = run(w)
+    check_forward(w, x, outs)
+    gidx = outs[2].cpu().numpy()
     ref = vo.backward(x["q"], x["k"], x["v"], x["do_fine"], x["do_coarse"], w.T, w.Hh, w.Ww, gidx)
     for name, got, want in zip(("dq", "dk", "dv"), grads, ref):
         assert_close(got.float().cpu().numpy(), want, w.dtype, name)

@@ -30,6 +30,12 @@ EDGE = [
              structure="field", alpha=0.5),
     Workload("one-cube-each", B=1, H=2, T=8, Hh=12, Ww=10, d=64, dtype="bf16", topk=1,
              structure="field", alpha=0.5),
+    # the top-K holds ceil(C/64) keys per lane, rounded up to a power of two:
+    # 288 cubes take the 8-key form, 640 cubes the 16-key form (ragged edges)
+    Workload("cubes288-ragged", B=1, H=2, T=15, Hh=31, Ww=36, d=64, dtype="bf16", topk=16,
+             structure="field", alpha=0.5),
+    Workload("cubes640-ragged", B=1, H=2, T=16, Hh=62, Ww=39, d=128, dtype="bf16", topk=20,
+             structure="field", alpha=0.5),
 ]
 SMALL = [configs.TINY_F32, configs.DIT_410M, configs.WAN_1_3B]
 CASES = SMALL + EDGE
