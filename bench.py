@@ -102,6 +102,23 @@ def per_call(fn, calls, warmup, rotate):
     return pick(0.5), pick(0.1), pick(0.9)
 
 
+def settle_clock(fn, rotate, seconds=1.0):
+    """Untimed calls of fn for at least `seconds` of wall time before any
+    measurement: an idle GPU starts at a low clock and needs some hundred
+    milliseconds of load to reach its working clock, which a few warm-up
+    calls of a 0.1 ms kernel do not give.  Returns the wall time spent (ms)."""
+    import torch
+    t0 = time.perf_counter()
+    i = 0
+    while True:
+        for _ in range(50):
+            fn(i % rotate)
+            i += 1
+        torch.cuda.synchronize()
+        if time.perf_counter() - t0 >= seconds:
+            return round((time.perf_counter() - t0) * 1e3, 1)
+
+
 def valid_counts(w):
     """Valid slots n_c of every cube of a workload's grid, cube order."""
     ct, ch, cw = -(-w.T // 4), -(-w.Hh // 4), -(-w.Ww // 4)
@@ -195,17 +212,33 @@ def traffic_record(kernel_source, record="fine_fwd_wan1.3b_traffic.json"):
     return rec["traffic_bytes"]
 
 
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(w, x, reps):
     from threadpoolctl import threadpool_info, threadpool_limits
     from oracle import vsa_oracle as vo
-    cores = os.cpu_count() or 1
-    with threadpool_limits(limits=cores):
+    host_cpus = os.cpu_count() or 1
+    try:
+        allowed = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        allowed = host_cpus
+    with threadpool_limits(limits=allowed):
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
         t0 = time.perf_counter()
         for _ in range(reps):
             vo.forward(x["q"], x["k"], x["v"], w.T, w.Hh, w.Ww, w.topk)
         dt = time.perf_counter() - t0
     return {"value": round(dt / reps * 1e3, 3), "unit": "ms", "cores": threads, "kind": "oracle",
+            "host_cpus": host_cpus, "cpus_allowed": allowed, "blas_threads": threads,
+            "cpu_model": cpu_model(),
             "sample": f"whole {w.name} forward (all {w.H} heads, {w.C} query cubes), fp64 NumPy, "
                       f"{reps} repetitions, {dt:.1f} s total"}
 
@@ -357,6 +390,7 @@ def main():
     if args.stage != "all":
         stage_only(args, w, grid, sets, cube_sets, step)
         return
+    settle_ms = settle_clock(step, N_SETS)
     ms = timed(step, args.steps, args.warmup, N_SETS)
     med_ms, p10_ms, p90_ms = per_call(step, max(20, args.steps // 2), args.warmup, N_SETS)
     warm_ms = timed(lambda i: step(0), args.steps, args.warmup, 1)
@@ -428,6 +462,7 @@ def main():
         "sparse_tflops": round(fwd_tflops, 2),
         "pct_bf16_peak": round(100 * fwd_tflops / flops.PEAK_BF16_TFLOPS, 2),
         "warm_ms": round(warm_ms, 5),
+        "clock_settle_ms": settle_ms,
         "fine_ms": round(fine_ms, 5),
         "fine_tflops": round(fine_tflops, 2),
         "coarse_fine_ms": round(cf_ms, 5),
