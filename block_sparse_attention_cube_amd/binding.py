@@ -155,6 +155,26 @@ def fine(qcube: torch.Tensor, kcube: torch.Tensor, vcube: torch.Tensor, idx: tor
     return o, lse
 
 
+def dense(qcube: torch.Tensor, kcube: torch.Tensor, vcube: torch.Tensor, grid: Grid,
+          return_lse: bool = True, out: Optional[torch.Tensor] = None):
+    """Dense attention over every cube (cube order, bf16): (o [B,H,Np,d], lse [B,H,Np])."""
+    _device_tensor(qcube, "qcube")
+    B, H, Np_in, d = qcube.shape
+    C, Np = cube_counts(grid)
+    if Np_in != Np:
+        raise ValueError(f"qcube has {Np_in} rows, expected {Np}")
+    _expect(kcube, qcube.shape, qcube.dtype, "kcube")
+    _expect(vcube, qcube.shape, qcube.dtype, "vcube")
+    prob = make_problem(B, H, grid, d, C, qcube.dtype)
+    dev = qcube.device
+    o = out if out is not None else torch.empty_like(qcube)
+    _expect(o, qcube.shape, qcube.dtype, "out")
+    lse = torch.empty((B, H, Np), dtype=torch.float32, device=dev) if return_lse else None
+    L.check(L.lib().vsa_dense(ctypes.byref(prob), _ptr(qcube), _ptr(kcube), _ptr(vcube), _ptr(o),
+                              _ptr(lse), _stream(dev)), "vsa_dense")
+    return o, lse
+
+
 class ForwardPlan:
     """Preallocated outputs and workspace for repeated vsa_forward calls on one shape."""
 

@@ -275,6 +275,15 @@ vsa_status vsa_fine(const vsa_problem* p, const void* qcube, const void* kcube,
                                    /*raster=*/false, nullptr, nullptr, stream));
 }
 
+vsa_status vsa_dense(const vsa_problem* p, const void* qcube, const void* kcube,
+                     const void* vcube, void* o, float* lse, hipStream_t stream) {
+  vsa_status st = check(p);
+  if (st != VSA_OK) return st;
+  if (p->dtype != VSA_BF16) return VSA_ERR_UNSUPPORTED;
+  if ((st = pointers({qcube, kcube, vcube, o}, {lse})) != VSA_OK) return st;
+  return launched(vsa::launch_dense(geometry(p), qcube, kcube, vcube, o, lse, stream));
+}
+
 vsa_status vsa_forward(const vsa_problem* p, const void* q, const void* k, const void* v,
                        void* o_fine, void* o_coarse, int32_t* idx, float* lse, void* ws,
                        size_t ws_bytes, hipStream_t stream) {

@@ -133,6 +133,11 @@ hipError_t launch_fine(const Geo& g, int dtype, const void* q, const void* k, co
                        const int32_t* idx, void* o, float* lse, bool raster,
                        const void* oc, void* o_coarse, hipStream_t s);
 
+// Dense attention over every key cube (bf16, cube order in and out), two
+// query cubes per workgroup sharing one key stream; lse optional.
+hipError_t launch_dense(const Geo& g, const void* q, const void* k, const void* v, void* o,
+                        float* lse, hipStream_t s);
+
 // FP8 (E4M3) copies of bf16 raster q, k, v (D = 128): x[i] raster in,
 // y[0], y[1] cube order [B,H,Np,D] bytes (q, k), y[2] per-cube transposed
 // V tiles [B,H,C,D,64] bytes, exps int32 [3][B*H*C] (per-cube exponents of

@@ -139,6 +139,21 @@ vsa_status vsa_fine(const vsa_problem* p, const void* qcube, const void* kcube,
                     const void* vcube, const int32_t* idx, void* o_fine, float* lse,
                     void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* Dense attention: the full softmax attention that the fine stage replaces,
+ * over every cube of the grid (the FastWan re-post's results section quotes
+ * the fine kernel's speed-up over FlashAttention-3 on the same sequence).
+ * The result equals vsa_fine with every cube selected; the kernel takes no
+ * index list and shares each staged key block between two query cubes (128
+ * query rows per workgroup).  It is the library's dense baseline.
+ *   qcube, kcube, vcube : [B,H,Np,d] bf16 cube order; pad slots of kcube and
+ *                         vcube are never attended to but must be finite.
+ *   o                   : [B,H,Np,d] out, cube order (pad rows unspecified).
+ *   lse                 : [B,H,Np] fp32 out (natural log), or NULL.
+ * p->topk must be valid (1..C) and is not used.  VSA_F32 problems return
+ * VSA_ERR_UNSUPPORTED. */
+vsa_status vsa_dense(const vsa_problem* p, const void* qcube, const void* kcube,
+                     const void* vcube, void* o, float* lse, hipStream_t stream);
+
 /* Whole forward on raster tensors: reorder + coarse + fine + inverse reorder
  * (the drop-in for FlashAttention of the section on why sparse attention
  * fails under distillation).

@@ -24,6 +24,10 @@ EDGE = [
              structure="field", alpha=0.5),
     Workload("ragged-f32-d64", B=2, H=1, T=3, Hh=7, Ww=5, d=64, dtype="f32", topk=2,
              structure="field", alpha=0.5),
+    # last cube layer two time slices deep: its query waves 2, 3 hold only pads
+    # and its key cubes take the half-depth V staging and score tiles
+    Workload("ragged-t2-bf16-d128", B=1, H=2, T=6, Hh=5, Ww=9, d=128, dtype="bf16", topk=4,
+             structure="offset", alpha=0.5),
     Workload("one-token", B=1, H=2, T=1, Hh=1, Ww=1, d=128, dtype="bf16", topk=1,
              structure="offset", alpha=0.5),
     Workload("all-cubes", B=1, H=2, T=8, Hh=12, Ww=10, d=128, dtype="bf16", topk=18,
