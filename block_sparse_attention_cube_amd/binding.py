@@ -244,6 +244,32 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, grid: Grid, topk:
     return plan.run(q, k, v)
 
 
+def forward_static(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, grid: Grid, topk: int,
+                   out=None, return_lse: bool = True):
+    """vsa_forward_static: the whole forward with the library's own device
+    scratch (no workspace).  out: optional preallocated (o_fine, o_coarse, idx,
+    lse) to write into, so that the call itself allocates nothing."""
+    B, H, N, d = _raster_inputs(q, k, v, grid)
+    C, Np = cube_counts(grid)
+    prob = make_problem(B, H, grid, d, topk, q.dtype)
+    L.check(L.lib().vsa_check_problem(ctypes.byref(prob)), "vsa_forward_static")
+    dev = q.device
+    if out is None:
+        out = (torch.empty_like(q), torch.empty_like(q),
+               torch.empty((B, H, C, topk), dtype=torch.int32, device=dev),
+               torch.empty((B, H, Np), dtype=torch.float32, device=dev) if return_lse else None)
+    o_fine, o_coarse, idx, lse = out
+    _expect(o_fine, q.shape, q.dtype, "o_fine")
+    _expect(o_coarse, q.shape, q.dtype, "o_coarse")
+    _expect(idx, (B, H, C, topk), torch.int32, "idx")
+    if lse is not None:
+        _expect(lse, (B, H, Np), torch.float32, "lse")
+    L.check(L.lib().vsa_forward_static(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v),
+                                       _ptr(o_fine), _ptr(o_coarse), _ptr(idx), _ptr(lse),
+                                       _stream(dev)), "vsa_forward_static")
+    return o_fine, o_coarse, idx, lse
+
+
 def backward(q, k, v, o_fine, lse, idx, do_fine, do_coarse, grid: Grid):
     """Gradients (dq, dk, dv) of sum(o_fine*do_fine) + sum(o_coarse*do_coarse)."""
     B, H, N, d = _raster_inputs(q, k, v, grid)

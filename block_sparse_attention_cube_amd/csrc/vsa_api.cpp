@@ -6,6 +6,7 @@
 #include "vsa_bwd.h"
 
 #include <initializer_list>
+#include <mutex>
 
 namespace {
 
@@ -191,6 +192,40 @@ vsa_status workspace(const vsa_problem* p, int op, const void* ws, size_t ws_byt
 
 vsa_status launched(hipError_t e) { return e == hipSuccess ? VSA_OK : VSA_ERR_LAUNCH; }
 
+// ---- scratch of vsa_forward_static (for callers that cannot allocate) ----
+// A file-scope device array holds the forward's workspace.  Each GPU the
+// library runs on keeps its own copy until the process ends; its device
+// address is looked up once per device (the array's name is only a host-side
+// stand-in) and every later call on that device reuses it.  Calls on one
+// device share the array: calls that overlap in time on one device race.
+constexpr size_t kScratchBytes = size_t(32) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mutex;
+void* scratch_ptr[kMaxDevices] = {};
+
+vsa_status scratch_address(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return VSA_ERR_LAUNCH;
+  std::lock_guard<std::mutex> lock(scratch_mutex);
+  if (scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr)
+      return VSA_ERR_LAUNCH;
+    scratch_ptr[dev] = ptr;
+  }
+  *out = scratch_ptr[dev];
+  return VSA_OK;
+}
+
+vsa_status forward_launch(const vsa_problem* p, const void* q, const void* k, const void* v,
+                          void* o_fine, void* o_coarse, int32_t* idx, float* lse, void* ws,
+                          hipStream_t stream);
+vsa_status backward_launch(const vsa_problem* p, const void* q, const void* k, const void* v,
+                           const void* o_fine, const float* lse, const int32_t* idx,
+                           const void* do_fine, const void* do_coarse, void* dq, void* dk,
+                           void* dv, void* ws, hipStream_t stream);
+
 }  // namespace
 
 extern "C" {
@@ -291,6 +326,43 @@ vsa_status vsa_forward(const vsa_problem* p, const void* q, const void* k, const
   if (st != VSA_OK) return st;
   if ((st = pointers({q, k, v, o_fine, o_coarse, idx}, {lse})) != VSA_OK) return st;
   if ((st = workspace(p, VSA_OP_FORWARD, ws, ws_bytes)) != VSA_OK) return st;
+  return forward_launch(p, q, k, v, o_fine, o_coarse, idx, lse, ws, stream);
+}
+
+vsa_status vsa_forward_static(const vsa_problem* p, const void* q, const void* k, const void* v,
+                              void* o_fine, void* o_coarse, int32_t* idx, float* lse,
+                              hipStream_t stream) {
+  vsa_status st = check(p);
+  if (st != VSA_OK) return st;
+  if ((st = pointers({q, k, v, o_fine, o_coarse, idx}, {lse})) != VSA_OK) return st;
+  if (vsa_workspace_bytes(p, VSA_OP_FORWARD) > kScratchBytes) return VSA_ERR_WORKSPACE;
+  void* ws = nullptr;
+  if ((st = scratch_address(&ws)) != VSA_OK) return st;
+  return forward_launch(p, q, k, v, o_fine, o_coarse, idx, lse, ws, stream);
+}
+
+vsa_status vsa_backward(const vsa_problem* p, const void* q, const void* k, const void* v,
+                        const void* o_fine, const float* lse, const int32_t* idx,
+                        const void* do_fine, const void* do_coarse, void* dq, void* dk,
+                        void* dv, void* ws, size_t ws_bytes, hipStream_t stream) {
+  vsa_status st = check(p);
+  if (st != VSA_OK) return st;
+  if ((st = pointers({q, k, v, o_fine, lse, idx, do_fine, dq, dk, dv}, {do_coarse})) != VSA_OK)
+    return st;
+  if ((st = check_backward(p)) != VSA_OK) return st;
+  if ((st = workspace(p, VSA_OP_BACKWARD, ws, ws_bytes)) != VSA_OK) return st;
+  return backward_launch(p, q, k, v, o_fine, lse, idx, do_fine, do_coarse, dq, dk, dv, ws, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+// The launch sequence of vsa_forward on a validated problem and a workspace
+// of vsa_workspace_bytes(p, VSA_OP_FORWARD) bytes.
+vsa_status forward_launch(const vsa_problem* p, const void* q, const void* k, const void* v,
+                          void* o_fine, void* o_coarse, int32_t* idx, float* lse, void* ws,
+                          hipStream_t stream) {
   const Geo g = geometry(p);
   const FwdWs w = carve_forward(p, ws, nullptr);
   const bool bf16 = p->dtype == VSA_BF16;
@@ -309,16 +381,11 @@ vsa_status vsa_forward(const vsa_problem* p, const void* q, const void* k, const
   return launched(e);
 }
 
-vsa_status vsa_backward(const vsa_problem* p, const void* q, const void* k, const void* v,
-                        const void* o_fine, const float* lse, const int32_t* idx,
-                        const void* do_fine, const void* do_coarse, void* dq, void* dk,
-                        void* dv, void* ws, size_t ws_bytes, hipStream_t stream) {
-  vsa_status st = check(p);
-  if (st != VSA_OK) return st;
-  if ((st = pointers({q, k, v, o_fine, lse, idx, do_fine, dq, dk, dv}, {do_coarse})) != VSA_OK)
-    return st;
-  if ((st = check_backward(p)) != VSA_OK) return st;
-  if ((st = workspace(p, VSA_OP_BACKWARD, ws, ws_bytes)) != VSA_OK) return st;
+// The launch sequence of vsa_backward on a validated problem and workspace.
+vsa_status backward_launch(const vsa_problem* p, const void* q, const void* k, const void* v,
+                           const void* o_fine, const float* lse, const int32_t* idx,
+                           const void* do_fine, const void* do_coarse, void* dq, void* dk,
+                           void* dv, void* ws, hipStream_t stream) {
   const Geo g = geometry(p);
   const BwdWs w = carve_backward(p, ws, nullptr);
   auto b16 = [](const void* x) { return static_cast<const uint16_t*>(x); };
@@ -352,6 +419,10 @@ vsa_status vsa_backward(const vsa_problem* p, const void* q, const void* k, cons
   }
   return launched(e);
 }
+
+}  // namespace
+
+extern "C" {
 
 vsa_status vsa_quantize_fp8(const vsa_problem* p, const void* q, const void* k, const void* v,
                             void* q8, void* k8, void* vt8, int32_t* exps, hipStream_t stream) {

@@ -167,6 +167,23 @@ vsa_status vsa_forward(const vsa_problem* p, const void* q, const void* k, const
                        void* o_fine, void* o_coarse, int32_t* idx, float* lse,
                        void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* vsa_forward without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  Arguments, results and errors are
+ * those of vsa_forward; the same kernels run.  Its workspace is a 32 MiB
+ * device array inside the library (one per GPU, held until the process
+ * ends): a problem whose vsa_workspace_bytes(p, VSA_OP_FORWARD) exceeds
+ * 32 MiB returns VSA_ERR_WORKSPACE before anything is enqueued (the Wan-1.3B
+ * 480p shape needs 2.4 MB; the Wan-14B 720p shape, 103 MB, does not fit).
+ * The call allocates nothing: the first call on a device looks up the
+ * array's device address (VSA_ERR_LAUNCH if that fails).  Every call on a
+ * device uses the same array, so calls that overlap in time on one device
+ * (for example on two streams) race; every byte of it a call reads is
+ * written earlier in the same call. */
+vsa_status vsa_forward_static(const vsa_problem* p, const void* q, const void* k,
+                              const void* v, void* o_fine, void* o_coarse, int32_t* idx,
+                              float* lse, hipStream_t stream);
+
 /* Backward of vsa_forward, the trainable path (VSA trains in place of
  * FlashAttention, section on why sparse attention fails under
  * distillation).  Gradients of  sum(o_fine*do_fine) + sum(o_coarse*do_coarse)
