@@ -337,7 +337,10 @@ hipError_t launch_typed(const Geo& g, const float* qm, const float* km, const fl
 // wave takes its operands into registers before any output is written) —
 // a per-wave load would fetch them once per wave.  Rows and columns past
 // the last cube repeat the last one (finite values no later step consumes).
-template <int D>
+// R rows per workgroup (16, or 8 for large C so that two R x C score tiles
+// fit in LDS): with R = 8 the 16-row MFMA tiles repeat the 8 rows and the
+// repeated half of each result is dropped.
+template <int D, int R>
 __device__ __forceinline__ void rows_dot2(const float* __restrict__ A1,
                                           const float* __restrict__ A2, int a0,
                                           const float* __restrict__ B1,
@@ -346,12 +349,12 @@ __device__ __forceinline__ void rows_dot2(const float* __restrict__ A1,
                                           int wave, int lane) {
   constexpr int kAS = D + 4;   // padded row stride of the staged rows (floats)
   const int li = lane & 15, lg = lane >> 4;
-  for (int e = threadIdx.x; e < 2 * kRows * D / 4; e += 64 * kWaves) {
-    const int t = e / (kRows * D / 4), rem = e % (kRows * D / 4);
+  for (int e = threadIdx.x; e < 2 * R * D / 4; e += 64 * kWaves) {
+    const int t = e / (R * D / 4), rem = e % (R * D / 4);
     const int r = rem / (D / 4), c4 = rem % (D / 4);
     const float* A = t ? A2 : A1;
     const float4 x = *reinterpret_cast<const float4*>(A + (int64_t)min(a0 + r, C - 1) * D + 4 * c4);
-    *reinterpret_cast<float4*>(stage + (t * kRows + r) * kAS + 4 * c4) = x;
+    *reinterpret_cast<float4*>(stage + (t * R + r) * kAS + 4 * c4) = x;
   }
   __syncthreads();
   // task = (product, column tile): even waves take product 1, odd waves 2
@@ -359,7 +362,7 @@ __device__ __forceinline__ void rows_dot2(const float* __restrict__ A1,
   float4 af[D / 16];
 #pragma unroll
   for (int kk = 0; kk < D / 16; ++kk)
-    af[kk] = *reinterpret_cast<const float4*>(stage + (prod * kRows + li) * kAS + 16 * kk + 4 * lg);
+    af[kk] = *reinterpret_cast<const float4*>(stage + (prod * R + li % R) * kAS + 16 * kk + 4 * lg);
   __syncthreads();
   const int ntile = (C + 15) / 16;
   const float* const B = prod ? B2 : B1;
@@ -370,18 +373,19 @@ __device__ __forceinline__ void rows_dot2(const float* __restrict__ A1,
     const int64_t cc = min(col, C - 1);
     const f32x4 acc = dot_tile<D>(af, B + cc * D, lg);
 #pragma unroll
-    for (int rr = 0; rr < 4; ++rr) out[(4 * lg + rr) * ldc + col] = acc[rr] * scale;
+    for (int rr = 0; rr < 4; ++rr)
+      if (4 * lg + rr < R) out[(4 * lg + rr) * ldc + col] = acc[rr] * scale;
   }
 }
 
-// y[r][:] = scale * sum_j T[r][j] Y[j][:] for the 16 LDS rows of T, stored to
+// y[r][:] = scale * sum_j T[r][j] Y[j][:] for the R LDS rows of T, stored to
 // out rows o0 + r (< C) of an fp32 [C][D] matrix.
-template <int D>
+template <int D, int R>
 __device__ __forceinline__ void lds_times(const float* T, int ldc, const float* __restrict__ Y,
                                           int C, float scale, float* __restrict__ out, int o0,
                                           int wave, int lane, int nwaves) {
   const int li = lane & 15, lg = lane >> 4;
-  const float* trow = T + li * ldc;
+  const float* trow = T + (li % R) * ldc;
   for (int dt = wave; dt < D / 16; dt += nwaves) {
     f32x4 acc[4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f},
                     {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
@@ -414,7 +418,7 @@ __device__ __forceinline__ void lds_times(const float* T, int ldc, const float* 
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int row = o0 + 4 * lg + r;
-      if (row < C) out[(int64_t)row * D + dt * 16 + li] = tot[r] * scale;
+      if (4 * lg + r < R && row < C) out[(int64_t)row * D + dt * 16 + li] = tot[r] * scale;
     }
   }
 }
@@ -426,7 +430,7 @@ struct ListArgs {
 };
 static_assert(64 * kWaves == kBitmapThreads, "block-list workgroups have the row kernel's size");
 
-template <int D>
+template <int D, int R>
 __global__ __launch_bounds__(64 * kWaves) void coarse_bwd_rows_kernel(
     const float* __restrict__ qm, const float* __restrict__ km, const float* __restrict__ vm,
     const float* __restrict__ docs, float* __restrict__ stats, float* __restrict__ dqc, Geo g,
@@ -438,17 +442,17 @@ __global__ __launch_bounds__(64 * kWaves) void coarse_bwd_rows_kernel(
     return;
   }
   float* s1 = lds;                 // scores, then probabilities
-  float* s2 = lds + kRows * ldc;   // dPc, then dSc
+  float* s2 = lds + R * ldc;       // dPc, then dSc
   constexpr float kScale = (D == 64) ? 0.125f : 0.08838834764831845f;
   const int C = g.C;
   const int64_t bh = blockIdx.y;
-  const int row0 = blockIdx.x * kRows;
+  const int row0 = blockIdx.x * R;
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t hoff = bh * C * D;
-  rows_dot2<D>(qm + hoff, docs + hoff, row0, km + hoff, vm + hoff, C, kScale, s1, s2, ldc, lds,
-               wave, lane);
+  rows_dot2<D, R>(qm + hoff, docs + hoff, row0, km + hoff, vm + hoff, C, kScale, s1, s2, ldc, lds,
+                  wave, lane);
   __syncthreads();
-  for (int rr = wave; rr < kRows; rr += kWaves) {
+  for (int rr = wave; rr < R; rr += kWaves) {
     float* p = s1 + rr * ldc;
     float* dp = s2 + rr * ldc;
     float m = -INFINITY;
@@ -474,31 +478,31 @@ __global__ __launch_bounds__(64 * kWaves) void coarse_bwd_rows_kernel(
     }
   }
   __syncthreads();
-  lds_times<D>(s2, ldc, km + hoff, C, kScale, dqc + hoff, row0, wave, lane, kWaves);
+  lds_times<D, R>(s2, ldc, km + hoff, C, kScale, dqc + hoff, row0, wave, lane, kWaves);
 }
 
-template <int D>
+template <int D, int R>
 __global__ __launch_bounds__(64 * kWaves) void coarse_bwd_cols_kernel(
     const float* __restrict__ qm, const float* __restrict__ km, const float* __restrict__ vm,
     const float* __restrict__ docs, const float* __restrict__ stats, float* __restrict__ dkc,
     float* __restrict__ dvc, Geo g, int ldc) {
   extern __shared__ float lds[];
-  float* t1 = lds;                 // Sc^T rows (16 key cubes x C query cubes), then Pc^T
-  float* t2 = lds + kRows * ldc;   // dPc^T, then dSc^T
+  float* t1 = lds;                 // Sc^T rows (R key cubes x C query cubes), then Pc^T
+  float* t2 = lds + R * ldc;       // dPc^T, then dSc^T
   constexpr float kScale = (D == 64) ? 0.125f : 0.08838834764831845f;
   const int C = g.C;
   const int64_t bh = blockIdx.y;
-  const int col0 = blockIdx.x * kRows;
+  const int col0 = blockIdx.x * R;
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t hoff = bh * C * D;
-  rows_dot2<D>(km + hoff, vm + hoff, col0, qm + hoff, docs + hoff, C, kScale, t1, t2, ldc, lds,
-               wave, lane);
+  rows_dot2<D, R>(km + hoff, vm + hoff, col0, qm + hoff, docs + hoff, C, kScale, t1, t2, ldc, lds,
+                  wave, lane);
   __syncthreads();
   const int64_t plane = (int64_t)g.B * g.H * C;
   const float* sm = stats + bh * C;
   const float* sl = sm + plane;
   const float* sr = sm + 2 * plane;
-  for (int e = threadIdx.x; e < kRows * C; e += 64 * kWaves) {
+  for (int e = threadIdx.x; e < R * C; e += 64 * kWaves) {
     const int jj = e / C, i = e % C;
     const float p = __expf(t1[jj * ldc + i] - sm[i]) / sl[i];
     t1[jj * ldc + i] = p;
@@ -507,22 +511,22 @@ __global__ __launch_bounds__(64 * kWaves) void coarse_bwd_cols_kernel(
   __syncthreads();
   // dKc on one half of the waves, dVc on the other
   constexpr int kHalf = kWaves / 2;
-  if (wave < kHalf) lds_times<D>(t2, ldc, qm + hoff, C, kScale, dkc + hoff, col0, wave, lane, kHalf);
-  else lds_times<D>(t1, ldc, docs + hoff, C, 1.f, dvc + hoff, col0, wave - kHalf, lane, kHalf);
+  if (wave < kHalf) lds_times<D, R>(t2, ldc, qm + hoff, C, kScale, dkc + hoff, col0, wave, lane, kHalf);
+  else lds_times<D, R>(t1, ldc, docs + hoff, C, 1.f, dvc + hoff, col0, wave - kHalf, lane, kHalf);
 }
 
-template <int D>
+template <int D, int R>
 hipError_t launch_coarse_bwd_typed(const Geo& g, const float* qm, const float* km,
                                    const float* vm, const float* docs, float* stats,
                                    float* dqc, float* dkc, float* dvc, const ListArgs& lists,
                                    hipStream_t s) {
-  const int ntile = (g.C + 15) / 16;
-  const int ldc = ntile * 16 + 1;
-  // two 16 x C score tiles, or the 2 x 16 staged operand rows if larger
-  size_t lds = (size_t)std::max(2 * kRows * ldc, 2 * kRows * (D + 4)) * sizeof(float);
+  const int ntile = (g.C + R - 1) / R;          // row (column) tiles of R cubes
+  const int ldc = (g.C + 15) / 16 * 16 + 1;     // scores are computed in 16-column tiles
+  // two R x C score tiles, or the 2 x R staged operand rows if larger
+  size_t lds = (size_t)std::max(2 * R * ldc, 2 * R * (D + 4)) * sizeof(float);
   if (lists.idx != nullptr) lds = std::max(lds, bitmap_words(g.C) * sizeof(uint32_t));
-  auto* rows = coarse_bwd_rows_kernel<D>;
-  auto* cols = coarse_bwd_cols_kernel<D>;
+  auto* rows = coarse_bwd_rows_kernel<D, R>;
+  auto* cols = coarse_bwd_cols_kernel<D, R>;
   if (lds > 65536) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(rows),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
@@ -561,9 +565,14 @@ hipError_t launch_coarse_bwd(const Geo& g, const float* qm, const float* km, con
                              float* dvc, const int32_t* idx, int32_t* offsets, int32_t* list,
                              int32_t* order, hipStream_t s) {
   const ListArgs lists = {g.C <= kBitmapCubes ? idx : nullptr, offsets, list, order};
+  // 16 cubes per workgroup while two 16 x C fp32 tiles fit the LDS, else 8
+  if (g.C <= kCoarseBwd16Cubes)
+    return g.D == 128
+               ? launch_coarse_bwd_typed<128, 16>(g, qm, km, vm, docs, stats, dqc, dkc, dvc, lists, s)
+               : launch_coarse_bwd_typed<64, 16>(g, qm, km, vm, docs, stats, dqc, dkc, dvc, lists, s);
   return g.D == 128
-             ? launch_coarse_bwd_typed<128>(g, qm, km, vm, docs, stats, dqc, dkc, dvc, lists, s)
-             : launch_coarse_bwd_typed<64>(g, qm, km, vm, docs, stats, dqc, dkc, dvc, lists, s);
+             ? launch_coarse_bwd_typed<128, 8>(g, qm, km, vm, docs, stats, dqc, dkc, dvc, lists, s)
+             : launch_coarse_bwd_typed<64, 8>(g, qm, km, vm, docs, stats, dqc, dkc, dvc, lists, s);
 }
 
 }  // namespace vsa

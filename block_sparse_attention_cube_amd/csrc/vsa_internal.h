@@ -12,7 +12,10 @@ namespace vsa {
 constexpr int kCube = 4;     // cube edge along each of (t, y, x)
 constexpr int kSlots = 64;   // tokens per cube
 constexpr int kMaxCubes = 2048;  // coarse score rows are staged in LDS: 16 x C fp32
-constexpr int kMaxCubesBackward = 1216;  // backward keeps two such tiles in LDS
+// The coarse backward keeps two R x C fp32 tiles in LDS: R = 16 cubes per
+// workgroup up to 1216 cubes, R = 8 up to kMaxCubes.
+constexpr int kCoarseBwd16Cubes = 1216;
+constexpr int kMaxCubesBackward = kMaxCubes;
 
 // Geometry of one problem, passed by value to every kernel.
 struct Geo {

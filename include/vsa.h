@@ -200,7 +200,7 @@ vsa_status vsa_forward_static(const vsa_problem* p, const void* q, const void* k
  *           NULL, meaning zero); lse [B,H,Np] and idx as written by vsa_forward.
  *   dq, dk, dv : [B,H,N,d] raster out (overwritten).
  * Deterministic: no floating-point atomics; repeated calls give the same bits.
- * Implemented for VSA_BF16 with C <= 1216 cubes; other problems return
+ * Implemented for VSA_BF16 (C <= 2048 cubes, as every entry point); other problems return
  * VSA_ERR_UNSUPPORTED before anything is enqueued. */
 vsa_status vsa_backward(const vsa_problem* p, const void* q, const void* k, const void* v,
                         const void* o_fine, const float* lse, const int32_t* idx,

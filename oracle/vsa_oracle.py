@@ -258,6 +258,68 @@ def backward(q, k, v, do_fine, do_coarse, T: int, Hh: int, Ww: int, idx: np.ndar
     return inverse_reorder(dq, g), inverse_reorder(dk, g), inverse_reorder(dv, g)
 
 
+def backward_sampled(q, k, v, do_fine, do_coarse, T: int, Hh: int, Ww: int, idx: np.ndarray,
+                     qcubes: Sequence[int], kcubes: Sequence[int]):
+    """The gradients of `backward` on a sample, for shapes too large for it.
+
+    dq is computed on the valid tokens of the query cubes `qcubes`, dk and dv
+    on those of the key cubes `kcubes`; every other element is NaN.  The
+    definitions are those of `backward`: a sampled key cube receives the
+    contributions of every query cube whose selection holds it (each such
+    query cube's softmax is taken over all of its selected keys), plus its
+    share of the coarse-stage gradient, which is computed for the whole head.
+    Returns raster (B, H, N, d) arrays.
+    """
+    g = geometry(T, Hh, Ww)
+    q, k, v, dof, doc = (np.asarray(a, dtype=np.float64) for a in (q, k, v, do_fine, do_coarse))
+    B, H, _, d = q.shape
+    scale = 1.0 / math.sqrt(d)
+    qcb, kcb, vcb, docb = reorder(q, g), reorder(k, g), reorder(v, g), reorder(dof, g)
+    qset, kset = set(int(i) for i in qcubes), set(int(j) for j in kcubes)
+    cube_rows = lambda c: np.arange(SLOTS * c, SLOTS * c + SLOTS)
+    sampled = lambda cubes: np.isin(np.arange(g["Np"]) // SLOTS, sorted(cubes)) & g["valid"]
+    qrows, krows = sampled(qset), sampled(kset)
+    dq = np.where(qrows[:, None], 0.0, np.nan) * np.ones_like(qcb)
+    dk = np.where(krows[:, None], 0.0, np.nan) * np.ones_like(kcb)
+    dv = dk.copy()
+    for b in range(B):
+        for h in range(H):
+            sel = idx[b, h]
+            for i in range(g["C"]):
+                hit = [j for j in sel[i] if int(j) in kset]
+                if i not in qset and not hit:
+                    continue
+                rows = cube_rows(i)
+                rows = rows[g["valid"][rows]]
+                keys = _key_positions(sel[i], g)
+                Q, Kk, V, dO = qcb[b, h, rows], kcb[b, h, keys], vcb[b, h, keys], docb[b, h, rows]
+                P = softmax_rows(Q @ Kk.T * scale)
+                dP = dO @ V.T
+                dS = P * (dP - (P * dP).sum(axis=1, keepdims=True))
+                if i in qset:
+                    dq[b, h, rows] += dS @ Kk * scale
+                for j in hit:
+                    cols = (keys // SLOTS) == j
+                    dk[b, h, keys[cols]] += dS[:, cols].T @ Q * scale
+                    dv[b, h, keys[cols]] += P[:, cols].T @ dO
+    # coarse stage, whole head (C x C), added on the sampled rows
+    n = g["n_valid"][:, None]
+    qp, kp, vp = pool(qcb, g), pool(kcb, g), pool(vcb, g)
+    _, pc, _ = coarse(qp, kp, vp)
+    doc_sum = pool(reorder(doc, g), g) * n
+    dvc = np.swapaxes(pc, -1, -2) @ doc_sum
+    dpc = doc_sum @ np.swapaxes(vp, -1, -2)
+    dsc = pc * (dpc - (pc * dpc).sum(axis=-1, keepdims=True))
+    dqc = dsc @ kp * scale
+    dkc = np.swapaxes(dsc, -1, -2) @ qp * scale
+    per_slot = lambda x: np.repeat(x / n, SLOTS, axis=-2)
+    dq += per_slot(dqc)
+    dk += per_slot(dkc)
+    dv += per_slot(dvc)
+    nan_raster = lambda x: np.where(np.isnan(x), np.nan, x)
+    return tuple(inverse_reorder(nan_raster(x), g) for x in (dq, dk, dv))
+
+
 # ----------------------------------------------------------------------------
 # FP8 fine stage (a design of this library, not of the pages)
 # ----------------------------------------------------------------------------

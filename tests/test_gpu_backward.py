@@ -1,5 +1,7 @@
 """GPU parity of the backward (dq, dk, dv through the fine and coarse stages,
 selection held constant) against the fp64 oracle, through the C ABI."""
+from dataclasses import replace
+
 import numpy as np
 import pytest
 import torch
@@ -28,6 +30,14 @@ EDGE = [
     # the round-by-round transpose runs; ragged last cube column
     Workload("bwd-many-cubes", B=1, H=1, T=4, Hh=96, Ww=90, d=64, dtype="bf16", topk=3,
              structure="field", alpha=0.5, backward=True),
+    # 1280 cubes: above 1216, the coarse backward takes 8 cubes per workgroup
+    # (two 8 x C score tiles in LDS); ragged edges on both spatial axes.  The
+    # per-cube offsets spread the selections (at most 12 query cubes per key
+    # cube): with the smooth field one key cube collects 53 and its dv reaches
+    # 9.7, where rounding the exact value to bf16 alone costs 0.0295 of the
+    # 0.03 bound
+    Workload("bwd-1280-cubes", B=1, H=1, T=4, Hh=126, Ww=158, d=64, dtype="bf16", topk=2,
+             structure="offset", alpha=0.5, backward=True),
 ]
 CASES = list(configs.SWEEP) + EDGE
 ids = [w.name for w in CASES]
@@ -106,3 +116,32 @@ def test_autograd_function_matches_direct_calls():
     ((of.float() * t["do_fine"].float()).sum() + (oc.float() * t["do_coarse"].float()).sum()).backward()
     for a, b in zip((q.grad, k.grad, v.grad), grads):
         assert torch.equal(a, b)
+
+
+def test_backward_wan14b_sampled():
+    """Wan-14B 720p shape (1440 cubes, top-K 144) forward and backward at full
+    size on the GPU; the oracle checks dq on 6 sampled query cubes and dk, dv
+    on 4 sampled key cubes (with every query cube that selected them) of 2
+    sampled heads, plus the whole coarse-stage gradient of those heads."""
+    w = replace(configs.WAN_14B, backward=True)
+    x = inputs.make_inputs(w, seed=0, grads=True)
+    t = {n: inputs.as_torch(a, w.dtype, DEV) for n, a in x.items()}
+    o_fine, o_coarse, idx, lse = vsa.forward(t["q"], t["k"], t["v"], grid(w), w.topk)
+    dq, dk, dv = vsa.backward(t["q"], t["k"], t["v"], o_fine, lse, idx, t["do_fine"],
+                              t["do_coarse"], grid(w))
+    torch.cuda.synchronize()
+    heads, qcubes = inputs.sample_plan(w, n_heads=2, n_qcubes=6)
+    kcubes = qcubes[:2] + qcubes[-2:]
+    hs = torch.tensor(heads, device=DEV)
+    sub = {n: x[n][:, heads] for n in x}
+    del x, t
+    gidx = idx[:, hs].cpu().numpy()
+    ref = vo.backward_sampled(sub["q"], sub["k"], sub["v"], sub["do_fine"], sub["do_coarse"],
+                              w.T, w.Hh, w.Ww, gidx, qcubes, kcubes)
+    g = vo.geometry(w.T, w.Hh, w.Ww)
+    cube = g["cube_of_token"]
+    for name, got, want, cubes in (("dq", dq, ref[0], qcubes), ("dk", dk, ref[1], kcubes),
+                                   ("dv", dv, ref[2], kcubes)):
+        toks = np.flatnonzero(np.isin(cube, cubes))
+        assert_close(got[:, hs].float().cpu().numpy()[:, :, toks], want[:, :, toks], w.dtype,
+                     f"{name} sampled")

@@ -345,3 +345,23 @@ def test_backward_all_cubes_fine_only_is_dense_attention_backward():
     (F.scaled_dot_product_attention(tq, tk, tv) * torch.from_numpy(gf)).sum().backward()
     for a, b in zip(got, (tq.grad, tk.grad, tv.grad)):
         np.testing.assert_allclose(a, b.numpy(), atol=1e-12)
+
+
+@pytest.mark.parametrize("grid,K", [((8, 8, 9), 3), ((5, 6, 7), 2)])
+def test_sampled_backward_equals_full_backward_on_its_sample(grid, K):
+    """The sampled backward (for shapes too large for the full one) gives the
+    full backward's values on the sampled cubes and NaN elsewhere."""
+    T, Hh, Ww = grid
+    g = vo.geometry(T, Hh, Ww)
+    rng = np.random.default_rng(13)
+    shape = (1, 2, T * Hh * Ww, 8)
+    q, k, v, gf, gc = (rng.standard_normal(shape) for _ in range(5))
+    idx = random_idx(rng, 2, g["C"], min(K, g["C"]))[None]
+    full = vo.backward(q, k, v, gf, gc, T, Hh, Ww, idx)
+    qcubes, kcubes = [0, g["C"] - 1], [1, g["C"] - 1]
+    got = vo.backward_sampled(q, k, v, gf, gc, T, Hh, Ww, idx, qcubes, kcubes)
+    cube = g["cube_of_token"]
+    for x, ref, cubes in zip(got, full, (qcubes, kcubes, kcubes)):
+        on = np.isin(cube, cubes)
+        np.testing.assert_allclose(x[..., on, :], ref[..., on, :], atol=1e-12)
+        assert np.all(np.isnan(x[..., ~on, :]))
