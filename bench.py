@@ -44,7 +44,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=400)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-reps", type=int, default=5)
-    ap.add_argument("--stage", choices=["all", "forward", "fine", "coarse", "reorder", "backward",
+    ap.add_argument("--stage", choices=["all", "forward", "fine", "fine_raster", "dense", "coarse",
+                                        "reorder", "backward",
                                         "fine_fp8", "forward_fp8", "quantize_fp8"],
                     default="all",
                     help="time one stage only (for profiler runs); prints a short JSON line")
@@ -120,6 +121,12 @@ def settle_clock(fn, rotate, seconds=1.0):
             return round((time.perf_counter() - t0) * 1e3, 1)
 
 
+def t_extents(w):
+    """Valid time slices (1..4) of every cube of a workload's grid, cube order."""
+    ct, ch, cw = -(-w.T // 4), -(-w.Hh // 4), -(-w.Ww // 4)
+    return [min(4, w.T - 4 * t) for t in range(ct) for _ in range(ch) for _ in range(cw)]
+
+
 def valid_counts(w):
     """Valid slots n_c of every cube of a workload's grid, cube order."""
     ct, ch, cw = -(-w.T // 4), -(-w.Hh // 4), -(-w.Ww // 4)
@@ -172,6 +179,9 @@ def per_config(args, dev):
                "fine_sparse_tflops": round(fl / (fine_ms * 1e-3) / 1e12, 2),
                "fine_useful_tflops": round(useful / (fine_ms * 1e-3) / 1e12, 2),
                "useful_over_computed": round(useful / fl, 4),
+               "executed_over_computed": round(
+                   flops.executed_fine_flops(w.B, w.H, w.topk, w.d, t_extents(w)) / fl, 4)
+               if w.dtype == "bf16" else 1.0,
                "timing": "hip graph replay"}
         del cube, obuf, plan      # the cube-order copies are not needed below
         if w.dtype == "bf16" and w.d == 128:
@@ -356,11 +366,21 @@ def stage_only(args, w, grid, sets, cube_sets, step):
         if args.stage == "fine":
             fn = lambda i: vsa.fine(cube_sets[i]["q"], cube_sets[i]["k"], cube_sets[i]["v"],
                                     idx[i], grid, out=out)
+        elif args.stage == "fine_raster":
+            ocs = [vsa.coarse(c["q"], c["k"], c["v"], grid, w.topk)[0] for c in cube_sets]
+            rout = (torch.empty_like(sets[0]["q"]), torch.empty_like(sets[0]["q"]))
+            fn = lambda i: vsa.fine_raster(sets[i]["q"], sets[i]["k"], sets[i]["v"], idx[i], grid,
+                                           oc=ocs[i], out=rout)
+        elif args.stage == "dense":
+            fn = lambda i: vsa.dense(cube_sets[i]["q"], cube_sets[i]["k"], cube_sets[i]["v"], grid,
+                                     return_lse=False, out=out)
         else:
             fn = lambda i: vsa.coarse(cube_sets[i]["q"], cube_sets[i]["k"], cube_sets[i]["v"],
                                       grid, w.topk)
     ms = timed(fn, args.steps, args.warmup, n)
-    print(json.dumps({"stage": args.stage, "ms": round(ms, 5), "steps": args.steps}), flush=True)
+    launch_ms = per_launch(fn, args.steps, 0, n)
+    print(json.dumps({"stage": args.stage, "ms": round(ms, 5), "launch_ms": round(launch_ms, 5),
+                      "steps": args.steps}), flush=True)
 
 
 def main():
@@ -397,15 +417,22 @@ def main():
     warm_ms = timed(lambda i: step(0), args.steps, args.warmup, 1)
 
     # fine kernel alone and coarse + fine on cube-order inputs
-    idx_sets = []
+    idx_sets, oc_sets = [], []
     for c in cube_sets:
-        _, idx = vsa.coarse(c["q"], c["k"], c["v"], grid, w.topk)
+        oc, idx = vsa.coarse(c["q"], c["k"], c["v"], grid, w.topk)
         idx_sets.append(idx)
+        oc_sets.append(oc)
     o_buf = torch.empty_like(cube_sets[0]["q"])
     fine_step = lambda i: vsa.fine(cube_sets[i]["q"], cube_sets[i]["k"], cube_sets[i]["v"],
                                    idx_sets[i], grid, out=o_buf)
     fine_ms = timed(fine_step, args.steps, args.warmup, N_SETS)
     fine_launch_ms = per_launch(fine_step, args.steps, args.warmup, N_SETS)
+    # the fine stage exactly as vsa_forward runs it: raster gather, raster
+    # O_fine and LSE, O_coarse broadcast (vsa_fine_raster)
+    raster_out = (torch.empty_like(sets[0]["q"]), torch.empty_like(sets[0]["q"]))
+    raster_step = lambda i: vsa.fine_raster(sets[i]["q"], sets[i]["k"], sets[i]["v"], idx_sets[i],
+                                            grid, oc=oc_sets[i], out=raster_out)
+    raster_launch_ms = per_launch(raster_step, args.steps, args.warmup, N_SETS)
 
     def coarse_fine(i):
         c = cube_sets[i]
@@ -451,7 +478,10 @@ def main():
     fl_dense = flops.fine_forward_flops(w.B, w.H, w.C, w.C, w.d)
     fine_tflops = fl / (fine_ms * 1e-3) / 1e12
     launch_tflops = fl / (fine_launch_ms * 1e-3) / 1e12
+    raster_tflops = fl / (raster_launch_ms * 1e-3) / 1e12
     traffic = traffic_record("block_sparse_attention_cube_amd/csrc/fine_fwd.hip")
+    raster_traffic = traffic_record("block_sparse_attention_cube_amd/csrc/fine_fwd.hip",
+                                    "fine_fwd_raster_wan1.3b_traffic.json")
     fwd_tflops = fl / (ms * 1e-3) / 1e12
 
     result = {
@@ -496,11 +526,21 @@ def main():
         "fp8": fp8,
         "sweep": sweep,
         "fine_launch_ms": round(fine_launch_ms, 5),
-        "roofline": {"bound": "mfma", "kernel": "fine_fwd_bf16_kernel<128,false> (vsa_fine)",
-                     "achieved": round(launch_tflops, 2), "peak": flops.PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(launch_tflops / flops.PEAK_BF16_TFLOPS, 4),
-                     "traffic": traffic,
-                     "flops_per_launch": fl, "launch_ms": round(fine_launch_ms, 5)},
+        "fine_raster_launch_ms": round(raster_launch_ms, 5),
+        "roofline": {"bound": "mfma",
+                     "kernel": "fine_fwd_bf16_kernel<128,true> (vsa_fine_raster: the fine stage "
+                               "of vsa_forward)",
+                     "achieved": round(raster_tflops, 2), "peak": flops.PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(raster_tflops / flops.PEAK_BF16_TFLOPS, 4),
+                     "traffic": raster_traffic,
+                     "flops_per_launch": fl, "launch_ms": round(raster_launch_ms, 5)},
+        "roofline_cube_order": {"bound": "mfma",
+                                "kernel": "fine_fwd_bf16_kernel<128,false> (vsa_fine)",
+                                "achieved": round(launch_tflops, 2),
+                                "peak": flops.PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                                "frac": round(launch_tflops / flops.PEAK_BF16_TFLOPS, 4),
+                                "traffic": traffic, "flops_per_launch": fl,
+                                "launch_ms": round(fine_launch_ms, 5)},
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, host_sets[0], args.cpu_reps)

@@ -28,7 +28,7 @@ VSA_OP_FINE = 3
 VSA_OP_FORWARD_FP8 = 4
 
 EXPORTS = ("vsa_workspace_bytes", "vsa_check_problem", "vsa_reorder", "vsa_coarse",
-           "vsa_fine", "vsa_dense", "vsa_forward", "vsa_forward_static", "vsa_backward", "vsa_quantize_fp8", "vsa_fine_fp8",
+           "vsa_fine", "vsa_fine_raster", "vsa_dense", "vsa_forward", "vsa_forward_static", "vsa_backward", "vsa_quantize_fp8", "vsa_fine_fp8",
            "vsa_forward_fp8", "vsa_status_string")
 
 
@@ -56,6 +56,7 @@ _SIG = {
     "vsa_reorder": (ctypes.c_int, [_P, _V, _V, ctypes.c_int, _V]),
     "vsa_coarse": (ctypes.c_int, [_P, _V, _V, _V, _V, _V, _V, _V, ctypes.c_size_t, _V]),
     "vsa_fine": (ctypes.c_int, [_P, _V, _V, _V, _V, _V, _V, _V, ctypes.c_size_t, _V]),
+    "vsa_fine_raster": (ctypes.c_int, [_P, _V, _V, _V, _V, _V, _V, _V, _V, _V]),
     "vsa_dense": (ctypes.c_int, [_P, _V, _V, _V, _V, _V, _V]),
     "vsa_forward": (ctypes.c_int, [_P, _V, _V, _V, _V, _V, _V, _V, _V, ctypes.c_size_t, _V]),
     "vsa_forward_static": (ctypes.c_int, [_P, _V, _V, _V, _V, _V, _V, _V, _V]),

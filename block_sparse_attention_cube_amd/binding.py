@@ -155,6 +155,33 @@ def fine(qcube: torch.Tensor, kcube: torch.Tensor, vcube: torch.Tensor, idx: tor
     return o, lse
 
 
+def fine_raster(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, idx: torch.Tensor, grid: Grid,
+                oc: Optional[torch.Tensor] = None, return_lse: bool = True, out=None):
+    """The fine stage of the forward on raster tensors (bf16): returns
+    (o_fine [B,H,N,d], lse [B,H,Np] or None, o_coarse [B,H,N,d] or None); with
+    oc (per-cube [B,H,C,d]) each valid token also receives its cube's row in
+    o_coarse.  out: optional preallocated (o_fine, o_coarse)."""
+    B, H, N, d = _raster_inputs(q, k, v, grid)
+    C, Np = cube_counts(grid)
+    _device_tensor(idx, "idx")
+    if idx.dtype != torch.int32 or idx.dim() != 4 or tuple(idx.shape[:3]) != (B, H, C):
+        raise ValueError(f"idx must be int32 [B,H,C,K], got {idx.dtype} {tuple(idx.shape)}")
+    prob = make_problem(B, H, grid, d, idx.shape[3], q.dtype)
+    dev = q.device
+    o, o_coarse = out if out is not None else (torch.empty_like(q),
+                                               torch.empty_like(q) if oc is not None else None)
+    _expect(o, q.shape, q.dtype, "o_fine")
+    if oc is not None:
+        _expect(oc, (B, H, C, d), q.dtype, "oc")
+        _expect(o_coarse, q.shape, q.dtype, "o_coarse")
+    lse = torch.empty((B, H, Np), dtype=torch.float32, device=dev) if return_lse else None
+    L.check(L.lib().vsa_fine_raster(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(idx),
+                                    _ptr(o), _ptr(lse), _ptr(oc),
+                                    _ptr(o_coarse if oc is not None else None), _stream(dev)),
+            "vsa_fine_raster")
+    return o, lse, (o_coarse if oc is not None else None)
+
+
 def dense(qcube: torch.Tensor, kcube: torch.Tensor, vcube: torch.Tensor, grid: Grid,
           return_lse: bool = True, out: Optional[torch.Tensor] = None):
     """Dense attention over every cube (cube order, bf16): (o [B,H,Np,d], lse [B,H,Np])."""

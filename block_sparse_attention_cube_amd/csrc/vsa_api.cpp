@@ -310,6 +310,18 @@ vsa_status vsa_fine(const vsa_problem* p, const void* qcube, const void* kcube,
                                    /*raster=*/false, nullptr, nullptr, stream));
 }
 
+vsa_status vsa_fine_raster(const vsa_problem* p, const void* q, const void* k, const void* v,
+                           const int32_t* idx, void* o_fine, float* lse, const void* oc,
+                           void* o_coarse, hipStream_t stream) {
+  vsa_status st = check(p);
+  if (st != VSA_OK) return st;
+  if (p->dtype != VSA_BF16) return VSA_ERR_UNSUPPORTED;
+  if ((oc == nullptr) != (o_coarse == nullptr)) return VSA_ERR_NULL;
+  if ((st = pointers({q, k, v, idx, o_fine}, {lse, oc, o_coarse})) != VSA_OK) return st;
+  return launched(vsa::launch_fine(geometry(p), p->dtype, q, k, v, idx, o_fine, lse,
+                                   /*raster=*/true, oc, o_coarse, stream));
+}
+
 vsa_status vsa_dense(const vsa_problem* p, const void* qcube, const void* kcube,
                      const void* vcube, void* o, float* lse, hipStream_t stream) {
   vsa_status st = check(p);

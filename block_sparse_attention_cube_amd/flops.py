@@ -45,6 +45,16 @@ def useful_fine_flops(B: int, H: int, d: int, n_valid: Sequence[int], idx) -> in
     return int(4 * d * (per_row * n[None, None, :]).sum())
 
 
+def executed_fine_flops(B: int, H: int, K: int, d: int, t_extent: Sequence[int]) -> int:
+    """FLOPs the bf16 fine kernel executes: each query cube's four 16-row
+    waves hold time slices 0..3, and a wave whose slice lies past the cube's
+    t extent (t_extent[c], 1..4) computes nothing, so a cube costs
+    min(t_extent, 4) / 4 of its 64x64-block FLOPs."""
+    import numpy as np
+    nt = np.minimum(np.asarray(t_extent, dtype=np.int64), 4)
+    return int(4 * d * BLOCK * BLOCK * B * H * K * nt.sum() // 4)
+
+
 def reorder_bytes(B: int, H: int, N: int, Np: int, d: int, elem: int, tensors: int = 3) -> int:
     """HBM bytes of the raster -> cube reorder: read N rows, write Np rows."""
     return tensors * B * H * (N + Np) * d * elem

@@ -139,6 +139,22 @@ vsa_status vsa_fine(const vsa_problem* p, const void* qcube, const void* kcube,
                     const void* vcube, const int32_t* idx, void* o_fine, float* lse,
                     void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* The fine stage of vsa_forward on its own: raster q, k, v in, raster
+ * outputs (the fine block-sparse kernel of the results section with the
+ * cube gather and its inverse fused in).
+ *   q, k, v       : [B,H,N,d] raster; each key cube is gathered straight
+ *                   from its raster rows (bf16; fp32 returns
+ *                   VSA_ERR_UNSUPPORTED).
+ *   idx           : [B,H,C,topk] int32, each in [0, C), distinct per row.
+ *   o_fine        : [B,H,N,d] out, raster.
+ *   lse           : [B,H,Np] fp32 out in cube order, or NULL.
+ *   oc, o_coarse  : optional pair (both NULL or both set): oc is a per-cube
+ *                   [B,H,C,d] row (vsa_coarse's O_coarse) that is written to
+ *                   every valid token of its cube in o_coarse [B,H,N,d]. */
+vsa_status vsa_fine_raster(const vsa_problem* p, const void* q, const void* k, const void* v,
+                           const int32_t* idx, void* o_fine, float* lse, const void* oc,
+                           void* o_coarse, hipStream_t stream);
+
 /* Dense attention: the full softmax attention that the fine stage replaces,
  * over every cube of the grid (the FastWan re-post's results section quotes
  * the fine kernel's speed-up over FlashAttention-3 on the same sequence).

@@ -94,3 +94,22 @@ def test_sample_plan_covers_the_corner_cube():
     heads, qcubes = inputs.sample_plan(configs.WAN_14B)
     assert len(set(heads)) == 4 and len(qcubes) == 16
     assert 0 in qcubes and configs.WAN_14B.C - 1 in qcubes
+
+
+def test_executed_flops_skip_query_waves_past_the_t_extent():
+    # Wan-1.3B: T = 16, every cube four time slices deep -> all block FLOPs run
+    w = configs.WAN_1_3B
+    nt = [min(4, w.T - 4 * t) for t in range(-(-w.T // 4)) for _ in range(w.C // (-(-w.T // 4)))]
+    assert flops.executed_fine_flops(1, 12, 14, 128, nt) == flops.fine_forward_flops(1, 12, 112, 14, 128)
+    # Wan-14B: T = 21, the last of 6 cube layers holds one time slice -> 1 of 4 waves
+    w = configs.WAN_14B
+    layers = -(-w.T // 4)
+    per_layer = w.C // layers
+    nt = [min(4, w.T - 4 * t) for t in range(layers) for _ in range(per_layer)]
+    assert nt.count(1) == 240
+    got = flops.executed_fine_flops(1, 40, 144, 128, nt)
+    full = flops.fine_forward_flops(1, 40, 1440, 144, 128)
+    assert got * 8 == full * 7          # (1200 + 240/4) / 1440 = 7/8
+    # brute force over cubes and waves
+    brute = sum(4 * 128 * 16 * 64 * 144 * 40 for c in range(w.C) for wave in range(4) if wave < nt[c])
+    assert got == brute

@@ -208,3 +208,26 @@ def test_forward_wan14b_sampled():
     assert_close(host(o_coarse[:, hs]), ref["o_coarse"], w.dtype, "O_coarse sampled heads")
     assert_close(lse[:, hs].cpu().numpy()[..., pos, None], ref_g["lse_cube"][..., pos, None],
                  w.dtype, "LSE sampled")
+
+
+@pytest.mark.parametrize("w", CASES, ids=ids(CASES))
+def test_fine_raster_is_the_forward_fine_stage(w, cache):
+    """vsa_fine_raster on the forward's own selection gives the forward's
+    O_fine bit for bit (same kernel) and, with the per-cube coarse rows,
+    O_coarse broadcast to every valid token; fp32 problems are refused."""
+    x, (q, k, v), (qc, kc, vc), ref = case_data(w, cache)
+    o_fine, o_coarse, idx, lse = vsa.forward(q, k, v, grid(w), w.topk)
+    oc, _ = vsa.coarse(qc, kc, vc, grid(w), w.topk)
+    if w.dtype == "f32":
+        with pytest.raises(vsa.VSAError):
+            vsa.fine_raster(q, k, v, idx, grid(w), oc=oc)
+        return
+    of, lse2, ocr = vsa.fine_raster(q, k, v, idx, grid(w), oc=oc)
+    torch.cuda.synchronize()
+    assert torch.equal(of, o_fine)
+    g = ref["geometry"]
+    valid = torch.from_numpy(g["valid"]).to(DEV)
+    assert torch.equal(lse2[..., valid], lse[..., valid])
+    assert_close(host(ocr), ref["o_coarse"], w.dtype, "O_coarse broadcast")
+    of_only, _, none = vsa.fine_raster(q, k, v, idx, grid(w), return_lse=False)
+    assert none is None and torch.equal(of_only, o_fine)
