@@ -26,9 +26,12 @@ VSA_OP_BACKWARD = 1
 VSA_OP_COARSE = 2
 VSA_OP_FINE = 3
 VSA_OP_FORWARD_FP8 = 4
+VSA_OP_FORWARD_CUBE = 5
+VSA_OP_BACKWARD_CUBE = 6
 
 EXPORTS = ("vsa_workspace_bytes", "vsa_check_problem", "vsa_reorder", "vsa_coarse",
-           "vsa_fine", "vsa_fine_raster", "vsa_dense", "vsa_forward", "vsa_forward_static", "vsa_backward", "vsa_quantize_fp8", "vsa_fine_fp8",
+           "vsa_fine", "vsa_fine_raster", "vsa_dense", "vsa_forward", "vsa_forward_static",
+           "vsa_forward_cube", "vsa_backward_cube", "vsa_backward", "vsa_quantize_fp8", "vsa_fine_fp8",
            "vsa_forward_fp8", "vsa_status_string")
 
 
@@ -60,6 +63,9 @@ _SIG = {
     "vsa_dense": (ctypes.c_int, [_P, _V, _V, _V, _V, _V, _V]),
     "vsa_forward": (ctypes.c_int, [_P, _V, _V, _V, _V, _V, _V, _V, _V, ctypes.c_size_t, _V]),
     "vsa_forward_static": (ctypes.c_int, [_P, _V, _V, _V, _V, _V, _V, _V, _V]),
+    "vsa_forward_cube": (ctypes.c_int, [_P, _V, _V, _V, _V, _V, _V, _V, _V, ctypes.c_size_t, _V]),
+    "vsa_backward_cube": (ctypes.c_int, [_P, _V, _V, _V, _V, _V, _V, _V, _V, _V, _V, _V, _V,
+                                         ctypes.c_size_t, _V]),
     "vsa_backward": (ctypes.c_int, [_P, _V, _V, _V, _V, _V, _V, _V, _V, _V, _V, _V, _V,
                                     ctypes.c_size_t, _V]),
     "vsa_quantize_fp8": (ctypes.c_int, [_P, _V, _V, _V, _V, _V, _V, _V, _V]),

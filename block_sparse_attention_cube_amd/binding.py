@@ -321,6 +321,60 @@ def backward(q, k, v, o_fine, lse, idx, do_fine, do_coarse, grid: Grid):
     return dq, dk, dv
 
 
+def _cube_inputs(qcube, kcube, vcube, grid):
+    _device_tensor(qcube, "qcube")
+    B, H, Np_in, d = qcube.shape
+    C, Np = cube_counts(grid)
+    if Np_in != Np:
+        raise ValueError(f"qcube has {Np_in} rows, expected {Np}")
+    _expect(kcube, qcube.shape, qcube.dtype, "kcube")
+    _expect(vcube, qcube.shape, qcube.dtype, "vcube")
+    return B, H, C, Np, d
+
+
+def forward_cube(qcube: torch.Tensor, kcube: torch.Tensor, vcube: torch.Tensor, grid: Grid,
+                 topk: int, return_lse: bool = True):
+    """Whole forward on cube-order tensors: (o_fine [B,H,Np,d] cube order,
+    o_coarse [B,H,C,d] per cube, idx [B,H,C,K], lse [B,H,Np])."""
+    B, H, C, Np, d = _cube_inputs(qcube, kcube, vcube, grid)
+    prob = make_problem(B, H, grid, d, topk, qcube.dtype)
+    L.check(L.lib().vsa_check_problem(ctypes.byref(prob)), "vsa_forward_cube")
+    dev = qcube.device
+    o = torch.empty_like(qcube)
+    oc = torch.empty((B, H, C, d), dtype=qcube.dtype, device=dev)
+    idx = torch.empty((B, H, C, topk), dtype=torch.int32, device=dev)
+    lse = torch.empty((B, H, Np), dtype=torch.float32, device=dev) if return_lse else None
+    ws, nws = _workspace(prob, L.VSA_OP_FORWARD_CUBE, dev)
+    L.check(L.lib().vsa_forward_cube(ctypes.byref(prob), _ptr(qcube), _ptr(kcube), _ptr(vcube),
+                                     _ptr(o), _ptr(oc), _ptr(idx), _ptr(lse), _ptr(ws), nws,
+                                     _stream(dev)), "vsa_forward_cube")
+    return o, oc, idx, lse
+
+
+def backward_cube(qcube, kcube, vcube, o_fine, lse, idx, do_fine, do_coarse, grid: Grid):
+    """Gradients (dq, dk, dv) in cube order of sum(o_fine*do_fine) +
+    sum(o_coarse*do_coarse) for the outputs of forward_cube (do_coarse per
+    cube [B,H,C,d] or None)."""
+    B, H, C, Np, d = _cube_inputs(qcube, kcube, vcube, grid)
+    _expect(o_fine, qcube.shape, qcube.dtype, "o_fine")
+    _expect(do_fine, qcube.shape, qcube.dtype, "do_fine")
+    if do_coarse is not None:
+        _expect(do_coarse, (B, H, C, d), qcube.dtype, "do_coarse")
+    _expect(lse, (B, H, Np), torch.float32, "lse")
+    _device_tensor(idx, "idx")
+    if idx.dtype != torch.int32 or tuple(idx.shape[:3]) != (B, H, C):
+        raise ValueError("idx must be int32 [B,H,C,K]")
+    prob = make_problem(B, H, grid, d, idx.shape[3], qcube.dtype)
+    dev = qcube.device
+    dq, dk, dv = (torch.empty_like(qcube) for _ in range(3))
+    ws, nws = _workspace(prob, L.VSA_OP_BACKWARD_CUBE, dev)
+    L.check(L.lib().vsa_backward_cube(ctypes.byref(prob), _ptr(qcube), _ptr(kcube), _ptr(vcube),
+                                      _ptr(o_fine), _ptr(lse), _ptr(idx), _ptr(do_fine),
+                                      _ptr(do_coarse), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(ws),
+                                      nws, _stream(dev)), "vsa_backward_cube")
+    return dq, dk, dv
+
+
 def quantize_fp8(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, grid: Grid):
     """E4M3 copies of bf16 raster q, k, v (d = 128) for fine_fp8.
 

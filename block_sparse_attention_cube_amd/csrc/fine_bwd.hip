@@ -151,7 +151,9 @@ __device__ __forceinline__ u32x4 tok_read(const uint16_t* t, int tro, int s) {
 // cube through LDS, adding an fp32 per-cube row `extra` (scaled by inv_n).
 // get(row, d) is evaluated by the owning lane; here the caller has already
 // written bf16 rows into `stage` ([64][D+8]).
-template <int D>
+// RASTER: the cube's valid rows go to their raster rows; otherwise all 64
+// cube-order rows are written, zeros on pad slots.
+template <int D, bool RASTER>
 __device__ __forceinline__ void write_cube_rows(const uint16_t* stage, uint16_t* __restrict__ out,
                                                 const Geo& g, int64_t bh, int c, int tid) {
   constexpr int kKC = D / 8, kOS = D + 8, kOutReg = 64 * kKC / 256;
@@ -160,9 +162,16 @@ __device__ __forceinline__ void write_cube_rows(const uint16_t* stage, uint16_t*
   for (int u = 0; u < kOutReg; ++u) {
     const int ch = tid + 256 * u, row = ch / kKC, cc = ch % kKC;
     const int64_t tok = slot_token(g, e, row);
-    if (tok >= 0)
-      *reinterpret_cast<u32x4*>(out + (bh * g.N + tok) * D + 8 * cc) =
-          *reinterpret_cast<const u32x4*>(stage + row * kOS + 8 * cc);
+    if (RASTER) {
+      if (tok >= 0)
+        *reinterpret_cast<u32x4*>(out + (bh * g.N + tok) * D + 8 * cc) =
+            *reinterpret_cast<const u32x4*>(stage + row * kOS + 8 * cc);
+    } else {
+      const u32x4 val = tok >= 0 ? *reinterpret_cast<const u32x4*>(stage + row * kOS + 8 * cc)
+                                 : u32x4{0u, 0u, 0u, 0u};
+      *reinterpret_cast<u32x4*>(out + (bh * g.Np + static_cast<int64_t>(c) * kSlots + row) * D +
+                                8 * cc) = val;
+    }
   }
 }
 
@@ -174,7 +183,9 @@ __device__ __forceinline__ void write_cube_rows(const uint16_t* stage, uint16_t*
 // Eight workgroups per CU: the C x B*H grid fits one round for the shapes
 // of the pages.  Each tensor is summed in its own phase (four loads in
 // flight per thread) so that the accumulators stay within 64 VGPRs.
-template <int D, bool COARSE>
+// RASTER = false: q, k, v, dO, O are cube order and dO_coarse is one row per
+// cube (the gradient of a per-cube O_coarse), taken as the cube's sum as is.
+template <int D, bool COARSE, bool RASTER>
 __global__ __launch_bounds__(256, 8) void bwd_prep_kernel(BwdPrepArgs a, Geo g) {
   constexpr int kCpr = D / 8;                  // 16-byte chunks per row
   constexpr int kRowsPerPass = 256 / kCpr;
@@ -183,11 +194,12 @@ __global__ __launch_bounds__(256, 8) void bwd_prep_kernel(BwdPrepArgs a, Geo g) 
   const int64_t bh = blockIdx.y;
   const CubeExt e = cube_extent(g, c);
   const int tid = threadIdx.x, chunk = tid % kCpr, row0 = tid / kCpr;
-  int64_t rrow[kPasses];   // raster row of each pass's slot, -1 for a pad slot
+  int64_t rrow[kPasses];   // input row of each pass's slot, -1 for a pad slot
 #pragma unroll
   for (int u = 0; u < kPasses; ++u) {
-    const int64_t r = slot_token(g, e, row0 + u * kRowsPerPass);
-    rrow[u] = r >= 0 ? bh * g.N + r : -1;
+    const int slot = row0 + u * kRowsPerPass;
+    const int64_t r = slot_token(g, e, slot);
+    rrow[u] = r < 0 ? -1 : RASTER ? bh * g.N + r : bh * g.Np + static_cast<int64_t>(c) * kSlots + slot;
   }
   auto load = [&](const uint16_t* x, int u) {
     return rrow[u] >= 0 ? *reinterpret_cast<const u32x4*>(x + rrow[u] * D + chunk * 8)
@@ -223,10 +235,11 @@ __global__ __launch_bounds__(256, 8) void bwd_prep_kernel(BwdPrepArgs a, Geo g) 
     // shuffles (lanes l, l + kCpr, ... hold the same chunk), the four waves
     // in LDS.
     const int lane = tid & 63, wave = tid >> 6;
-    __shared__ float red[4][4][D];   // [wave][tensor][dim]
+    constexpr int kSums = RASTER ? 4 : 3;   // q, k, v (and dO_coarse per token)
+    __shared__ float red[4][kSums][D];       // [wave][tensor][dim]
     const uint16_t* const src[4] = {a.q, a.k, a.v, a.doc};
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
+    for (int t = 0; t < kSums; ++t) {
       u32x4 val[kPasses];
 #pragma unroll
       for (int u = 0; u < kPasses; ++u) val[u] = load(src[t], u);
@@ -253,15 +266,16 @@ __global__ __launch_bounds__(256, 8) void bwd_prep_kernel(BwdPrepArgs a, Geo g) 
     __syncthreads();
     if (tid < D) {
       const float inv_n = 1.f / static_cast<float>(e.nt * e.nh * e.nw);
-      float sum[4];
+      float sum[kSums];
 #pragma unroll
-      for (int t = 0; t < 4; ++t)
+      for (int t = 0; t < kSums; ++t)
         sum[t] = (red[0][t][tid] + red[1][t][tid]) + (red[2][t][tid] + red[3][t][tid]);
       const int64_t m = (bh * g.C + c) * D + tid;
       a.qm[m] = sum[0] * inv_n;
       a.km[m] = sum[1] * inv_n;
       a.vm[m] = sum[2] * inv_n;
-      a.docs[m] = sum[3];
+      if constexpr (RASTER) a.docs[m] = sum[3];
+      else a.docs[m] = __uint_as_float(static_cast<uint32_t>(a.doc[m]) << 16);
     }
   }
 }
@@ -355,7 +369,7 @@ __global__ __launch_bounds__(256) void idx_transpose_kernel(const int32_t* __res
 // Pad key slots get P = 0 as in the forward: a -inf accumulator init for the
 // (ih, iw) part, a -inf exp2 offset for key tiles past the cube's t extent,
 // extents read per step from a per-lane table.
-template <int D>
+template <int D, bool RASTER>
 __global__ __launch_bounds__(256, 2) void fine_bwd_dq_kernel(BwdFineArgs a, Geo g) {
   using Tl = BwdTile<D>;
   constexpr int kKS = D / 32, kDT = D / 16, kOS = D + 8, kT = Tl::kElems;
@@ -377,7 +391,7 @@ __global__ __launch_bounds__(256, 2) void fine_bwd_dq_kernel(BwdFineArgs a, Geo 
   const int qslot = 16 * (li >> 2) + 4 * wave + (li & 3);
   const bool active = wave < eq.nh;   // wave-uniform
   const int64_t qrow = bh * g.Np + static_cast<int64_t>(qc) * 64 + qslot;   // cube-order stats
-  const int64_t head0 = bh * g.N * D;   // raster q, k, v, dO of this head
+  const int64_t head0 = bh * (RASTER ? g.N : g.Np) * D;   // q, k, v, dO rows of this head
 
   // DMA byte offsets (from a key cube's first raster row) of this thread's
   // chunks; alt: the same chunk of the first row, for pad slots
@@ -389,9 +403,9 @@ __global__ __launch_bounds__(256, 2) void fine_bwd_dq_kernel(BwdFineArgs a, Geo 
     int it, ih, iw;
     dma_slot<D>(u, wave, lane, it, ih, iw);
     alt[u] = static_cast<uint32_t>(row_offset<D>(r, P % Tl::kKC) - r * D) * 2u;
-    off[u] = static_cast<uint32_t>(slot_row<true>(g, it, ih, iw) * D) * 2u + alt[u];
+    off[u] = static_cast<uint32_t>(slot_row<RASTER>(g, it, ih, iw) * D) * 2u + alt[u];
   }
-  const uint32_t head_bytes = static_cast<uint32_t>(g.N * D * 2);
+  const uint32_t head_bytes = static_cast<uint32_t>((RASTER ? g.N : g.Np) * D * 2);
   const __amdgpu_buffer_rsrc_t krs = head_rsrc(a.k + head0, head_bytes);
   const __amdgpu_buffer_rsrc_t vrs = head_rsrc(a.v + head0, head_bytes);
   int rro[kKS], tro[kDT];
@@ -404,7 +418,7 @@ __global__ __launch_bounds__(256, 2) void fine_bwd_dq_kernel(BwdFineArgs a, Geo 
   {
     const int it = li >> 2, ih = wave, iw = li & 3;
     const bool valid = it < eq.nt && ih < eq.nh && iw < eq.nw;   // pad rows: P = 0 via lse2
-    const int64_t row = cube_row<true>(g, eq, qc) + (valid ? slot_row<true>(g, it, ih, iw) : 0);
+    const int64_t row = cube_row<RASTER>(g, eq, qc) + (valid ? slot_row<RASTER>(g, it, ih, iw) : 0);
 #pragma unroll
     for (int ks = 0; ks < kKS; ++ks) {
       qf[ks] = *reinterpret_cast<const u32x4*>(a.q + head0 + row * D + 32 * ks + 8 * lg);
@@ -424,7 +438,7 @@ __global__ __launch_bounds__(256, 2) void fine_bwd_dq_kernel(BwdFineArgs a, Geo 
     if (m < K) {
       const CubeExt e = cube_extent(g, sel[m]);
       ext_lanes = e.nt | (e.nh << 3) | (e.nw << 6);
-      row_lanes = cube_row<true>(g, e, sel[m]);
+      row_lanes = cube_row<RASTER>(g, e, sel[m]);
     }
   };
   keys(0);
@@ -440,7 +454,7 @@ __global__ __launch_bounds__(256, 2) void fine_bwd_dq_kernel(BwdFineArgs a, Geo 
   auto stage = [&](int n, uint16_t* slot) {
     const int ext = __builtin_amdgcn_readlane(ext_lanes, n & 63);
     const uint32_t row_bytes = static_cast<uint32_t>(__builtin_amdgcn_readlane(row_lanes, n & 63)) * (D * 2);
-    if (ext == kFull) {
+    if (!RASTER || ext == kFull) {
       dma_rows<D>(krs, row_bytes, off, slot, wave);
       dma_rows<D>(vrs, row_bytes, off, slot + kT, wave);
     } else {
@@ -545,7 +559,7 @@ __global__ __launch_bounds__(256, 2) void fine_bwd_dq_kernel(BwdFineArgs a, Geo 
     if (active) *reinterpret_cast<u32x2*>(stage_o + qslot * kOS + 16 * dt + 4 * lg) = w;
   }
   __syncthreads();
-  write_cube_rows<D>(stage_o, a.dq, g, bh, qc, tid);
+  write_cube_rows<D, RASTER>(stage_o, a.dq, g, bh, qc, tid);
 }
 
 // ---------------------------------------------------------------------------
@@ -554,7 +568,7 @@ __global__ __launch_bounds__(256, 2) void fine_bwd_dq_kernel(BwdFineArgs a, Geo 
 // and dO tiles and its 64 lse2 / delta values go straight into a 2-slot LDS
 // ring by DMA; Q^T and dO^T come from transposed reads.  Pad query slots
 // have lse2 = +inf (P = 0) and zero dO rows, so they add nothing.
-template <int D>
+template <int D, bool RASTER>
 __global__ __launch_bounds__(256, 2) void fine_bwd_dkdv_kernel(BwdFineArgs a, Geo g) {
   using Tl = BwdTile<D>;
   constexpr int kKS = D / 32, kDT = D / 16, kOS = D + 8, kT = Tl::kElems;
@@ -570,7 +584,7 @@ __global__ __launch_bounds__(256, 2) void fine_bwd_dkdv_kernel(BwdFineArgs a, Ge
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int li = lane & 15, lg = lane >> 4;
   const float c2 = inv_sqrt_d<D>() * kLog2e;
-  const int64_t head0 = bh * g.N * D;   // raster q, k, v, dO of this head
+  const int64_t head0 = bh * (RASTER ? g.N : g.Np) * D;   // q, k, v, dO rows of this head
   const int64_t stat0 = bh * g.Np;      // cube-order lse2 / delta of this head
 
   // DMA byte offsets (from a query cube's first raster row) of this
@@ -583,9 +597,9 @@ __global__ __launch_bounds__(256, 2) void fine_bwd_dkdv_kernel(BwdFineArgs a, Ge
     int it, ih, iw;
     dma_slot<D>(u, wave, lane, it, ih, iw);
     alt[u] = static_cast<uint32_t>(row_offset<D>(r, P % Tl::kKC) - r * D) * 2u;
-    off[u] = static_cast<uint32_t>(slot_row<true>(g, it, ih, iw) * D) * 2u + alt[u];
+    off[u] = static_cast<uint32_t>(slot_row<RASTER>(g, it, ih, iw) * D) * 2u + alt[u];
   }
-  const uint32_t head_bytes = static_cast<uint32_t>(g.N * D * 2);
+  const uint32_t head_bytes = static_cast<uint32_t>((RASTER ? g.N : g.Np) * D * 2);
   const __amdgpu_buffer_rsrc_t qrs = head_rsrc(a.q + head0, head_bytes);
   const __amdgpu_buffer_rsrc_t ors = head_rsrc(a.dof + head0, head_bytes);
   const uint32_t stat_bytes = static_cast<uint32_t>(g.Np * 4);
@@ -603,7 +617,7 @@ __global__ __launch_bounds__(256, 2) void fine_bwd_dkdv_kernel(BwdFineArgs a, Ge
     const CubeExt ek = cube_extent(g, kc);
     const int it = wave, ih = li >> 2, iw = li & 3;
     const bool valid = it < ek.nt && ih < ek.nh && iw < ek.nw;   // pad key rows are not written
-    const int64_t row = cube_row<true>(g, ek, kc) + (valid ? slot_row<true>(g, it, ih, iw) : 0);
+    const int64_t row = cube_row<RASTER>(g, ek, kc) + (valid ? slot_row<RASTER>(g, it, ih, iw) : 0);
 #pragma unroll
     for (int ks = 0; ks < kKS; ++ks) {
       kf[ks] = *reinterpret_cast<const u32x4*>(a.k + head0 + row * D + 32 * ks + 8 * lg);
@@ -634,7 +648,7 @@ __global__ __launch_bounds__(256, 2) void fine_bwd_dkdv_kernel(BwdFineArgs a, Ge
       const int c = lst[m];
       const CubeExt e = cube_extent(g, c);
       ext_lanes = e.nt | (e.nh << 3) | (e.nw << 6);
-      row_lanes = cube_row<true>(g, e, c);
+      row_lanes = cube_row<RASTER>(g, e, c);
       cube_lanes = c;
     }
   };
@@ -644,7 +658,7 @@ __global__ __launch_bounds__(256, 2) void fine_bwd_dkdv_kernel(BwdFineArgs a, Ge
     const int ext = __builtin_amdgcn_readlane(ext_lanes, i & 63);
     const uint32_t row_bytes = static_cast<uint32_t>(__builtin_amdgcn_readlane(row_lanes, i & 63)) * (D * 2);
     uint16_t* const dst = smem + slot * 2 * kT;
-    if (ext == kFull) {
+    if (!RASTER || ext == kFull) {
       dma_rows<D>(qrs, row_bytes, off, dst, wave);
       dma_rows<D>(ors, row_bytes, off, dst + kT, wave);
     } else {
@@ -768,19 +782,36 @@ __global__ __launch_bounds__(256, 2) void fine_bwd_dkdv_kernel(BwdFineArgs a, Ge
     }
   }
   __syncthreads();
-  write_cube_rows<D>(stage_k, a.dk, g, bh, kc, tid);
-  write_cube_rows<D>(stage_v, a.dv, g, bh, kc, tid);
+  write_cube_rows<D, RASTER>(stage_k, a.dk, g, bh, kc, tid);
+  write_cube_rows<D, RASTER>(stage_v, a.dv, g, bh, kc, tid);
 }
 
 }  // namespace
 
-hipError_t launch_bwd_prep(const Geo& g, const BwdPrepArgs& a, hipStream_t s) {
+namespace {
+template <bool RASTER>
+hipError_t launch_prep_layout(const Geo& g, const BwdPrepArgs& a, hipStream_t s) {
   const dim3 grid(g.C, g.B * g.H), block(256);
   if (a.doc != nullptr)
-    return g.D == 128 ? launch_kernel(bwd_prep_kernel<128, true>, grid, block, 0, s, a, g)
-                      : launch_kernel(bwd_prep_kernel<64, true>, grid, block, 0, s, a, g);
-  return g.D == 128 ? launch_kernel(bwd_prep_kernel<128, false>, grid, block, 0, s, a, g)
-                    : launch_kernel(bwd_prep_kernel<64, false>, grid, block, 0, s, a, g);
+    return g.D == 128 ? launch_kernel(bwd_prep_kernel<128, true, RASTER>, grid, block, 0, s, a, g)
+                      : launch_kernel(bwd_prep_kernel<64, true, RASTER>, grid, block, 0, s, a, g);
+  return g.D == 128 ? launch_kernel(bwd_prep_kernel<128, false, RASTER>, grid, block, 0, s, a, g)
+                    : launch_kernel(bwd_prep_kernel<64, false, RASTER>, grid, block, 0, s, a, g);
+}
+template <bool RASTER>
+hipError_t launch_fine_layout(const Geo& g, const BwdFineArgs& a, hipStream_t s) {
+  const dim3 grid(g.B * g.H * g.C), block(256);
+  hipError_t e = g.D == 128
+                     ? launch_kernel(fine_bwd_dq_kernel<128, RASTER>, grid, block, 0, s, a, g)
+                     : launch_kernel(fine_bwd_dq_kernel<64, RASTER>, grid, block, 0, s, a, g);
+  if (e != hipSuccess) return e;
+  return g.D == 128 ? launch_kernel(fine_bwd_dkdv_kernel<128, RASTER>, grid, block, 0, s, a, g)
+                    : launch_kernel(fine_bwd_dkdv_kernel<64, RASTER>, grid, block, 0, s, a, g);
+}
+}  // namespace
+
+hipError_t launch_bwd_prep(const Geo& g, const BwdPrepArgs& a, bool raster, hipStream_t s) {
+  return raster ? launch_prep_layout<true>(g, a, s) : launch_prep_layout<false>(g, a, s);
 }
 
 hipError_t launch_idx_transpose(const Geo& g, const int32_t* idx, int32_t* offsets,
@@ -794,13 +825,8 @@ hipError_t launch_idx_transpose(const Geo& g, const int32_t* idx, int32_t* offse
                        order, g);
 }
 
-hipError_t launch_bwd_fine(const Geo& g, const BwdFineArgs& a, hipStream_t s) {
-  const dim3 grid(g.B * g.H * g.C), block(256);
-  hipError_t e = g.D == 128 ? launch_kernel(fine_bwd_dq_kernel<128>, grid, block, 0, s, a, g)
-                            : launch_kernel(fine_bwd_dq_kernel<64>, grid, block, 0, s, a, g);
-  if (e != hipSuccess) return e;
-  return g.D == 128 ? launch_kernel(fine_bwd_dkdv_kernel<128>, grid, block, 0, s, a, g)
-                    : launch_kernel(fine_bwd_dkdv_kernel<64>, grid, block, 0, s, a, g);
+hipError_t launch_bwd_fine(const Geo& g, const BwdFineArgs& a, bool raster, hipStream_t s) {
+  return raster ? launch_fine_layout<true>(g, a, s) : launch_fine_layout<false>(g, a, s);
 }
 
 }  // namespace vsa

@@ -224,7 +224,7 @@ vsa_status forward_launch(const vsa_problem* p, const void* q, const void* k, co
 vsa_status backward_launch(const vsa_problem* p, const void* q, const void* k, const void* v,
                            const void* o_fine, const float* lse, const int32_t* idx,
                            const void* do_fine, const void* do_coarse, void* dq, void* dk,
-                           void* dv, void* ws, hipStream_t stream);
+                           void* dv, void* ws, bool raster, hipStream_t stream);
 
 }  // namespace
 
@@ -244,9 +244,11 @@ size_t vsa_workspace_bytes(const vsa_problem* p, int op) {
       carve_forward_fp8(p, nullptr, &total);
       return total;
     case VSA_OP_BACKWARD:
+    case VSA_OP_BACKWARD_CUBE:
       if (check_backward(p) != VSA_OK) return 0;
       carve_backward(p, nullptr, &total);
       return total;
+    case VSA_OP_FORWARD_CUBE: carve_coarse(p, nullptr, &total); return total;
     default: return 0;
   }
 }
@@ -363,7 +365,46 @@ vsa_status vsa_backward(const vsa_problem* p, const void* q, const void* k, cons
     return st;
   if ((st = check_backward(p)) != VSA_OK) return st;
   if ((st = workspace(p, VSA_OP_BACKWARD, ws, ws_bytes)) != VSA_OK) return st;
-  return backward_launch(p, q, k, v, o_fine, lse, idx, do_fine, do_coarse, dq, dk, dv, ws, stream);
+  return backward_launch(p, q, k, v, o_fine, lse, idx, do_fine, do_coarse, dq, dk, dv, ws,
+                         /*raster=*/true, stream);
+}
+
+vsa_status vsa_forward_cube(const vsa_problem* p, const void* qcube, const void* kcube,
+                            const void* vcube, void* o_fine, void* o_coarse, int32_t* idx,
+                            float* lse, void* ws, size_t ws_bytes, hipStream_t stream) {
+  vsa_status st = check(p);
+  if (st != VSA_OK) return st;
+  if ((st = pointers({qcube, kcube, vcube, o_fine, o_coarse, idx}, {lse})) != VSA_OK) return st;
+  if ((st = workspace(p, VSA_OP_FORWARD_CUBE, ws, ws_bytes)) != VSA_OK) return st;
+  const Geo g = geometry(p);
+  const CoarseWs w = carve_coarse(p, ws, nullptr);
+  vsa::ReorderBatch b = {};
+  b.x[0] = qcube; b.x[1] = kcube; b.x[2] = vcube;
+  b.mean[0] = w.qm; b.mean[1] = w.km; b.mean[2] = w.vm;
+  b.count = 3;
+  hipError_t e = vsa::launch_reorder(g, p->dtype, 2, b, stream);
+  if (e == hipSuccess)
+    e = vsa::launch_coarse(g, p->dtype, w.qm, w.km, w.vm, o_coarse, idx, nullptr, stream);
+  if (e == hipSuccess)
+    e = vsa::launch_fine(g, p->dtype, qcube, kcube, vcube, idx, o_fine, lse, /*raster=*/false,
+                         nullptr, nullptr, stream);
+  return launched(e);
+}
+
+vsa_status vsa_backward_cube(const vsa_problem* p, const void* qcube, const void* kcube,
+                             const void* vcube, const void* o_fine, const float* lse,
+                             const int32_t* idx, const void* do_fine, const void* do_coarse,
+                             void* dq, void* dk, void* dv, void* ws, size_t ws_bytes,
+                             hipStream_t stream) {
+  vsa_status st = check(p);
+  if (st != VSA_OK) return st;
+  if ((st = pointers({qcube, kcube, vcube, o_fine, lse, idx, do_fine, dq, dk, dv}, {do_coarse})) !=
+      VSA_OK)
+    return st;
+  if ((st = check_backward(p)) != VSA_OK) return st;
+  if ((st = workspace(p, VSA_OP_BACKWARD_CUBE, ws, ws_bytes)) != VSA_OK) return st;
+  return backward_launch(p, qcube, kcube, vcube, o_fine, lse, idx, do_fine, do_coarse, dq, dk, dv,
+                         ws, /*raster=*/false, stream);
 }
 
 }  // extern "C"
@@ -393,11 +434,12 @@ vsa_status forward_launch(const vsa_problem* p, const void* q, const void* k, co
   return launched(e);
 }
 
-// The launch sequence of vsa_backward on a validated problem and workspace.
+// The launch sequence of vsa_backward (raster) or vsa_backward_cube on a
+// validated problem and workspace.
 vsa_status backward_launch(const vsa_problem* p, const void* q, const void* k, const void* v,
                            const void* o_fine, const float* lse, const int32_t* idx,
                            const void* do_fine, const void* do_coarse, void* dq, void* dk,
-                           void* dv, void* ws, hipStream_t stream) {
+                           void* dv, void* ws, bool raster, hipStream_t stream) {
   const Geo g = geometry(p);
   const BwdWs w = carve_backward(p, ws, nullptr);
   auto b16 = [](const void* x) { return static_cast<const uint16_t*>(x); };
@@ -408,7 +450,7 @@ vsa_status backward_launch(const vsa_problem* p, const void* q, const void* k, c
   pa.delta = w.delta;
   pa.lse2 = w.lse2;
   pa.qm = w.qm; pa.km = w.km; pa.vm = w.vm; pa.docs = w.docs;
-  hipError_t e = vsa::launch_bwd_prep(g, pa, stream);
+  hipError_t e = vsa::launch_bwd_prep(g, pa, raster, stream);
   const bool coarse = do_coarse != nullptr;
   // the coarse backward builds the block lists in spare workgroups when it runs
   if (e == hipSuccess && coarse)
@@ -427,7 +469,7 @@ vsa_status backward_launch(const vsa_problem* p, const void* q, const void* k, c
     fa.dq = static_cast<uint16_t*>(dq);
     fa.dk = static_cast<uint16_t*>(dk);
     fa.dv = static_cast<uint16_t*>(dv);
-    e = vsa::launch_bwd_fine(g, fa, stream);
+    e = vsa::launch_bwd_fine(g, fa, raster, stream);
   }
   return launched(e);
 }

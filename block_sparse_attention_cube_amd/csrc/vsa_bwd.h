@@ -5,7 +5,8 @@
 
 namespace vsa {
 
-// Preparation pass over raster tensors (bf16).
+// Preparation pass (bf16): raster tensors, or cube-order tensors with a
+// per-cube dO_coarse [B,H,C,D] (raster = false).
 struct BwdPrepArgs {
   const uint16_t* q; const uint16_t* k; const uint16_t* v;
   const uint16_t* dof;   // upstream gradient of O_fine
@@ -17,7 +18,7 @@ struct BwdPrepArgs {
   float* qm; float* km; float* vm;   // [B,H,C,D] means over valid slots
   float* docs;           // [B,H,C,D] sums of dO_coarse over valid slots
 };
-hipError_t launch_bwd_prep(const Geo& g, const BwdPrepArgs& a, hipStream_t s);
+hipError_t launch_bwd_prep(const Geo& g, const BwdPrepArgs& a, bool raster, hipStream_t s);
 
 // Coarse-stage gradients from the means (fp32): dqc/dkc/dvc [B,H,C,D] and row
 // statistics stats [3][B,H,C] (row max, row sum of exp, rowsum(P * dP)).
@@ -39,14 +40,16 @@ hipError_t launch_idx_transpose(const Geo& g, const int32_t* idx, int32_t* offse
                                 int32_t* list, int32_t* order, hipStream_t s);
 
 struct BwdFineArgs {
-  const uint16_t* q; const uint16_t* k; const uint16_t* v; const uint16_t* dof;   // raster
+  const uint16_t* q; const uint16_t* k; const uint16_t* v; const uint16_t* dof;   // rows
   const float* lse2;     // [B,H,Np] lse * log2(e), +inf on pad slots
   const float* delta;    // [B,H,Np]
   const int32_t* idx;    // [B,H,C,K]
   const int32_t* offsets; const int32_t* list; const int32_t* order;
   const float* dqc; const float* dkc; const float* dvc;   // coarse gradients or nullptr
-  uint16_t* dq; uint16_t* dk; uint16_t* dv;               // raster out
+  uint16_t* dq; uint16_t* dk; uint16_t* dv;               // out, layout of the inputs
 };
-hipError_t launch_bwd_fine(const Geo& g, const BwdFineArgs& a, hipStream_t s);
+// raster = false: q, k, v, dO in cube order [B,H,Np,D], dq/dk/dv written in
+// cube order with zero pad rows.
+hipError_t launch_bwd_fine(const Geo& g, const BwdFineArgs& a, bool raster, hipStream_t s);
 
 }  // namespace vsa

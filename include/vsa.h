@@ -82,12 +82,13 @@ typedef struct {
 } vsa_problem;
 
 enum { VSA_OP_FORWARD = 0, VSA_OP_BACKWARD = 1, VSA_OP_COARSE = 2, VSA_OP_FINE = 3,
-       VSA_OP_FORWARD_FP8 = 4 };
+       VSA_OP_FORWARD_FP8 = 4, VSA_OP_FORWARD_CUBE = 5, VSA_OP_BACKWARD_CUBE = 6 };
 
 /* Bytes of device workspace the entry point `op` needs for problem `p`
  * (VSA_OP_FORWARD: vsa_forward, VSA_OP_BACKWARD: vsa_backward,
  * VSA_OP_COARSE: vsa_coarse, VSA_OP_FINE: vsa_fine,
- * VSA_OP_FORWARD_FP8: vsa_forward_fp8).  Returns 0 if `p` is
+ * VSA_OP_FORWARD_FP8: vsa_forward_fp8, VSA_OP_FORWARD_CUBE: vsa_forward_cube,
+ * VSA_OP_BACKWARD_CUBE: vsa_backward_cube).  Returns 0 if `p` is
  * invalid (see vsa_check_problem) or `op` unknown; a valid problem may also
  * need 0 bytes (then ws may be NULL).  Host-only, never touches the GPU. */
 size_t vsa_workspace_bytes(const vsa_problem* p, int op);
@@ -223,6 +224,41 @@ vsa_status vsa_backward(const vsa_problem* p, const void* q, const void* k, cons
                         const void* do_fine, const void* do_coarse,
                         void* dq, void* dk, void* dv,
                         void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* ---- cube order kept across calls --------------------------------------
+ * VSA drops in for FlashAttention inside a DiT (section on why sparse
+ * attention fails under distillation): a model that keeps its tokens in cube
+ * order from layer to layer calls these instead of vsa_forward/vsa_backward
+ * and pays no reorder on either side.  O_coarse stays one row per cube
+ * ([B,H,C,d], the row every token of the cube would receive); how it is
+ * combined with O_fine is left to the caller, as for the raster calls. */
+
+/* Whole forward on cube-order tensors.
+ *   qcube, kcube, vcube : [B,H,Np,d] cube order; pad slots must be finite
+ *                         (vsa_reorder writes zeros) and are never attended to.
+ *   o_fine              : [B,H,Np,d] out, cube order (pad rows unspecified).
+ *   o_coarse            : [B,H,C,d] out, one row per cube.
+ *   idx, lse            : as vsa_forward.
+ *   ws                  : vsa_workspace_bytes(p, VSA_OP_FORWARD_CUBE) bytes.
+ * Equals vsa_forward followed by vsa_reorder of o_fine (bf16 and fp32). */
+vsa_status vsa_forward_cube(const vsa_problem* p, const void* qcube, const void* kcube,
+                            const void* vcube, void* o_fine, void* o_coarse, int32_t* idx,
+                            float* lse, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Backward of vsa_forward_cube: gradients of
+ * sum(o_fine*do_fine) + sum(o_coarse*do_coarse) w.r.t. qcube, kcube, vcube with
+ * idx held constant (the definitions of vsa_backward, with dOc = do_coarse).
+ *   qcube, kcube, vcube, o_fine, do_fine : [B,H,Np,d] cube order (pad slots finite).
+ *   do_coarse : [B,H,C,d], one row per cube, or NULL (zero).
+ *   lse, idx  : as written by vsa_forward_cube.
+ *   dq, dk, dv: [B,H,Np,d] out, cube order, zero on pad slots.
+ *   ws        : vsa_workspace_bytes(p, VSA_OP_BACKWARD_CUBE) bytes.
+ * Limits of vsa_backward (VSA_BF16). */
+vsa_status vsa_backward_cube(const vsa_problem* p, const void* qcube, const void* kcube,
+                             const void* vcube, const void* o_fine, const float* lse,
+                             const int32_t* idx, const void* do_fine, const void* do_coarse,
+                             void* dq, void* dk, void* dv, void* ws, size_t ws_bytes,
+                             hipStream_t stream);
 
 /* ---- FP8 fine stage ----------------------------------------------------
  * The pages note that sparse attention and low-bit attention are orthogonal
