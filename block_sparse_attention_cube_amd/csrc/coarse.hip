@@ -105,7 +105,10 @@ __device__ __forceinline__ f32x4 dot_tile(const float4 (&af)[D / 16],
 }
 
 // KPL: keys per lane in the top-K, ceil(C / 64) rounded up to a power of two.
-template <typename TOut, int D, int KPL>
+// R: query-cube rows per workgroup, 16, or 8 above 2048 cubes so that the
+// R x C score tile fits in LDS (the 16-row MFMA tiles then repeat the 8 rows
+// and drop the repeated half of each result; waves R..15 take no top-K row).
+template <typename TOut, int D, int KPL, int R>
 __global__ __launch_bounds__(64 * kFwdWaves) void coarse_kernel(const float* __restrict__ qm,
                                                                const float* __restrict__ km,
                                                                const float* __restrict__ vm,
@@ -117,16 +120,16 @@ __global__ __launch_bounds__(64 * kFwdWaves) void coarse_kernel(const float* __r
   constexpr int kHalves = kFwdWaves / kOcWaves;   // waves sharing one slice, over key batches
   constexpr int kQS = D + 4;                      // padded row stride of qs (floats)
   extern __shared__ float lds[];
-  float* sc = lds;                       // [kRows][ldc]
-  float* rowmax = lds + kRows * ldc;     // [kRows]
-  float* rowinv = rowmax + kRows;        // [kRows]
-  float* qs = rowinv + kRows;            // [kRows][kQS]: the query rows, loaded once
-  float* part = qs + kRows * kQS;        // [kFwdWaves - kOcWaves][64][4]: O_coarse partial sums
+  float* sc = lds;                       // [R][ldc]
+  float* rowmax = lds + R * ldc;         // [R]
+  float* rowinv = rowmax + R;            // [R]
+  float* qs = rowinv + R;                // [R][kQS]: the query rows, loaded once
+  float* part = qs + R * kQS;            // [kFwdWaves - kOcWaves][64][4]: O_coarse partial sums
 
   constexpr float kScale = (D == 64) ? 0.125f : 0.08838834764831845f;  // 1/sqrt(D)
   const int C = g.C;
   const int64_t bh = blockIdx.y;
-  const int row0 = blockIdx.x * kRows;
+  const int row0 = blockIdx.x * R;
   // split grid: z = 0 statistics and O_coarse, z = 1 top-K; otherwise both
   const bool both = gridDim.z == 1;
   const bool oc_role = blockIdx.z == 0;
@@ -156,7 +159,7 @@ __global__ __launch_bounds__(64 * kFwdWaves) void coarse_kernel(const float* __r
   // The 16 query rows are read from memory once, coalesced, into LDS: every
   // scoring wave needs all of them, and a per-wave load would fetch them 16
   // times over the workgroup's vector memory path.
-  for (int e = threadIdx.x; e < kRows * D / 4; e += 64 * kFwdWaves) {
+  for (int e = threadIdx.x; e < R * D / 4; e += 64 * kFwdWaves) {
     const int r = e / (D / 4), c4 = e % (D / 4);
     const float4 x = (row0 + r < C) ? *reinterpret_cast<const float4*>(qh + (int64_t)(row0 + r) * D + 4 * c4)
                                     : make_float4(0.f, 0.f, 0.f, 0.f);
@@ -168,7 +171,7 @@ __global__ __launch_bounds__(64 * kFwdWaves) void coarse_kernel(const float* __r
   if (wave < ntile) {
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk)
-      qf[kk] = *reinterpret_cast<const float4*>(qs + li * kQS + 16 * kk + 4 * lg);
+      qf[kk] = *reinterpret_cast<const float4*>(qs + (li % R) * kQS + 16 * kk + 4 * lg);
   }
   for (int ct = wave; ct < ntile; ct += kFwdWaves) {
     const int col = ct * 16 + li;
@@ -177,6 +180,7 @@ __global__ __launch_bounds__(64 * kFwdWaves) void coarse_kernel(const float* __r
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int rr = 4 * lg + r;
+      if (rr >= R) continue;
       const float s = acc[r] * kScale;
       sc[rr * ldc + col] = s;
       if (oc_role && scores != nullptr && row0 + rr < C && col < C)
@@ -187,7 +191,7 @@ __global__ __launch_bounds__(64 * kFwdWaves) void coarse_kernel(const float* __r
 
   if (oc_role) {
     // -- 2. softmax statistics, one row per wave
-    for (int rr = wave; rr < kRows; rr += kFwdWaves) {
+    for (int rr = wave; rr < R; rr += kFwdWaves) {
       const float* srow = sc + rr * ldc;
       float m = -INFINITY;
       for (int j = lane; j < C; j += 64) m = fmaxf(m, srow[j]);
@@ -206,8 +210,8 @@ __global__ __launch_bounds__(64 * kFwdWaves) void coarse_kernel(const float* __r
     // The kHalves waves of a slice take every kHalves-th batch of 64 keys;
     // each batch of 16 Vc loads is issued one batch ahead of its MFMAs, and
     // the 16 MFMAs of a batch alternate between 4 accumulators.
-    const float mrow = rowmax[li], irow = rowinv[li];
-    const float* prow = sc + li * ldc;
+    const float mrow = rowmax[li % R], irow = rowinv[li % R];
+    const float* prow = sc + (li % R) * ldc;
     f32x4 acc[4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f},
                     {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
     for (int j0 = 64 * half; j0 < C; j0 += 64 * kHalves) {
@@ -237,7 +241,7 @@ __global__ __launch_bounds__(64 * kFwdWaves) void coarse_kernel(const float* __r
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int row = row0 + 4 * lg + r;
-        if (row < C) store_out(oc + (bh * C + row) * D + dt * 16 + li, sum[r]);
+        if (4 * lg + r < R && row < C) store_out(oc + (bh * C + row) * D + dt * 16 + li, sum[r]);
       }
     }
     if (!both) return;
@@ -245,9 +249,9 @@ __global__ __launch_bounds__(64 * kFwdWaves) void coarse_kernel(const float* __r
 
   // -- 4. top-K, one row per wave.  Counting a predicate over the row is one
   // 64-bit ballot plus a scalar popcount per 64 keys.
-  static_assert(kRows == kFwdWaves, "one top-K row per wave");
+  static_assert(R <= kFwdWaves, "one top-K row per wave");
   const int rr = wave;
-  if (row0 + rr >= C) return;
+  if (rr >= R || row0 + rr >= C) return;
   const int K = g.K;
   const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   const float* srow = sc + rr * ldc;
@@ -288,14 +292,14 @@ __global__ __launch_bounds__(64 * kFwdWaves) void coarse_kernel(const float* __r
   }
 }
 
-template <typename TOut, int D, int KPL>
+template <typename TOut, int D, int KPL, int R>
 hipError_t launch_kpl(const Geo& g, const float* qm, const float* km, const float* vm, void* oc,
                       int32_t* idx, float* scores, hipStream_t s) {
   const int ntile = (g.C + 15) / 16;
   const int ldc = ntile * 16 + 1;  // odd stride spreads a column over the LDS banks
-  const size_t lds = (size_t)(kRows * ldc + 2 * kRows + kRows * (D + 4) +
+  const size_t lds = (size_t)(R * ldc + 2 * R + R * (D + 4) +
                               (kFwdWaves - D / 16) * 64 * 4) * sizeof(float);
-  auto* kern = coarse_kernel<TOut, D, KPL>;
+  auto* kern = coarse_kernel<TOut, D, KPL, R>;
   if (lds > 65536) {
     const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                              hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -303,22 +307,24 @@ hipError_t launch_kpl(const Geo& g, const float* qm, const float* km, const floa
     if (e != hipSuccess) return e;
   }
   // two workgroups per row tile while one per tile leaves CUs idle
-  const int roles = int64_t(ntile) * g.B * g.H <= kSplitTiles ? 2 : 1;
-  return launch_kernel(kern, dim3(ntile, g.B * g.H, roles), dim3(64 * kFwdWaves), lds, s, qm, km,
+  const int rtiles = (g.C + R - 1) / R;
+  const int roles = int64_t(rtiles) * g.B * g.H <= kSplitTiles ? 2 : 1;
+  return launch_kernel(kern, dim3(rtiles, g.B * g.H, roles), dim3(64 * kFwdWaves), lds, s, qm, km,
                        vm, static_cast<TOut*>(oc), idx, scores, g, ldc);
 }
 
 template <typename TOut, int D>
 hipError_t launch_typed(const Geo& g, const float* qm, const float* km, const float* vm,
                         void* oc, int32_t* idx, float* scores, hipStream_t s) {
-  static_assert(kMaxCubes <= 32 * 64, "top-K holds at most 32 keys per lane");
+  static_assert(kMaxCubes <= 64 * 64, "top-K holds at most 64 keys per lane");
   const int per_lane = (g.C + 63) / 64;
-  if (per_lane <= 1) return launch_kpl<TOut, D, 1>(g, qm, km, vm, oc, idx, scores, s);
-  if (per_lane <= 2) return launch_kpl<TOut, D, 2>(g, qm, km, vm, oc, idx, scores, s);
-  if (per_lane <= 4) return launch_kpl<TOut, D, 4>(g, qm, km, vm, oc, idx, scores, s);
-  if (per_lane <= 8) return launch_kpl<TOut, D, 8>(g, qm, km, vm, oc, idx, scores, s);
-  if (per_lane <= 16) return launch_kpl<TOut, D, 16>(g, qm, km, vm, oc, idx, scores, s);
-  return launch_kpl<TOut, D, 32>(g, qm, km, vm, oc, idx, scores, s);
+  if (per_lane <= 1) return launch_kpl<TOut, D, 1, 16>(g, qm, km, vm, oc, idx, scores, s);
+  if (per_lane <= 2) return launch_kpl<TOut, D, 2, 16>(g, qm, km, vm, oc, idx, scores, s);
+  if (per_lane <= 4) return launch_kpl<TOut, D, 4, 16>(g, qm, km, vm, oc, idx, scores, s);
+  if (per_lane <= 8) return launch_kpl<TOut, D, 8, 16>(g, qm, km, vm, oc, idx, scores, s);
+  if (per_lane <= 16) return launch_kpl<TOut, D, 16, 16>(g, qm, km, vm, oc, idx, scores, s);
+  if (per_lane <= 32) return launch_kpl<TOut, D, 32, 16>(g, qm, km, vm, oc, idx, scores, s);
+  return launch_kpl<TOut, D, 64, 8>(g, qm, km, vm, oc, idx, scores, s);
 }
 
 // ---------------------------------------------------------------------------
@@ -565,7 +571,12 @@ hipError_t launch_coarse_bwd(const Geo& g, const float* qm, const float* km, con
                              float* dvc, const int32_t* idx, int32_t* offsets, int32_t* list,
                              int32_t* order, hipStream_t s) {
   const ListArgs lists = {g.C <= kBitmapCubes ? idx : nullptr, offsets, list, order};
-  // 16 cubes per workgroup while two 16 x C fp32 tiles fit the LDS, else 8
+  // 16 cubes per workgroup while two 16 x C fp32 tiles fit the LDS, else 8,
+  // else 4
+  if (g.C > kCoarseBwd8Cubes)
+    return g.D == 128
+               ? launch_coarse_bwd_typed<128, 4>(g, qm, km, vm, docs, stats, dqc, dkc, dvc, lists, s)
+               : launch_coarse_bwd_typed<64, 4>(g, qm, km, vm, docs, stats, dqc, dkc, dvc, lists, s);
   if (g.C <= kCoarseBwd16Cubes)
     return g.D == 128
                ? launch_coarse_bwd_typed<128, 16>(g, qm, km, vm, docs, stats, dqc, dkc, dvc, lists, s)

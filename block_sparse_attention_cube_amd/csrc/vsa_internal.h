@@ -11,10 +11,12 @@ namespace vsa {
 
 constexpr int kCube = 4;     // cube edge along each of (t, y, x)
 constexpr int kSlots = 64;   // tokens per cube
-constexpr int kMaxCubes = 2048;  // coarse score rows are staged in LDS: 16 x C fp32
-// The coarse backward keeps two R x C fp32 tiles in LDS: R = 16 cubes per
-// workgroup up to 1216 cubes, R = 8 up to kMaxCubes.
+// The coarse stage keeps R x C fp32 score rows in LDS: the forward R = 16
+// query cubes per workgroup up to 2048 cubes, R = 8 above; the backward two
+// such tiles, R = 16 up to 1216 cubes, 8 up to 2048, 4 above.
+constexpr int kMaxCubes = 4096;
 constexpr int kCoarseBwd16Cubes = 1216;
+constexpr int kCoarseBwd8Cubes = 2048;
 constexpr int kMaxCubesBackward = kMaxCubes;
 
 // Geometry of one problem, passed by value to every kernel.

@@ -45,7 +45,8 @@ def prob(**kw):
     (dict(Ww=0), L.VSA_ERR_SHAPE), (dict(topk=0), L.VSA_ERR_SHAPE),
     (dict(topk=113), L.VSA_ERR_SHAPE), (dict(d=96), L.VSA_ERR_UNSUPPORTED),
     (dict(cube_t=2), L.VSA_ERR_UNSUPPORTED), (dict(dtype=7), L.VSA_ERR_UNSUPPORTED),
-    (dict(T=4 * 40, Hh=4 * 8, Ww=4 * 8, topk=1), L.VSA_ERR_UNSUPPORTED),   # 2560 cubes
+    (dict(T=4 * 80, Hh=4 * 8, Ww=4 * 8, topk=1), L.VSA_ERR_UNSUPPORTED),   # 5120 cubes
+    (dict(T=4 * 64, Hh=4 * 8, Ww=4 * 8, topk=1), L.VSA_OK),                # 4096 cubes
     (dict(), L.VSA_OK), (dict(topk=112), L.VSA_OK), (dict(T=1, Hh=1, Ww=1, topk=1), L.VSA_OK),
 ])
 def test_problem_validation(kw, status):

@@ -38,6 +38,9 @@ EDGE = [
     # 0.03 bound
     Workload("bwd-1280-cubes", B=1, H=1, T=4, Hh=126, Ww=158, d=64, dtype="bf16", topk=2,
              structure="offset", alpha=0.5, backward=True),
+    # 2304 cubes: the coarse backward takes 4 cubes per workgroup
+    Workload("bwd-2304-cubes", B=1, H=1, T=4, Hh=190, Ww=189, d=64, dtype="bf16", topk=2,
+             structure="offset", alpha=0.5, backward=True),
 ]
 CASES = list(configs.SWEEP) + EDGE
 ids = [w.name for w in CASES]

@@ -40,6 +40,10 @@ EDGE = [
              structure="field", alpha=0.5),
     Workload("cubes640-ragged", B=1, H=2, T=16, Hh=62, Ww=39, d=128, dtype="bf16", topk=20,
              structure="field", alpha=0.5),
+    # 2304 cubes: above 2048 the coarse stage takes 8 query cubes per workgroup
+    # and the top-K 64 keys per lane
+    Workload("cubes2304-ragged", B=1, H=1, T=4, Hh=190, Ww=189, d=64, dtype="bf16", topk=3,
+             structure="offset", alpha=0.5),
 ]
 SMALL = [configs.TINY_F32, configs.DIT_410M, configs.WAN_1_3B]
 CASES = SMALL + EDGE
