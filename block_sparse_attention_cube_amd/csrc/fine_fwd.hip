@@ -226,7 +226,12 @@ __device__ __forceinline__ void pv_tile(const uint16_t* v_lds, const int* vtr, c
 
 // RASTER: q, k, v are raster [B,H,N,D] and o, o_coarse are raster;
 // otherwise q, k, v and o are cube order [B,H,Np,D].
-template <int D, bool RASTER>
+// HROWS: wave w owns the 16 query slots of the cube's h-row ih = w (slot
+// 16 it + 4 w + iw) instead of its time slice it = w (slots 16w..16w+15); a
+// wave whose row or slice lies past the cube's extent holds only pad slots
+// and computes nothing.  The launcher takes the mapping that idles more
+// waves on the grid at hand.
+template <int D, bool RASTER, bool HROWS>
 __global__ __launch_bounds__(256, 2) void fine_fwd_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const int32_t* __restrict__ idx,
@@ -296,12 +301,14 @@ __global__ __launch_bounds__(256, 2) void fine_fwd_bf16_kernel(
   // Q fragment: B operand of S^T, lane holds Q[slot 16w+li][32ks + 8lg .. +7]
   u32x4 qf[kKS];
   const CubeExt eq = cube_extent(g, qc);
-  // wave w holds time slice w of the query cube: past the cube's t extent
-  // its 16 slots are all pads and it computes nothing (it still stages its
-  // share of the tiles and meets every barrier)
-  const bool active = wave < eq.nt;
+  // wave w holds time slice w (or h-row w) of the query cube: past the
+  // cube's extent its 16 slots are all pads and it computes nothing (it
+  // still stages its share of the tiles and meets every barrier).  Lane li
+  // serves query slot qslot.
+  const bool active = wave < (HROWS ? eq.nh : eq.nt);
+  const int qslot = HROWS ? 16 * (li >> 2) + 4 * wave + (li & 3) : 16 * wave + li;
   {
-    const int it = wave, ih = li >> 2, iw = li & 3;
+    const int it = qslot >> 4, ih = (qslot >> 2) & 3, iw = li & 3;
     const bool valid = !RASTER || (it < eq.nt && ih < eq.nh && iw < eq.nw);
     const int row = cube_row<RASTER>(g, eq, qc) + (valid ? slot_row<RASTER>(g, it, ih, iw) : 0);
     const uint16_t* qrow = q + head0 + static_cast<int64_t>(row) * D;
@@ -435,16 +442,16 @@ __global__ __launch_bounds__(256, 2) void fine_fwd_bf16_kernel(
   const float l = lacc[0];
   const float inv = active ? 1.f / l : 0.f;
   if (lse != nullptr && lg == 0)
-    lse[bh * g.Np + static_cast<int64_t>(qc) * 64 + wave * 16 + li] =
+    lse[bh * g.Np + static_cast<int64_t>(qc) * 64 + qslot] =
         active ? (mb + log2f(l)) * kLn2 : 0.f;
 
   uint16_t* const o_lds = smem;  // [64][kOS]
 #pragma unroll
   for (int dt = 0; dt < kDT; ++dt) {
-    // lane holds O[q = 16w+li][d = 16dt + 4lg + r], r = 0..3
+    // lane holds O[q = qslot][d = 16dt + 4lg + r], r = 0..3
     const u32x2 w = {pack_bf16x2(oacc[dt][0] * inv, oacc[dt][1] * inv),
                      pack_bf16x2(oacc[dt][2] * inv, oacc[dt][3] * inv)};
-    *reinterpret_cast<u32x2*>(o_lds + (wave * 16 + li) * kOS + 16 * dt + 4 * lg) = w;
+    *reinterpret_cast<u32x2*>(o_lds + qslot * kOS + 16 * dt + 4 * lg) = w;
   }
   __syncthreads();
 #pragma unroll
@@ -916,11 +923,18 @@ hipError_t launch_typed(const Geo& g, int dtype, const void* q, const void* k, c
                         const int32_t* idx, void* o, float* lse, const void* oc,
                         void* o_coarse, hipStream_t s) {
   const dim3 grid(g.B * g.H * g.C), block(256);
-  if (dtype == 1)
-    return launch_kernel(fine_fwd_bf16_kernel<D, RASTER>, grid, block, 0, s,
+  if (dtype == 1) {
+    // idle query waves over the cube grid: time slices past T in the last
+    // cube layer (4 - nt per cube) or h-rows past Hh in the last cube row
+    const int64_t t_idle = int64_t(4 * g.Ct - g.T) * g.Ch * g.Cw;
+    const int64_t h_idle = int64_t(4 * g.Ch - g.Hh) * g.Ct * g.Cw;
+    auto kern = h_idle > t_idle ? fine_fwd_bf16_kernel<D, RASTER, true>
+                                : fine_fwd_bf16_kernel<D, RASTER, false>;
+    return launch_kernel(kern, grid, block, 0, s,
                          static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                          static_cast<const uint16_t*>(v), idx, static_cast<uint16_t*>(o), lse,
                          static_cast<const uint16_t*>(oc), static_cast<uint16_t*>(o_coarse), g);
+  }
   return launch_kernel(fine_fwd_f32_kernel<D, RASTER>, grid, block, 0, s,
                        static_cast<const float*>(q), static_cast<const float*>(k),
                        static_cast<const float*>(v), idx, static_cast<float*>(o), lse,
