@@ -50,20 +50,21 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 
 // LDS tile of one 64-token block, row major [64][D], filled by DMA.  It is
 // read two ways: 16 bytes per lane down 16 rows (MFMA operands contracted
-// over the head dim) and by transposed reads, 8 bytes per lane, 16 rows x
-// 32 bytes per half-wave (operands contracted over the tokens).  Chunk c of
-// row r sits at c ^ sw(r); sw is one-to-one on every 16 consecutive rows
-// (the row reads) and its upper bits are one-to-one on every 8 (the
-// transposed reads), so both patterns hit distinct bank positions.
+// over the head dim) and by transposed reads, 8 bytes per lane, 4 rows x 32
+// bytes per 16 lanes (operands contracted over the tokens).  gfx950's LDS
+// has 64 banks of 4 bytes; measured with the bank-conflict counter, a
+// 16-byte read is served in four 16-lane phases, lanes {0-3, 12-15, 20-23,
+// 24-27}, {4-11, 16-19, 28-31} and the same sets + 32, and an 8-byte read
+// (plain or transposed) in two phases of 32 consecutive lanes.  Chunk c of
+// row r sits at c ^ sw(r); sw(r) = 2 (r mod 8) (d = 128) or
+// 2 ((r / 2) mod 4) (d = 64) puts every phase of both reads on distinct
+// banks.
 template <int D>
 struct BwdTile {
   static constexpr int kElems = 64 * D;
   static constexpr int kKC = D / 8;                // 16-byte chunks per row
   static constexpr int kDma = kElems / (256 * 8);  // DMA loads per thread per tile
-  __device__ static constexpr int sw(int r) {
-    return kKC == 16 ? (((r & 7) << 1) | ((r >> 3) & 1))
-                     : ((((r >> 1) & 3) << 1) | ((r >> 3) & 1));
-  }
+  __device__ static constexpr int sw(int r) { return kKC == 16 ? 2 * (r & 7) : 2 * ((r >> 1) & 3); }
 };
 
 // Buffer resource over `bytes` bytes from base (one head of a tensor);
