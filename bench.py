@@ -44,6 +44,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=400)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-reps", type=int, default=5)
+    ap.add_argument("--workload", choices=["wan1.3b", "wan14b"], default="wan1.3b",
+                    help="shape of --stage runs (the full bench always uses wan1.3b)")
     ap.add_argument("--stage", choices=["all", "forward", "fine", "fine_raster", "dense", "coarse",
                                         "reorder", "backward",
                                         "fine_fp8", "forward_fp8", "quantize_fp8"],
@@ -398,11 +400,14 @@ def main():
     from synth import configs, inputs
 
     w = configs.WAN_1_3B
+    n_sets = N_SETS
+    if args.stage != "all" and args.workload == "wan14b":
+        w, n_sets = configs.WAN_14B, 1     # 2.3 GB of q, k, v: beyond every cache already
     grid = (w.T, w.Hh, w.Ww)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
 
-    host_sets = [inputs.make_inputs(w, seed=s) for s in range(N_SETS)]
+    host_sets = [inputs.make_inputs(w, seed=s) for s in range(n_sets)]
     sets = [{n: inputs.as_torch(h[n], w.dtype, dev) for n in "qkv"} for h in host_sets]
     cube_sets = [{n: vsa.reorder(s[n], grid) for n in "qkv"} for s in sets]
 
