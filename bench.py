@@ -269,16 +269,18 @@ def sparsity_sweep(args, dev):
         grid = (w.T, w.Hh, w.Ww)
         host = [inputs.make_inputs(w, seed=s, grads=True) for s in range(2)]
         sets = [{n: inputs.as_torch(h[n], w.dtype, dev) for n in h} for h in host]
-        fwd = vsa.ForwardPlan(w.B, w.H, grid, w.d, w.topk, torch.bfloat16, dev)
+        # the training pair: the forward keeps its per-cube means for the backward
+        fwd = vsa.ForwardPlan(w.B, w.H, grid, w.d, w.topk, torch.bfloat16, dev, keep_means=True)
         bwd = vsa.BackwardPlan(w.B, w.H, grid, w.d, w.topk, torch.bfloat16, dev)
         outs = []
         for s in sets:
             of, oc, idx, lse = fwd.run(s["q"], s["k"], s["v"])
-            outs.append((of.clone(), idx.clone(), lse.clone()))
+            outs.append((of.clone(), idx.clone(), lse.clone(), fwd.means.clone()))
         f_ms = timed(lambda i: fwd.run(sets[i]["q"], sets[i]["k"], sets[i]["v"]), steps, warm, 2)
         b_ms = timed(lambda i: bwd.run(sets[i]["q"], sets[i]["k"], sets[i]["v"], outs[i][0],
                                        outs[i][2], outs[i][1], sets[i]["do_fine"],
-                                       sets[i]["do_coarse"]), steps, warm, 2)
+                                       sets[i]["do_coarse"], means=outs[i][3]),
+                     steps, warm, 2)
         ff = flops.fine_forward_flops(w.B, w.H, w.C, w.topk, w.d)
         fb = flops.fine_backward_flops(w.B, w.H, w.C, w.topk, w.d)
         out.append({"topk": w.topk, "sparsity": round(1 - w.topk / w.C, 4),

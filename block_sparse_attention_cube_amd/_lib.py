@@ -61,12 +61,14 @@ _SIG = {
     "vsa_fine": (ctypes.c_int, [_P, _V, _V, _V, _V, _V, _V, _V, ctypes.c_size_t, _V]),
     "vsa_fine_raster": (ctypes.c_int, [_P, _V, _V, _V, _V, _V, _V, _V, _V, _V]),
     "vsa_dense": (ctypes.c_int, [_P, _V, _V, _V, _V, _V, _V]),
-    "vsa_forward": (ctypes.c_int, [_P, _V, _V, _V, _V, _V, _V, _V, _V, ctypes.c_size_t, _V]),
-    "vsa_forward_static": (ctypes.c_int, [_P, _V, _V, _V, _V, _V, _V, _V, _V]),
-    "vsa_forward_cube": (ctypes.c_int, [_P, _V, _V, _V, _V, _V, _V, _V, _V, ctypes.c_size_t, _V]),
-    "vsa_backward_cube": (ctypes.c_int, [_P, _V, _V, _V, _V, _V, _V, _V, _V, _V, _V, _V, _V,
+    "vsa_forward": (ctypes.c_int, [_P, _V, _V, _V, _V, _V, _V, _V, _V, _V, ctypes.c_size_t,
+                                   _V]),
+    "vsa_forward_static": (ctypes.c_int, [_P, _V, _V, _V, _V, _V, _V, _V, _V, _V]),
+    "vsa_forward_cube": (ctypes.c_int, [_P, _V, _V, _V, _V, _V, _V, _V, _V, _V,
+                                        ctypes.c_size_t, _V]),
+    "vsa_backward_cube": (ctypes.c_int, [_P, _V, _V, _V, _V, _V, _V, _V, _V, _V, _V, _V, _V, _V,
                                          ctypes.c_size_t, _V]),
-    "vsa_backward": (ctypes.c_int, [_P, _V, _V, _V, _V, _V, _V, _V, _V, _V, _V, _V, _V,
+    "vsa_backward": (ctypes.c_int, [_P, _V, _V, _V, _V, _V, _V, _V, _V, _V, _V, _V, _V, _V,
                                     ctypes.c_size_t, _V]),
     "vsa_quantize_fp8": (ctypes.c_int, [_P, _V, _V, _V, _V, _V, _V, _V, _V]),
     "vsa_fine_fp8": (ctypes.c_int, [_P, _V, _V, _V, _V, _V, _V, _V, _V]),

@@ -81,6 +81,12 @@ def check_problem(B: int, H: int, grid: Grid, d: int, topk: int, dtype: torch.dt
     return int(L.lib().vsa_check_problem(ctypes.byref(prob)))
 
 
+def _means(means: Optional[torch.Tensor], B: int, H: int, C: int, d: int) -> None:
+    """Checks an optional per-cube means buffer [3,B,H,C,d] fp32 (q, k, v)."""
+    if means is not None:
+        _expect(means, (3, B, H, C, d), torch.float32, "means")
+
+
 def _raster_inputs(q, k, v, grid):
     _device_tensor(q, "q")
     B, H, N, d = q.shape
@@ -203,10 +209,13 @@ def dense(qcube: torch.Tensor, kcube: torch.Tensor, vcube: torch.Tensor, grid: G
 
 
 class ForwardPlan:
-    """Preallocated outputs and workspace for repeated vsa_forward calls on one shape."""
+    """Preallocated outputs and workspace for repeated vsa_forward calls on one shape.
+    keep_means: also write the per-cube means of q, k, v into self.means
+    [3,B,H,C,d] fp32, for a later backward."""
 
     def __init__(self, B: int, H: int, grid: Grid, d: int, topk: int, dtype: torch.dtype,
-                 device, return_lse: bool = True, op: int = L.VSA_OP_FORWARD):
+                 device, return_lse: bool = True, op: int = L.VSA_OP_FORWARD,
+                 keep_means: bool = False):
         self.prob = make_problem(B, H, grid, d, topk, dtype)
         L.check(L.lib().vsa_check_problem(ctypes.byref(self.prob)), "vsa_forward")
         C, Np = cube_counts(grid)
@@ -218,6 +227,8 @@ class ForwardPlan:
         self.o_coarse = torch.empty(self.shape, dtype=dtype, device=device)
         self.idx = torch.empty((B, H, C, topk), dtype=torch.int32, device=device)
         self.lse = torch.empty((B, H, Np), dtype=torch.float32, device=device) if return_lse else None
+        self.means = (torch.empty((3, B, H, C, d), dtype=torch.float32, device=device)
+                      if keep_means else None)
         self.ws, self.nws = _workspace(self.prob, op, device)
 
     def run(self, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor):
@@ -225,7 +236,7 @@ class ForwardPlan:
             _expect(t, self.shape, self.dtype, n)
         L.check(L.lib().vsa_forward(ctypes.byref(self.prob), _ptr(q), _ptr(k), _ptr(v),
                                     _ptr(self.o_fine), _ptr(self.o_coarse), _ptr(self.idx),
-                                    _ptr(self.lse), _ptr(self.ws), self.nws,
+                                    _ptr(self.lse), _ptr(self.means), _ptr(self.ws), self.nws,
                                     _stream(self.device)), "vsa_forward")
         return self.o_fine, self.o_coarse, self.idx, self.lse
 
@@ -242,21 +253,26 @@ class BackwardPlan:
         self.shape = (B, H, N, d)
         self.lse_shape = (B, H, Np)
         self.idx_shape = (B, H, C, topk)
+        self.means_shape = (3, B, H, C, d)
         self.dtype = dtype
         self.device = torch.device(device)
         self.dq, self.dk, self.dv = (torch.empty(self.shape, dtype=dtype, device=device)
                                      for _ in range(3))
         self.ws, self.nws = _workspace(self.prob, L.VSA_OP_BACKWARD, device)
 
-    def run(self, q, k, v, o_fine, lse, idx, do_fine, do_coarse=None):
+    def run(self, q, k, v, o_fine, lse, idx, do_fine, do_coarse=None, means=None):
+        """means: the forward's per-cube means (ForwardPlan(keep_means=True).means),
+        or None to recompute them from q, k, v."""
         for t, n in ((q, "q"), (k, "k"), (v, "v"), (o_fine, "o_fine"), (do_fine, "do_fine")):
             _expect(t, self.shape, self.dtype, n)
         if do_coarse is not None:
             _expect(do_coarse, self.shape, self.dtype, "do_coarse")
         _expect(lse, self.lse_shape, torch.float32, "lse")
         _expect(idx, self.idx_shape, torch.int32, "idx")
+        if means is not None:
+            _expect(means, self.means_shape, torch.float32, "means")
         L.check(L.lib().vsa_backward(ctypes.byref(self.prob), _ptr(q), _ptr(k), _ptr(v),
-                                     _ptr(o_fine), _ptr(lse), _ptr(idx), _ptr(do_fine),
+                                     _ptr(o_fine), _ptr(lse), _ptr(idx), _ptr(means), _ptr(do_fine),
                                      _ptr(do_coarse), _ptr(self.dq), _ptr(self.dk), _ptr(self.dv),
                                      _ptr(self.ws), self.nws, _stream(self.device)),
                 "vsa_backward")
@@ -264,20 +280,26 @@ class BackwardPlan:
 
 
 def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, grid: Grid, topk: int,
-            return_lse: bool = True):
-    """Whole VSA forward on raster tensors: (o_fine, o_coarse, idx, lse)."""
+            return_lse: bool = True, means: Optional[torch.Tensor] = None):
+    """Whole VSA forward on raster tensors: (o_fine, o_coarse, idx, lse).
+    means: optional [3,B,H,C,d] fp32 tensor that receives the per-cube means
+    of q, k, v (hand it to backward)."""
     B, H, N, d = _raster_inputs(q, k, v, grid)
+    _means(means, B, H, cube_counts(grid)[0], d)
     plan = ForwardPlan(B, H, grid, d, topk, q.dtype, q.device, return_lse)
+    plan.means = means
     return plan.run(q, k, v)
 
 
 def forward_static(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, grid: Grid, topk: int,
-                   out=None, return_lse: bool = True):
+                   out=None, return_lse: bool = True, means: Optional[torch.Tensor] = None):
     """vsa_forward_static: the whole forward with the library's own device
     scratch (no workspace).  out: optional preallocated (o_fine, o_coarse, idx,
-    lse) to write into, so that the call itself allocates nothing."""
+    lse) to write into, so that the call itself allocates nothing; means as
+    for forward."""
     B, H, N, d = _raster_inputs(q, k, v, grid)
     C, Np = cube_counts(grid)
+    _means(means, B, H, C, d)
     prob = make_problem(B, H, grid, d, topk, q.dtype)
     L.check(L.lib().vsa_check_problem(ctypes.byref(prob)), "vsa_forward_static")
     dev = q.device
@@ -293,14 +315,17 @@ def forward_static(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, grid: Grid
         _expect(lse, (B, H, Np), torch.float32, "lse")
     L.check(L.lib().vsa_forward_static(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v),
                                        _ptr(o_fine), _ptr(o_coarse), _ptr(idx), _ptr(lse),
-                                       _stream(dev)), "vsa_forward_static")
+                                       _ptr(means), _stream(dev)), "vsa_forward_static")
     return o_fine, o_coarse, idx, lse
 
 
-def backward(q, k, v, o_fine, lse, idx, do_fine, do_coarse, grid: Grid):
-    """Gradients (dq, dk, dv) of sum(o_fine*do_fine) + sum(o_coarse*do_coarse)."""
+def backward(q, k, v, o_fine, lse, idx, do_fine, do_coarse, grid: Grid,
+             means: Optional[torch.Tensor] = None):
+    """Gradients (dq, dk, dv) of sum(o_fine*do_fine) + sum(o_coarse*do_coarse).
+    means: the forward's per-cube means, or None to recompute them."""
     B, H, N, d = _raster_inputs(q, k, v, grid)
     C, Np = cube_counts(grid)
+    _means(means, B, H, C, d)
     _expect(o_fine, q.shape, q.dtype, "o_fine")
     _expect(do_fine, q.shape, q.dtype, "do_fine")
     if do_coarse is not None:
@@ -315,7 +340,7 @@ def backward(q, k, v, o_fine, lse, idx, do_fine, do_coarse, grid: Grid):
     dq, dk, dv = (torch.empty_like(q) for _ in range(3))
     ws, nws = _workspace(prob, L.VSA_OP_BACKWARD, dev)
     L.check(L.lib().vsa_backward(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(o_fine),
-                                 _ptr(lse), _ptr(idx), _ptr(do_fine), _ptr(do_coarse),
+                                 _ptr(lse), _ptr(idx), _ptr(means), _ptr(do_fine), _ptr(do_coarse),
                                  _ptr(dq), _ptr(dk), _ptr(dv), _ptr(ws), nws, _stream(dev)),
             "vsa_backward")
     return dq, dk, dv
@@ -333,10 +358,12 @@ def _cube_inputs(qcube, kcube, vcube, grid):
 
 
 def forward_cube(qcube: torch.Tensor, kcube: torch.Tensor, vcube: torch.Tensor, grid: Grid,
-                 topk: int, return_lse: bool = True):
+                 topk: int, return_lse: bool = True, means: Optional[torch.Tensor] = None):
     """Whole forward on cube-order tensors: (o_fine [B,H,Np,d] cube order,
-    o_coarse [B,H,C,d] per cube, idx [B,H,C,K], lse [B,H,Np])."""
+    o_coarse [B,H,C,d] per cube, idx [B,H,C,K], lse [B,H,Np]); means as for
+    forward."""
     B, H, C, Np, d = _cube_inputs(qcube, kcube, vcube, grid)
+    _means(means, B, H, C, d)
     prob = make_problem(B, H, grid, d, topk, qcube.dtype)
     L.check(L.lib().vsa_check_problem(ctypes.byref(prob)), "vsa_forward_cube")
     dev = qcube.device
@@ -346,16 +373,18 @@ def forward_cube(qcube: torch.Tensor, kcube: torch.Tensor, vcube: torch.Tensor, 
     lse = torch.empty((B, H, Np), dtype=torch.float32, device=dev) if return_lse else None
     ws, nws = _workspace(prob, L.VSA_OP_FORWARD_CUBE, dev)
     L.check(L.lib().vsa_forward_cube(ctypes.byref(prob), _ptr(qcube), _ptr(kcube), _ptr(vcube),
-                                     _ptr(o), _ptr(oc), _ptr(idx), _ptr(lse), _ptr(ws), nws,
-                                     _stream(dev)), "vsa_forward_cube")
+                                     _ptr(o), _ptr(oc), _ptr(idx), _ptr(lse), _ptr(means),
+                                     _ptr(ws), nws, _stream(dev)), "vsa_forward_cube")
     return o, oc, idx, lse
 
 
-def backward_cube(qcube, kcube, vcube, o_fine, lse, idx, do_fine, do_coarse, grid: Grid):
+def backward_cube(qcube, kcube, vcube, o_fine, lse, idx, do_fine, do_coarse, grid: Grid,
+                  means: Optional[torch.Tensor] = None):
     """Gradients (dq, dk, dv) in cube order of sum(o_fine*do_fine) +
     sum(o_coarse*do_coarse) for the outputs of forward_cube (do_coarse per
-    cube [B,H,C,d] or None)."""
+    cube [B,H,C,d] or None; means from forward_cube or None)."""
     B, H, C, Np, d = _cube_inputs(qcube, kcube, vcube, grid)
+    _means(means, B, H, C, d)
     _expect(o_fine, qcube.shape, qcube.dtype, "o_fine")
     _expect(do_fine, qcube.shape, qcube.dtype, "do_fine")
     if do_coarse is not None:
@@ -369,9 +398,9 @@ def backward_cube(qcube, kcube, vcube, o_fine, lse, idx, do_fine, do_coarse, gri
     dq, dk, dv = (torch.empty_like(qcube) for _ in range(3))
     ws, nws = _workspace(prob, L.VSA_OP_BACKWARD_CUBE, dev)
     L.check(L.lib().vsa_backward_cube(ctypes.byref(prob), _ptr(qcube), _ptr(kcube), _ptr(vcube),
-                                      _ptr(o_fine), _ptr(lse), _ptr(idx), _ptr(do_fine),
-                                      _ptr(do_coarse), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(ws),
-                                      nws, _stream(dev)), "vsa_backward_cube")
+                                      _ptr(o_fine), _ptr(lse), _ptr(idx), _ptr(means),
+                                      _ptr(do_fine), _ptr(do_coarse), _ptr(dq), _ptr(dk),
+                                      _ptr(dv), _ptr(ws), nws, _stream(dev)), "vsa_backward_cube")
     return dq, dk, dv
 
 
@@ -457,19 +486,22 @@ class VSAFunction(torch.autograd.Function):
     @staticmethod
     def forward(ctx, q, k, v, grid, topk):
         q, k, v = q.contiguous(), k.contiguous(), v.contiguous()
-        o_fine, o_coarse, idx, lse = forward(q, k, v, grid, topk, return_lse=True)
+        B, H, N, d = q.shape
+        means = torch.empty((3, B, H, cube_counts(grid)[0], d), dtype=torch.float32,
+                            device=q.device)
+        o_fine, o_coarse, idx, lse = forward(q, k, v, grid, topk, return_lse=True, means=means)
         o_fine, o_coarse = o_fine.clone(), o_coarse.clone()
-        ctx.save_for_backward(q, k, v, o_fine, lse, idx)
+        ctx.save_for_backward(q, k, v, o_fine, lse, idx, means)
         ctx.grid = grid
         ctx.mark_non_differentiable(idx)
         return o_fine, o_coarse, idx.clone()
 
     @staticmethod
     def backward(ctx, do_fine, do_coarse, _didx):
-        q, k, v, o_fine, lse, idx = ctx.saved_tensors
+        q, k, v, o_fine, lse, idx, means = ctx.saved_tensors
         do_fine = torch.zeros_like(o_fine) if do_fine is None else do_fine.contiguous()
         do_coarse = None if do_coarse is None else do_coarse.contiguous()
-        dq, dk, dv = backward(q, k, v, o_fine, lse, idx, do_fine, do_coarse, ctx.grid)
+        dq, dk, dv = backward(q, k, v, o_fine, lse, idx, do_fine, do_coarse, ctx.grid, means)
         return dq, dk, dv, None, None
 
 

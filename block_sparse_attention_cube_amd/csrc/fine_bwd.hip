@@ -186,7 +186,9 @@ __device__ __forceinline__ void write_cube_rows(const uint16_t* stage, uint16_t*
 // flight per thread) so that the accumulators stay within 64 VGPRs.
 // RASTER = false: q, k, v, dO, O are cube order and dO_coarse is one row per
 // cube (the gradient of a per-cube O_coarse), taken as the cube's sum as is.
-template <int D, bool COARSE, bool RASTER>
+// MEANS = false: the caller holds the means (those of the forward) and q, k,
+// v are not read at all.
+template <int D, bool COARSE, bool MEANS, bool RASTER>
 __global__ __launch_bounds__(256, 8) void bwd_prep_kernel(BwdPrepArgs a, Geo g) {
   constexpr int kCpr = D / 8;                  // 16-byte chunks per row
   constexpr int kRowsPerPass = 256 / kCpr;
@@ -231,19 +233,26 @@ __global__ __launch_bounds__(256, 8) void bwd_prep_kernel(BwdPrepArgs a, Geo g) 
       }
     }
   }
-  if constexpr (COARSE) {
+  if constexpr (COARSE && !MEANS && !RASTER) {
+    // nothing to sum: dO_coarse is already one row per cube
+    if (tid < D) {
+      const int64_t m = (bh * g.C + c) * D + tid;
+      a.docs[m] = __uint_as_float(static_cast<uint32_t>(a.doc[m]) << 16);
+    }
+  } else if constexpr (COARSE) {
     // Column sums of the cube per tensor: the rows of one wave meet by lane
     // shuffles (lanes l, l + kCpr, ... hold the same chunk), the four waves
-    // in LDS.
+    // in LDS.  Tensors t0 .. 3 of (q, k, v, dO_coarse per token).
     const int lane = tid & 63, wave = tid >> 6;
-    constexpr int kSums = RASTER ? 4 : 3;   // q, k, v (and dO_coarse per token)
-    __shared__ float red[4][kSums][D];       // [wave][tensor][dim]
+    constexpr int kT0 = MEANS ? 0 : 3;
+    constexpr int kSums = (RASTER ? 4 : 3) - kT0;
+    __shared__ float red[4][kSums][D];       // [wave][tensor - t0][dim]
     const uint16_t* const src[4] = {a.q, a.k, a.v, a.doc};
 #pragma unroll
     for (int t = 0; t < kSums; ++t) {
       u32x4 val[kPasses];
 #pragma unroll
-      for (int u = 0; u < kPasses; ++u) val[u] = load(src[t], u);
+      for (int u = 0; u < kPasses; ++u) val[u] = load(src[kT0 + t], u);
       float acc[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) acc[i] = 0.f;
@@ -272,10 +281,12 @@ __global__ __launch_bounds__(256, 8) void bwd_prep_kernel(BwdPrepArgs a, Geo g) 
       for (int t = 0; t < kSums; ++t)
         sum[t] = (red[0][t][tid] + red[1][t][tid]) + (red[2][t][tid] + red[3][t][tid]);
       const int64_t m = (bh * g.C + c) * D + tid;
-      a.qm[m] = sum[0] * inv_n;
-      a.km[m] = sum[1] * inv_n;
-      a.vm[m] = sum[2] * inv_n;
-      if constexpr (RASTER) a.docs[m] = sum[3];
+      if constexpr (MEANS) {
+        a.qm[m] = sum[0] * inv_n;
+        a.km[m] = sum[1] * inv_n;
+        a.vm[m] = sum[2] * inv_n;
+      }
+      if constexpr (RASTER) a.docs[m] = sum[kSums - 1];
       else a.docs[m] = __uint_as_float(static_cast<uint32_t>(a.doc[m]) << 16);
     }
   }
@@ -790,14 +801,18 @@ __global__ __launch_bounds__(256, 2) void fine_bwd_dkdv_kernel(BwdFineArgs a, Ge
 }  // namespace
 
 namespace {
+template <int D, bool RASTER>
+hipError_t launch_prep_dim(const Geo& g, const BwdPrepArgs& a, hipStream_t s) {
+  const dim3 grid(g.C, g.B * g.H), block(256);
+  if (a.doc == nullptr)
+    return launch_kernel(bwd_prep_kernel<D, false, false, RASTER>, grid, block, 0, s, a, g);
+  if (a.qm == nullptr)
+    return launch_kernel(bwd_prep_kernel<D, true, false, RASTER>, grid, block, 0, s, a, g);
+  return launch_kernel(bwd_prep_kernel<D, true, true, RASTER>, grid, block, 0, s, a, g);
+}
 template <bool RASTER>
 hipError_t launch_prep_layout(const Geo& g, const BwdPrepArgs& a, hipStream_t s) {
-  const dim3 grid(g.C, g.B * g.H), block(256);
-  if (a.doc != nullptr)
-    return g.D == 128 ? launch_kernel(bwd_prep_kernel<128, true, RASTER>, grid, block, 0, s, a, g)
-                      : launch_kernel(bwd_prep_kernel<64, true, RASTER>, grid, block, 0, s, a, g);
-  return g.D == 128 ? launch_kernel(bwd_prep_kernel<128, false, RASTER>, grid, block, 0, s, a, g)
-                    : launch_kernel(bwd_prep_kernel<64, false, RASTER>, grid, block, 0, s, a, g);
+  return g.D == 128 ? launch_prep_dim<128, RASTER>(g, a, s) : launch_prep_dim<64, RASTER>(g, a, s);
 }
 template <bool RASTER>
 hipError_t launch_fine_layout(const Geo& g, const BwdFineArgs& a, hipStream_t s) {

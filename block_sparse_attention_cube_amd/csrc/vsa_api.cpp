@@ -219,12 +219,24 @@ vsa_status scratch_address(void** out) {
 }
 
 vsa_status forward_launch(const vsa_problem* p, const void* q, const void* k, const void* v,
-                          void* o_fine, void* o_coarse, int32_t* idx, float* lse, void* ws,
-                          hipStream_t stream);
+                          void* o_fine, void* o_coarse, int32_t* idx, float* lse, float* means,
+                          void* ws, hipStream_t stream);
 vsa_status backward_launch(const vsa_problem* p, const void* q, const void* k, const void* v,
                            const void* o_fine, const float* lse, const int32_t* idx,
-                           const void* do_fine, const void* do_coarse, void* dq, void* dk,
-                           void* dv, void* ws, bool raster, hipStream_t stream);
+                           const float* means, const void* do_fine, const void* do_coarse,
+                           void* dq, void* dk, void* dv, void* ws, bool raster,
+                           hipStream_t stream);
+
+// The three [B,H,C,d] fp32 blocks of a caller's means buffer [3,B,H,C,d]
+// (q, k, v), or the workspace's own when the caller passes none.
+struct Means { float* q; float* k; float* v; };
+Means means_of(const vsa_problem* p, const float* means, float* wq, float* wk, float* wv) {
+  if (means == nullptr) return {wq, wk, wv};
+  const Geo g = geometry(p);
+  const size_t n = size_t(g.B) * g.H * g.C * g.D;
+  float* m = const_cast<float*>(means);
+  return {m, m + n, m + 2 * n};
+}
 
 }  // namespace
 
@@ -334,57 +346,62 @@ vsa_status vsa_dense(const vsa_problem* p, const void* qcube, const void* kcube,
 }
 
 vsa_status vsa_forward(const vsa_problem* p, const void* q, const void* k, const void* v,
-                       void* o_fine, void* o_coarse, int32_t* idx, float* lse, void* ws,
-                       size_t ws_bytes, hipStream_t stream) {
+                       void* o_fine, void* o_coarse, int32_t* idx, float* lse, float* means,
+                       void* ws, size_t ws_bytes, hipStream_t stream) {
   vsa_status st = check(p);
   if (st != VSA_OK) return st;
-  if ((st = pointers({q, k, v, o_fine, o_coarse, idx}, {lse})) != VSA_OK) return st;
+  if ((st = pointers({q, k, v, o_fine, o_coarse, idx}, {lse, means})) != VSA_OK) return st;
   if ((st = workspace(p, VSA_OP_FORWARD, ws, ws_bytes)) != VSA_OK) return st;
-  return forward_launch(p, q, k, v, o_fine, o_coarse, idx, lse, ws, stream);
+  return forward_launch(p, q, k, v, o_fine, o_coarse, idx, lse, means, ws, stream);
 }
 
 vsa_status vsa_forward_static(const vsa_problem* p, const void* q, const void* k, const void* v,
                               void* o_fine, void* o_coarse, int32_t* idx, float* lse,
-                              hipStream_t stream) {
+                              float* means, hipStream_t stream) {
   vsa_status st = check(p);
   if (st != VSA_OK) return st;
-  if ((st = pointers({q, k, v, o_fine, o_coarse, idx}, {lse})) != VSA_OK) return st;
+  if ((st = pointers({q, k, v, o_fine, o_coarse, idx}, {lse, means})) != VSA_OK) return st;
   if (vsa_workspace_bytes(p, VSA_OP_FORWARD) > kScratchBytes) return VSA_ERR_WORKSPACE;
   void* ws = nullptr;
   if ((st = scratch_address(&ws)) != VSA_OK) return st;
-  return forward_launch(p, q, k, v, o_fine, o_coarse, idx, lse, ws, stream);
+  return forward_launch(p, q, k, v, o_fine, o_coarse, idx, lse, means, ws, stream);
 }
 
 vsa_status vsa_backward(const vsa_problem* p, const void* q, const void* k, const void* v,
                         const void* o_fine, const float* lse, const int32_t* idx,
-                        const void* do_fine, const void* do_coarse, void* dq, void* dk,
-                        void* dv, void* ws, size_t ws_bytes, hipStream_t stream) {
+                        const float* means, const void* do_fine, const void* do_coarse,
+                        void* dq, void* dk, void* dv, void* ws, size_t ws_bytes,
+                        hipStream_t stream) {
   vsa_status st = check(p);
   if (st != VSA_OK) return st;
-  if ((st = pointers({q, k, v, o_fine, lse, idx, do_fine, dq, dk, dv}, {do_coarse})) != VSA_OK)
+  if ((st = pointers({q, k, v, o_fine, lse, idx, do_fine, dq, dk, dv}, {means, do_coarse})) !=
+      VSA_OK)
     return st;
   if ((st = check_backward(p)) != VSA_OK) return st;
   if ((st = workspace(p, VSA_OP_BACKWARD, ws, ws_bytes)) != VSA_OK) return st;
-  return backward_launch(p, q, k, v, o_fine, lse, idx, do_fine, do_coarse, dq, dk, dv, ws,
+  return backward_launch(p, q, k, v, o_fine, lse, idx, means, do_fine, do_coarse, dq, dk, dv, ws,
                          /*raster=*/true, stream);
 }
 
 vsa_status vsa_forward_cube(const vsa_problem* p, const void* qcube, const void* kcube,
                             const void* vcube, void* o_fine, void* o_coarse, int32_t* idx,
-                            float* lse, void* ws, size_t ws_bytes, hipStream_t stream) {
+                            float* lse, float* means, void* ws, size_t ws_bytes,
+                            hipStream_t stream) {
   vsa_status st = check(p);
   if (st != VSA_OK) return st;
-  if ((st = pointers({qcube, kcube, vcube, o_fine, o_coarse, idx}, {lse})) != VSA_OK) return st;
+  if ((st = pointers({qcube, kcube, vcube, o_fine, o_coarse, idx}, {lse, means})) != VSA_OK)
+    return st;
   if ((st = workspace(p, VSA_OP_FORWARD_CUBE, ws, ws_bytes)) != VSA_OK) return st;
   const Geo g = geometry(p);
   const CoarseWs w = carve_coarse(p, ws, nullptr);
+  const Means m = means_of(p, means, w.qm, w.km, w.vm);
   vsa::ReorderBatch b = {};
   b.x[0] = qcube; b.x[1] = kcube; b.x[2] = vcube;
-  b.mean[0] = w.qm; b.mean[1] = w.km; b.mean[2] = w.vm;
+  b.mean[0] = m.q; b.mean[1] = m.k; b.mean[2] = m.v;
   b.count = 3;
   hipError_t e = vsa::launch_reorder(g, p->dtype, 2, b, stream);
   if (e == hipSuccess)
-    e = vsa::launch_coarse(g, p->dtype, w.qm, w.km, w.vm, o_coarse, idx, nullptr, stream);
+    e = vsa::launch_coarse(g, p->dtype, m.q, m.k, m.v, o_coarse, idx, nullptr, stream);
   if (e == hipSuccess)
     e = vsa::launch_fine(g, p->dtype, qcube, kcube, vcube, idx, o_fine, lse, /*raster=*/false,
                          nullptr, nullptr, stream);
@@ -393,18 +410,18 @@ vsa_status vsa_forward_cube(const vsa_problem* p, const void* qcube, const void*
 
 vsa_status vsa_backward_cube(const vsa_problem* p, const void* qcube, const void* kcube,
                              const void* vcube, const void* o_fine, const float* lse,
-                             const int32_t* idx, const void* do_fine, const void* do_coarse,
-                             void* dq, void* dk, void* dv, void* ws, size_t ws_bytes,
-                             hipStream_t stream) {
+                             const int32_t* idx, const float* means, const void* do_fine,
+                             const void* do_coarse, void* dq, void* dk, void* dv, void* ws,
+                             size_t ws_bytes, hipStream_t stream) {
   vsa_status st = check(p);
   if (st != VSA_OK) return st;
-  if ((st = pointers({qcube, kcube, vcube, o_fine, lse, idx, do_fine, dq, dk, dv}, {do_coarse})) !=
-      VSA_OK)
+  if ((st = pointers({qcube, kcube, vcube, o_fine, lse, idx, do_fine, dq, dk, dv},
+                     {means, do_coarse})) != VSA_OK)
     return st;
   if ((st = check_backward(p)) != VSA_OK) return st;
   if ((st = workspace(p, VSA_OP_BACKWARD_CUBE, ws, ws_bytes)) != VSA_OK) return st;
-  return backward_launch(p, qcube, kcube, vcube, o_fine, lse, idx, do_fine, do_coarse, dq, dk, dv,
-                         ws, /*raster=*/false, stream);
+  return backward_launch(p, qcube, kcube, vcube, o_fine, lse, idx, means, do_fine, do_coarse, dq,
+                         dk, dv, ws, /*raster=*/false, stream);
 }
 
 }  // extern "C"
@@ -414,20 +431,21 @@ namespace {
 // The launch sequence of vsa_forward on a validated problem and a workspace
 // of vsa_workspace_bytes(p, VSA_OP_FORWARD) bytes.
 vsa_status forward_launch(const vsa_problem* p, const void* q, const void* k, const void* v,
-                          void* o_fine, void* o_coarse, int32_t* idx, float* lse, void* ws,
-                          hipStream_t stream) {
+                          void* o_fine, void* o_coarse, int32_t* idx, float* lse, float* means,
+                          void* ws, hipStream_t stream) {
   const Geo g = geometry(p);
   const FwdWs w = carve_forward(p, ws, nullptr);
+  const Means m = means_of(p, means, w.qm, w.km, w.vm);   // the caller's buffer, if any
   const bool bf16 = p->dtype == VSA_BF16;
   vsa::ReorderBatch b = {};
   b.x[0] = q; b.x[1] = k; b.x[2] = v;
   b.y[0] = w.qc; b.y[1] = w.kc; b.y[2] = w.vc;
-  b.mean[0] = w.qm; b.mean[1] = w.km; b.mean[2] = w.vm;
+  b.mean[0] = m.q; b.mean[1] = m.k; b.mean[2] = m.v;
   b.count = 3;
   // bf16: pool only (the fine kernel gathers from raster); fp32: cube-order copies + means
   hipError_t e = vsa::launch_reorder(g, p->dtype, bf16 ? 3 : 0, b, stream);
   if (e == hipSuccess)
-    e = vsa::launch_coarse(g, p->dtype, w.qm, w.km, w.vm, w.oc, idx, nullptr, stream);
+    e = vsa::launch_coarse(g, p->dtype, m.q, m.k, m.v, w.oc, idx, nullptr, stream);
   if (e == hipSuccess)
     e = vsa::launch_fine(g, p->dtype, bf16 ? q : w.qc, bf16 ? k : w.kc, bf16 ? v : w.vc, idx,
                          o_fine, lse, /*raster=*/true, w.oc, o_coarse, stream);
@@ -438,8 +456,9 @@ vsa_status forward_launch(const vsa_problem* p, const void* q, const void* k, co
 // validated problem and workspace.
 vsa_status backward_launch(const vsa_problem* p, const void* q, const void* k, const void* v,
                            const void* o_fine, const float* lse, const int32_t* idx,
-                           const void* do_fine, const void* do_coarse, void* dq, void* dk,
-                           void* dv, void* ws, bool raster, hipStream_t stream) {
+                           const float* means, const void* do_fine, const void* do_coarse,
+                           void* dq, void* dk, void* dv, void* ws, bool raster,
+                           hipStream_t stream) {
   const Geo g = geometry(p);
   const BwdWs w = carve_backward(p, ws, nullptr);
   auto b16 = [](const void* x) { return static_cast<const uint16_t*>(x); };
@@ -449,12 +468,15 @@ vsa_status backward_launch(const vsa_problem* p, const void* q, const void* k, c
   pa.lse = lse;
   pa.delta = w.delta;
   pa.lse2 = w.lse2;
-  pa.qm = w.qm; pa.km = w.km; pa.vm = w.vm; pa.docs = w.docs;
+  // with the forward's means the preparation pass does not read q, k, v
+  const Means m = means_of(p, means, w.qm, w.km, w.vm);
+  pa.qm = means ? nullptr : w.qm; pa.km = means ? nullptr : w.km; pa.vm = means ? nullptr : w.vm;
+  pa.docs = w.docs;
   hipError_t e = vsa::launch_bwd_prep(g, pa, raster, stream);
   const bool coarse = do_coarse != nullptr;
   // the coarse backward builds the block lists in spare workgroups when it runs
   if (e == hipSuccess && coarse)
-    e = vsa::launch_coarse_bwd(g, w.qm, w.km, w.vm, w.docs, w.stats, w.dqc, w.dkc, w.dvc, idx,
+    e = vsa::launch_coarse_bwd(g, m.q, m.k, m.v, w.docs, w.stats, w.dqc, w.dkc, w.dvc, idx,
                                w.offsets, w.list, w.order, stream);
   if (e == hipSuccess && !(coarse && vsa::coarse_bwd_builds_lists(g)))
     e = vsa::launch_idx_transpose(g, idx, w.offsets, w.list, w.order, stream);

@@ -15,7 +15,8 @@ struct BwdPrepArgs {
   const float* lse;      // [B,H,Np] forward log-sum-exp (natural log)
   float* delta;          // [B,H,Np] rowsum(dO * O), 0 on pad slots
   float* lse2;           // [B,H,Np] lse * log2(e), +inf on pad slots (their P is 0)
-  float* qm; float* km; float* vm;   // [B,H,C,D] means over valid slots
+  float* qm; float* km; float* vm;   // [B,H,C,D] means over valid slots, or all
+                                     // nullptr when the caller holds them
   float* docs;           // [B,H,C,D] sums of dO_coarse over valid slots
 };
 hipError_t launch_bwd_prep(const Geo& g, const BwdPrepArgs& a, bool raster, hipStream_t s);

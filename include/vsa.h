@@ -179,9 +179,13 @@ vsa_status vsa_dense(const vsa_problem* p, const void* qcube, const void* kcube,
  *   o_coarse  : [B,H,N,d] out, raster; token r holds its cube's coarse row.
  *   idx       : [B,H,C,topk] int32 out, ascending (as vsa_coarse).
  *   lse       : [B,H,Np] fp32 out in cube order (for vsa_backward), or NULL.
+ *   means     : [3,B,H,C,d] fp32 out, the per-cube means of q, k and v over
+ *               the valid slots (the pooled operands of the coarse stage), or
+ *               NULL.  Handing them to vsa_backward spares it a pass over q,
+ *               k and v; writing them costs the forward nothing extra.
  *   ws        : vsa_workspace_bytes(p, VSA_OP_FORWARD) bytes. */
 vsa_status vsa_forward(const vsa_problem* p, const void* q, const void* k, const void* v,
-                       void* o_fine, void* o_coarse, int32_t* idx, float* lse,
+                       void* o_fine, void* o_coarse, int32_t* idx, float* lse, float* means,
                        void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* vsa_forward without a workspace argument, for callers that cannot
@@ -199,7 +203,7 @@ vsa_status vsa_forward(const vsa_problem* p, const void* q, const void* k, const
  * written earlier in the same call. */
 vsa_status vsa_forward_static(const vsa_problem* p, const void* q, const void* k,
                               const void* v, void* o_fine, void* o_coarse, int32_t* idx,
-                              float* lse, hipStream_t stream);
+                              float* lse, float* means, hipStream_t stream);
 
 /* Backward of vsa_forward, the trainable path (VSA trains in place of
  * FlashAttention, section on why sparse attention fails under
@@ -215,13 +219,16 @@ vsa_status vsa_forward_static(const vsa_problem* p, const void* q, const void* k
  *           of a cube receives that cube's gradient divided by its valid count.
  *   q, k, v, o_fine, do_fine, do_coarse : [B,H,N,d] raster (do_coarse may be
  *           NULL, meaning zero); lse [B,H,Np] and idx as written by vsa_forward.
+ *   means : [3,B,H,C,d] fp32 as written by vsa_forward for the same q, k, v,
+ *           or NULL: then the means are recomputed from q, k and v.  Only the
+ *           coarse gradients use them (ignored when do_coarse is NULL).
  *   dq, dk, dv : [B,H,N,d] raster out (overwritten).
  * Deterministic: no floating-point atomics; repeated calls give the same bits.
  * Implemented for VSA_BF16 (C <= 4096 cubes, as every entry point); other problems return
  * VSA_ERR_UNSUPPORTED before anything is enqueued. */
 vsa_status vsa_backward(const vsa_problem* p, const void* q, const void* k, const void* v,
                         const void* o_fine, const float* lse, const int32_t* idx,
-                        const void* do_fine, const void* do_coarse,
+                        const float* means, const void* do_fine, const void* do_coarse,
                         void* dq, void* dk, void* dv,
                         void* ws, size_t ws_bytes, hipStream_t stream);
 
@@ -238,27 +245,28 @@ vsa_status vsa_backward(const vsa_problem* p, const void* q, const void* k, cons
  *                         (vsa_reorder writes zeros) and are never attended to.
  *   o_fine              : [B,H,Np,d] out, cube order (pad rows unspecified).
  *   o_coarse            : [B,H,C,d] out, one row per cube.
- *   idx, lse            : as vsa_forward.
+ *   idx, lse, means     : as vsa_forward.
  *   ws                  : vsa_workspace_bytes(p, VSA_OP_FORWARD_CUBE) bytes.
  * Equals vsa_forward followed by vsa_reorder of o_fine (bf16 and fp32). */
 vsa_status vsa_forward_cube(const vsa_problem* p, const void* qcube, const void* kcube,
                             const void* vcube, void* o_fine, void* o_coarse, int32_t* idx,
-                            float* lse, void* ws, size_t ws_bytes, hipStream_t stream);
+                            float* lse, float* means, void* ws, size_t ws_bytes,
+                            hipStream_t stream);
 
 /* Backward of vsa_forward_cube: gradients of
  * sum(o_fine*do_fine) + sum(o_coarse*do_coarse) w.r.t. qcube, kcube, vcube with
  * idx held constant (the definitions of vsa_backward, with dOc = do_coarse).
  *   qcube, kcube, vcube, o_fine, do_fine : [B,H,Np,d] cube order (pad slots finite).
  *   do_coarse : [B,H,C,d], one row per cube, or NULL (zero).
- *   lse, idx  : as written by vsa_forward_cube.
+ *   lse, idx  : as written by vsa_forward_cube; means as written by it, or NULL.
  *   dq, dk, dv: [B,H,Np,d] out, cube order, zero on pad slots.
  *   ws        : vsa_workspace_bytes(p, VSA_OP_BACKWARD_CUBE) bytes.
  * Limits of vsa_backward (VSA_BF16). */
 vsa_status vsa_backward_cube(const vsa_problem* p, const void* qcube, const void* kcube,
                              const void* vcube, const void* o_fine, const float* lse,
-                             const int32_t* idx, const void* do_fine, const void* do_coarse,
-                             void* dq, void* dk, void* dv, void* ws, size_t ws_bytes,
-                             hipStream_t stream);
+                             const int32_t* idx, const float* means, const void* do_fine,
+                             const void* do_coarse, void* dq, void* dk, void* dv, void* ws,
+                             size_t ws_bytes, hipStream_t stream);
 
 /* ---- FP8 fine stage ----------------------------------------------------
  * The pages note that sparse attention and low-bit attention are orthogonal

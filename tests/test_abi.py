@@ -59,8 +59,8 @@ def test_problem_validation(kw, status):
 def test_null_problem():
     assert L.lib().vsa_check_problem(None) == L.VSA_ERR_NULL
     assert L.lib().vsa_workspace_bytes(None, L.VSA_OP_FORWARD) == 0
-    assert L.lib().vsa_forward(None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, 1 << 40,
-                               None) == L.VSA_ERR_NULL
+    assert L.lib().vsa_forward(None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, FAKE,
+                               1 << 40, None) == L.VSA_ERR_NULL
 
 
 def test_workspace_sizes():
@@ -81,16 +81,21 @@ def test_forward_argument_errors():
     lib = L.lib()
     p = prob()
     big = 1 << 40
+    # arguments after the problem: q k v o_fine o_coarse idx lse means ws ws_bytes stream
     call = lambda *a: lib.vsa_forward(ctypes.byref(p), *a)
-    assert call(None, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, big, None) == L.VSA_ERR_NULL
-    assert call(FAKE, FAKE, FAKE, FAKE, None, FAKE, None, FAKE, big, None) == L.VSA_ERR_NULL
-    assert call(MISALIGNED, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, big, None) == L.VSA_ERR_ALIGN
-    assert call(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, MISALIGNED, FAKE, big, None) == L.VSA_ERR_ALIGN
-    assert call(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, big, None) == L.VSA_ERR_NULL
-    assert call(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, 1024, None) == L.VSA_ERR_WORKSPACE
+    ok = (FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, FAKE, big, None)
+    def with_(i, x):
+        a = list(ok); a[i] = x
+        return call(*a)
+    assert with_(0, None) == L.VSA_ERR_NULL
+    assert with_(4, None) == L.VSA_ERR_NULL
+    assert with_(0, MISALIGNED) == L.VSA_ERR_ALIGN
+    assert with_(6, MISALIGNED) == L.VSA_ERR_ALIGN     # lse
+    assert with_(7, MISALIGNED) == L.VSA_ERR_ALIGN     # means
+    assert with_(8, None) == L.VSA_ERR_NULL            # workspace
+    assert with_(9, 1024) == L.VSA_ERR_WORKSPACE
     bad = prob(topk=0)
-    assert lib.vsa_forward(ctypes.byref(bad), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE,
-                           big, None) == L.VSA_ERR_SHAPE
+    assert lib.vsa_forward(ctypes.byref(bad), *ok) == L.VSA_ERR_SHAPE
 
 
 def test_other_entry_points_validate_first():
@@ -110,8 +115,11 @@ def test_other_entry_points_validate_first():
     bad = prob(d=80)
     assert lib.vsa_fine(ctypes.byref(bad), FAKE, FAKE, FAKE, FAKE, FAKE, None, None, 0,
                         None) == L.VSA_ERR_UNSUPPORTED
-    assert lib.vsa_backward(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, None,
+    # q k v o_fine lse idx means do_fine do_coarse dq dk dv ws ws_bytes stream
+    assert lib.vsa_backward(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, None, FAKE, None, FAKE, None,
                             FAKE, FAKE, FAKE, FAKE, big, None) == L.VSA_ERR_NULL
+    assert lib.vsa_backward(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, MISALIGNED, FAKE,
+                            None, FAKE, FAKE, FAKE, FAKE, big, None) == L.VSA_ERR_ALIGN
 
 
 def test_reorder_direction_codes():

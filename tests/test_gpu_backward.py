@@ -50,13 +50,24 @@ def grid(w):
     return (w.T, w.Hh, w.Ww)
 
 
-def run(w, with_coarse=True):
+def means_like(w):
+    return torch.full((3, w.B, w.H, w.C, w.d), float("nan"), dtype=torch.float32, device=DEV)
+
+
+def run(w, with_coarse=True, keep_means=False):
+    """Forward then backward; keep_means: the forward writes its per-cube
+    means and the backward takes them instead of recomputing them."""
     x = inputs.make_inputs(w, seed=0, grads=True)
     t = {n: inputs.as_torch(a, w.dtype, DEV) for n, a in x.items()}
-    o_fine, o_coarse, idx, lse = vsa.forward(t["q"], t["k"], t["v"], grid(w), w.topk)
+    means = means_like(w) if keep_means else None
+    o_fine, o_coarse, idx, lse = vsa.forward(t["q"], t["k"], t["v"], grid(w), w.topk,
+                                             means=means)
     doc = t["do_coarse"] if with_coarse else None
-    dq, dk, dv = vsa.backward(t["q"], t["k"], t["v"], o_fine, lse, idx, t["do_fine"], doc, grid(w))
+    dq, dk, dv = vsa.backward(t["q"], t["k"], t["v"], o_fine, lse, idx, t["do_fine"], doc, grid(w),
+                              means=means)
     torch.cuda.synchronize()
+    if keep_means:
+        t["means"] = means
     return x, t, (o_fine, o_coarse, idx, lse), (dq, dk, dv)
 
 
@@ -101,6 +112,29 @@ def test_backward_fine_branch_only(w):
         assert_close(got.float().cpu().numpy(), want, w.dtype, name)
 
 
+MEANS_CASES = [configs.SWEEP[2], EDGE[0], EDGE[1]]
+
+
+@pytest.mark.parametrize("w", MEANS_CASES, ids=[w.name for w in MEANS_CASES])
+def test_backward_with_the_forward_means(w):
+    """The forward's per-cube means (the pooled q, k, v of the coarse stage)
+    against the oracle's pool, and the gradients of a backward that takes them
+    instead of reading q, k, v again."""
+    x, t, (_, _, idx, _), grads = run(w, keep_means=True)
+    g = vo.geometry(w.T, w.Hh, w.Ww)
+    for i, n in enumerate("qkv"):
+        want = vo.pool(vo.reorder(np.asarray(x[n], dtype=np.float64), g), g)
+        got = t["means"][i].double().cpu().numpy()
+        # a mean of at most 64 bf16 values summed in fp32: each partial sum is
+        # rounded once, relative 2^-24 per addition
+        bound = 64 * 2.0 ** -24 * np.abs(np.asarray(x[n], dtype=np.float64)).max() + 1e-30
+        assert np.abs(got - want).max() <= bound, f"{n} means"
+    gidx = idx.cpu().numpy()
+    ref = vo.backward(x["q"], x["k"], x["v"], x["do_fine"], x["do_coarse"], w.T, w.Hh, w.Ww, gidx)
+    for name, got, want in zip(("dq", "dk", "dv"), grads, ref):
+        assert_close(got.float().cpu().numpy(), want, w.dtype, name)
+
+
 def test_backward_is_deterministic():
     w = configs.SWEEP[0]
     _, t, (o_fine, _, idx, lse), first = run(w)
@@ -111,8 +145,9 @@ def test_backward_is_deterministic():
 
 
 def test_autograd_function_matches_direct_calls():
+    # the Function hands the forward's means to its backward, as run() does here
     w = EDGE[0]
-    x, t, (o_fine, o_coarse, idx, lse), grads = run(w)
+    x, t, (o_fine, o_coarse, idx, lse), grads = run(w, keep_means=True)
     q, k, v = (t[n].clone().requires_grad_(True) for n in "qkv")
     of, oc, idx2 = vsa.vsa_attention(q, k, v, grid(w), w.topk)
     assert torch.equal(of, o_fine) and torch.equal(oc, o_coarse) and torch.equal(idx2, idx)

@@ -37,7 +37,9 @@ def test_cube_order_forward_and_backward(w):
     g = vo.geometry(w.T, w.Hh, w.Ww)
     t = {n: inputs.as_torch(x[n], w.dtype, DEV) for n in x}
     cube = {n: vsa.reorder(t[n], grid(w)) for n in ("q", "k", "v", "do_fine")}
-    o, oc, idx, lse = vsa.forward_cube(cube["q"], cube["k"], cube["v"], grid(w), w.topk)
+    means = torch.empty((3, w.B, w.H, g["C"], w.d), dtype=torch.float32, device=DEV)
+    o, oc, idx, lse = vsa.forward_cube(cube["q"], cube["k"], cube["v"], grid(w), w.topk,
+                                       means=means)
     torch.cuda.synchronize()
     ref = vo.forward(x["q"], x["k"], x["v"], w.T, w.Hh, w.Ww, w.topk)
     gidx = idx.cpu().numpy()
@@ -55,14 +57,16 @@ def test_cube_order_forward_and_backward(w):
                        o[..., torch.from_numpy(valid).to(DEV), :])
 
     # backward with a per-cube dO_coarse (a bf16 [B,H,C,d] drawn from the recipe's stream)
+    # (means recomputed from the inputs, then the forward's means handed over)
     doc = inputs.as_torch(x["do_coarse"][:, :, :g["C"]], w.dtype, DEV).contiguous()
-    dq, dk, dv = vsa.backward_cube(cube["q"], cube["k"], cube["v"], o, lse, idx,
-                                   cube["do_fine"], doc, grid(w))
-    torch.cuda.synchronize()
     doc64 = doc.double().cpu().numpy()
     spread = doc64[:, :, g["cube_of_token"], :] / g["n_valid"][g["cube_of_token"]][:, None]
     want = vo.backward(x["q"], x["k"], x["v"], x["do_fine"], spread, w.T, w.Hh, w.Ww, gidx)
-    for name, got, ref_r in zip(("dq", "dk", "dv"), (dq, dk, dv), want):
-        gc = got.float().cpu().numpy()
-        assert_close(gc, vo.reorder(ref_r, g), w.dtype, f"{name} cube order", rows=valid)
-        assert np.all(gc[..., ~valid, :] == 0), f"{name}: pad rows are not zero"
+    for m in (None, means):
+        dq, dk, dv = vsa.backward_cube(cube["q"], cube["k"], cube["v"], o, lse, idx,
+                                       cube["do_fine"], doc, grid(w), means=m)
+        torch.cuda.synchronize()
+        for name, got, ref_r in zip(("dq", "dk", "dv"), (dq, dk, dv), want):
+            gc = got.float().cpu().numpy()
+            assert_close(gc, vo.reorder(ref_r, g), w.dtype, f"{name} cube order", rows=valid)
+            assert np.all(gc[..., ~valid, :] == 0), f"{name}: pad rows are not zero"

@@ -47,5 +47,5 @@ def test_static_forward_rejects_problems_beyond_its_scratch():
     p = vsa.make_problem(w.B, w.H, (w.T, w.Hh, w.Ww), w.d, w.topk, torch.bfloat16)
     fake = ctypes.c_void_p(0x1000)   # never dereferenced: the size check comes first
     st = L.lib().vsa_forward_static(ctypes.byref(p), fake, fake, fake, fake, fake, fake, None,
-                                    None)
+                                    None, None)
     assert st == L.VSA_ERR_WORKSPACE
