@@ -381,13 +381,13 @@ __global__ __launch_bounds__(256) void idx_transpose_kernel(const int32_t* __res
 // Pad key slots get P = 0 as in the forward: a -inf accumulator init for the
 // (ih, iw) part, a -inf exp2 offset for key tiles past the cube's t extent,
 // extents read per step from a per-lane table.
+// tile = bh * C + query cube; smem: 4 K/V tiles, [2 slots][K | V].
 template <int D, bool RASTER>
-__global__ __launch_bounds__(256, 2) void fine_bwd_dq_kernel(BwdFineArgs a, Geo g) {
+__device__ __forceinline__ void dq_tile(const BwdFineArgs& a, const Geo& g, int tile,
+                                        uint16_t* smem) {
   using Tl = BwdTile<D>;
   constexpr int kKS = D / 32, kDT = D / 16, kOS = D + 8, kT = Tl::kElems;
-  __shared__ __attribute__((aligned(16))) uint16_t smem[4 * kT];   // [2 slots][K | V]
 
-  const int tile = xcd_remap(blockIdx.x, gridDim.x);
   const int64_t bh = tile / g.C;
   const int qc = tile % g.C;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -580,16 +580,14 @@ __global__ __launch_bounds__(256, 2) void fine_bwd_dq_kernel(BwdFineArgs a, Geo 
 // and dO tiles and its 64 lse2 / delta values go straight into a 2-slot LDS
 // ring by DMA; Q^T and dO^T come from transposed reads.  Pad query slots
 // have lse2 = +inf (P = 0) and zero dO rows, so they add nothing.
+// tile = bh * C + rank of the key cube in the head's order (descending
+// selection counts); smem: [2 slots][Q | dO]; stat: [slot][lse2 | delta][q].
 template <int D, bool RASTER>
-__global__ __launch_bounds__(256, 2) void fine_bwd_dkdv_kernel(BwdFineArgs a, Geo g) {
+__device__ __forceinline__ void dkdv_tile(const BwdFineArgs& a, const Geo& g, int tile,
+                                          uint16_t* smem, float (*stat)[2][64]) {
   using Tl = BwdTile<D>;
   constexpr int kKS = D / 32, kDT = D / 16, kOS = D + 8, kT = Tl::kElems;
-  __shared__ __attribute__((aligned(16))) uint16_t smem[4 * kT];   // [2 slots][Q | dO]
-  __shared__ __attribute__((aligned(16))) float stat[2][2][64];    // [slot][lse2 | delta][q]
 
-  // key cubes in descending order of their selection counts within each
-  // head, so that the longest lists start first and short ones fill the tail
-  const int tile = xcd_remap(blockIdx.x, gridDim.x);
   const int64_t bh = tile / g.C;
   const int kc = __builtin_amdgcn_readfirstlane(a.order[bh * g.C + tile % g.C]);
   const int tid = threadIdx.x, lane = tid & 63;
@@ -798,6 +796,23 @@ __global__ __launch_bounds__(256, 2) void fine_bwd_dkdv_kernel(BwdFineArgs a, Ge
   write_cube_rows<D, RASTER>(stage_v, a.dv, g, bh, kc, tid);
 }
 
+// dQ and dK/dV in one launch.  Logical tile t of 2 B H C: per head the C
+// dK/dV tiles (longest block lists first) and then its C dQ tiles, so that
+// dQ tiles take the slots that the short lists of a head leave free while its
+// long lists still run, and both kinds of tile of a head share one XCD's L2
+// (every head's q, k, v and dO rows are read by both).
+template <int D, bool RASTER>
+__global__ __launch_bounds__(256, 2) void fine_bwd_kernel(BwdFineArgs a, Geo g) {
+  __shared__ __attribute__((aligned(16))) uint16_t smem[4 * BwdTile<D>::kElems];
+  __shared__ __attribute__((aligned(16))) float stat[2][2][64];
+  const int t = xcd_remap(blockIdx.x, gridDim.x);
+  const int bh = t / (2 * g.C), r = t - bh * (2 * g.C);
+  if (r < g.C)
+    dkdv_tile<D, RASTER>(a, g, bh * g.C + r, smem, stat);
+  else
+    dq_tile<D, RASTER>(a, g, bh * g.C + (r - g.C), smem);
+}
+
 }  // namespace
 
 namespace {
@@ -816,13 +831,9 @@ hipError_t launch_prep_layout(const Geo& g, const BwdPrepArgs& a, hipStream_t s)
 }
 template <bool RASTER>
 hipError_t launch_fine_layout(const Geo& g, const BwdFineArgs& a, hipStream_t s) {
-  const dim3 grid(g.B * g.H * g.C), block(256);
-  hipError_t e = g.D == 128
-                     ? launch_kernel(fine_bwd_dq_kernel<128, RASTER>, grid, block, 0, s, a, g)
-                     : launch_kernel(fine_bwd_dq_kernel<64, RASTER>, grid, block, 0, s, a, g);
-  if (e != hipSuccess) return e;
-  return g.D == 128 ? launch_kernel(fine_bwd_dkdv_kernel<128, RASTER>, grid, block, 0, s, a, g)
-                    : launch_kernel(fine_bwd_dkdv_kernel<64, RASTER>, grid, block, 0, s, a, g);
+  const dim3 grid(2 * g.B * g.H * g.C), block(256);
+  return g.D == 128 ? launch_kernel(fine_bwd_kernel<128, RASTER>, grid, block, 0, s, a, g)
+                    : launch_kernel(fine_bwd_kernel<64, RASTER>, grid, block, 0, s, a, g);
 }
 }  // namespace
 

@@ -27,7 +27,7 @@ vsa_status check(const vsa_problem* p) {
   if (p->topk < 1 || p->topk > C) return VSA_ERR_SHAPE;
   const int64_t bh = int64_t(p->B) * p->H;
   if (bh > 65535) return VSA_ERR_UNSUPPORTED;                 // grid y extent
-  if (bh * C > (int64_t(1) << 30)) return VSA_ERR_UNSUPPORTED; // 1-D tile grid
+  if (bh * C > (int64_t(1) << 29)) return VSA_ERR_UNSUPPORTED; // 1-D grids of 2 B H C
   // B*H*Np*d elements must stay far from int64 overflow
   if (bh * C * 64 * p->d > (int64_t(1) << 58)) return VSA_ERR_UNSUPPORTED;
   // in-cube raster offsets (elements) are 32-bit: 4 frames of the grid
