@@ -405,17 +405,19 @@ __device__ __forceinline__ void dq_tile(const BwdFineArgs& a, const Geo& g, int 
   const int64_t qrow = bh * g.Np + static_cast<int64_t>(qc) * 64 + qslot;   // cube-order stats
   const int64_t head0 = bh * (RASTER ? g.N : g.Np) * D;   // q, k, v, dO rows of this head
 
-  // DMA byte offsets (from a key cube's first raster row) of this thread's
-  // chunks; alt: the same chunk of the first row, for pad slots
-  uint32_t off[Tl::kDma], alt[Tl::kDma];
+  // DMA byte offsets (from a key cube's first row) of this thread's chunks;
+  // a pad slot of a raster edge cube reads its own raster address (a token
+  // of a neighbouring row or frame, or zeros past the head's rows), a
+  // finite value whose probability is exactly 0
+  uint32_t off[Tl::kDma];
 #pragma unroll
   for (int u = 0; u < Tl::kDma; ++u) {
     const int P = u * 256 + tid;
     const int r = P / Tl::kKC;
     int it, ih, iw;
     dma_slot<D>(u, wave, lane, it, ih, iw);
-    alt[u] = static_cast<uint32_t>(row_offset<D>(r, P % Tl::kKC) - r * D) * 2u;
-    off[u] = static_cast<uint32_t>(slot_row<RASTER>(g, it, ih, iw) * D) * 2u + alt[u];
+    off[u] = static_cast<uint32_t>(slot_row<RASTER>(g, it, ih, iw) * D) * 2u +
+             static_cast<uint32_t>(row_offset<D>(r, P % Tl::kKC) - r * D) * 2u;
   }
   const uint32_t head_bytes = static_cast<uint32_t>((RASTER ? g.N : g.Np) * D * 2);
   const __amdgpu_buffer_rsrc_t krs = head_rsrc(a.k + head0, head_bytes);
@@ -462,24 +464,11 @@ __device__ __forceinline__ void dq_tile(const BwdFineArgs& a, const Geo& g, int 
 #pragma unroll
   for (int dt = 0; dt < kDT; ++dt) dacc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // stage K and V of step n (pad slots of an edge cube read its first row)
+  // stage K and V of step n
   auto stage = [&](int n, uint16_t* slot) {
-    const int ext = __builtin_amdgcn_readlane(ext_lanes, n & 63);
     const uint32_t row_bytes = static_cast<uint32_t>(__builtin_amdgcn_readlane(row_lanes, n & 63)) * (D * 2);
-    if (!RASTER || ext == kFull) {
-      dma_rows<D>(krs, row_bytes, off, slot, wave);
-      dma_rows<D>(vrs, row_bytes, off, slot + kT, wave);
-    } else {
-      uint32_t eoff[Tl::kDma];
-#pragma unroll
-      for (int u = 0; u < Tl::kDma; ++u) {
-        int it, ih, iw;
-        dma_slot<D>(u, wave, lane, it, ih, iw);
-        eoff[u] = (it < (ext & 7) && ih < ((ext >> 3) & 7) && iw < (ext >> 6)) ? off[u] : alt[u];
-      }
-      dma_rows<D>(krs, row_bytes, eoff, slot, wave);
-      dma_rows<D>(vrs, row_bytes, eoff, slot + kT, wave);
-    }
+    dma_rows<D>(krs, row_bytes, off, slot, wave);
+    dma_rows<D>(vrs, row_bytes, off, slot + kT, wave);
   };
   stage(0, smem);
   // one step per selected key cube, unrolled by two so that the ring slot
@@ -597,17 +586,18 @@ __device__ __forceinline__ void dkdv_tile(const BwdFineArgs& a, const Geo& g, in
   const int64_t head0 = bh * (RASTER ? g.N : g.Np) * D;   // q, k, v, dO rows of this head
   const int64_t stat0 = bh * g.Np;      // cube-order lse2 / delta of this head
 
-  // DMA byte offsets (from a query cube's first raster row) of this
-  // thread's chunks; alt: the same chunk of the first row, for pad slots
-  uint32_t off[Tl::kDma], alt[Tl::kDma];
+  // DMA byte offsets (from a query cube's first row) of this thread's
+  // chunks; a pad slot of a raster edge cube reads its own raster address (a
+  // finite value, see dq_tile), and its lse2 of +inf makes its P exactly 0
+  uint32_t off[Tl::kDma];
 #pragma unroll
   for (int u = 0; u < Tl::kDma; ++u) {
     const int P = u * 256 + tid;
     const int r = P / Tl::kKC;
     int it, ih, iw;
     dma_slot<D>(u, wave, lane, it, ih, iw);
-    alt[u] = static_cast<uint32_t>(row_offset<D>(r, P % Tl::kKC) - r * D) * 2u;
-    off[u] = static_cast<uint32_t>(slot_row<RASTER>(g, it, ih, iw) * D) * 2u + alt[u];
+    off[u] = static_cast<uint32_t>(slot_row<RASTER>(g, it, ih, iw) * D) * 2u +
+             static_cast<uint32_t>(row_offset<D>(r, P % Tl::kKC) - r * D) * 2u;
   }
   const uint32_t head_bytes = static_cast<uint32_t>((RASTER ? g.N : g.Np) * D * 2);
   const __amdgpu_buffer_rsrc_t qrs = head_rsrc(a.q + head0, head_bytes);
@@ -645,43 +635,25 @@ __device__ __forceinline__ void dkdv_tile(const BwdFineArgs& a, const Geo& g, in
   const int32_t* off_l = a.offsets + bh * (g.C + 1);
   const int beg = off_l[kc], end = off_l[kc + 1];
   const int32_t* lst = a.list + bh * g.C * g.K;
-  // extents (nt | nh << 3 | nw << 6) and first raster rows of the listed
-  // query cubes, 64 steps per lane vector
-  constexpr int kFull = 4 | (4 << 3) | (4 << 6);
-  int ext_lanes = kFull, row_lanes = 0, cube_lanes = 0;
+  // first rows and indices of the listed query cubes, 64 steps per lane
+  // vector
+  int row_lanes = 0, cube_lanes = 0;
   auto cubes = [&](int first) {   // list positions beg + first ...
     const int m = beg + first + lane;
-    ext_lanes = kFull;
     row_lanes = 0;
     cube_lanes = 0;
     if (m < end) {
       const int c = lst[m];
-      const CubeExt e = cube_extent(g, c);
-      ext_lanes = e.nt | (e.nh << 3) | (e.nw << 6);
-      row_lanes = cube_row<RASTER>(g, e, c);
+      row_lanes = cube_row<RASTER>(g, cube_extent(g, c), c);
       cube_lanes = c;
     }
   };
-  // stage Q, dO (pad slots of an edge cube read its first row) and the
-  // statistics of list position beg + i
+  // stage Q, dO and the statistics of list position beg + i
   auto stage = [&](int i, int slot) {
-    const int ext = __builtin_amdgcn_readlane(ext_lanes, i & 63);
     const uint32_t row_bytes = static_cast<uint32_t>(__builtin_amdgcn_readlane(row_lanes, i & 63)) * (D * 2);
     uint16_t* const dst = smem + slot * 2 * kT;
-    if (!RASTER || ext == kFull) {
-      dma_rows<D>(qrs, row_bytes, off, dst, wave);
-      dma_rows<D>(ors, row_bytes, off, dst + kT, wave);
-    } else {
-      uint32_t eoff[Tl::kDma];
-#pragma unroll
-      for (int u = 0; u < Tl::kDma; ++u) {
-        int it, ih, iw;
-        dma_slot<D>(u, wave, lane, it, ih, iw);
-        eoff[u] = (it < (ext & 7) && ih < ((ext >> 3) & 7) && iw < (ext >> 6)) ? off[u] : alt[u];
-      }
-      dma_rows<D>(qrs, row_bytes, eoff, dst, wave);
-      dma_rows<D>(ors, row_bytes, eoff, dst + kT, wave);
-    }
+    dma_rows<D>(qrs, row_bytes, off, dst, wave);
+    dma_rows<D>(ors, row_bytes, off, dst + kT, wave);
     const uint32_t at = static_cast<uint32_t>(__builtin_amdgcn_readlane(cube_lanes, i & 63)) * (64 * 4);
     if (wave == 0) dma_stats(lrs, at, &stat[slot][0][0], lane);
     if (wave == 1) dma_stats(drs, at, &stat[slot][1][0], lane);

@@ -1,8 +1,9 @@
 // Fine stage of VSA: exact softmax attention of each 64-token query cube over
 // its K selected 64-token key cubes (64x64 blocks).
 //
-// bf16 path (the hot loop), one workgroup = 4 waves = one query cube; wave w
-// owns query slots 16w..16w+15 and keeps its Q fragment in VGPRs.
+// bf16 path (the hot loop), one workgroup = 4 waves = one query cube; each
+// wave owns 16 query slots (a time slice or an h-row of the cube) and keeps
+// their Q fragment in VGPRs; a wave whose slots are all pads computes nothing.
 //   * Gather: q, k, v are read either in cube order (64 rows per cube) or
 //     straight from raster order, where slot (it, ih, iw) of a cube is row
 //     base(cube) + (it*Hh + ih)*Ww + iw, so no reordered copy is needed.
@@ -13,7 +14,8 @@
 //     Each lane's source chunk is chosen so that LDS holds the tiles
 //     XOR-swizzled for the reads below; K runs one key cube ahead of V in a
 //     2-slot ring each (64 KB at D = 128).  Pad slots of a raster edge cube
-//     are redirected to the cube's first row (finite, masked).
+//     read their own raster address (a neighbouring token, or zeros past
+//     the head's rows): finite values, masked to probability 0.
 //   * S^T = K Q^T with v_mfma_f32_16x16x32_bf16: the accumulator then holds,
 //     per lane, 16 scores of ONE query row, which is the B-operand layout of
 //     O^T += V^T P^T, so probabilities go from the softmax straight into the
@@ -84,7 +86,7 @@ struct FineTile {
 
 // Buffer resource over one head of a [rows][D] bf16 tensor.  Reads beyond
 // `bytes` return zeros instead of faulting; a head holds at most
-// 2048 cubes x 64 rows x 256 bytes, so byte offsets fit 32 bits.
+// 4096 cubes x 64 rows x 256 bytes, so byte offsets fit 32 bits.
 static_assert(int64_t(kMaxCubes) * kSlots * 128 * 2 < (int64_t(1) << 32), "32-bit head offsets");
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t head_rsrc(const uint16_t* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(base), 0, static_cast<int>(bytes),
@@ -263,10 +265,12 @@ __global__ __launch_bounds__(256, 2) void fine_fwd_bf16_kernel(
   const __amdgpu_buffer_rsrc_t krs = head_rsrc(k + head0, head_bytes);
   const __amdgpu_buffer_rsrc_t vrs = head_rsrc(v + head0, head_bytes);
 
-  // DMA byte offsets (from the cube's first row) of this thread's chunks;
-  // *alt: the same chunk of the cube's first row, for pad slots of raster
-  // edge cubes
-  uint32_t koff[Tl::kDma], voff[Tl::kDma], kalt[Tl::kDma], valt[Tl::kDma];
+  // DMA byte offsets (from the cube's first row) of this thread's chunks.
+  // A pad slot of a raster edge cube reads its own raster address all the
+  // same: a token of a neighbouring row or frame, or past the head's rows,
+  // where the buffer resource returns zeros.  Either way a finite value
+  // whose probability the masks below make exactly 0.
+  uint32_t koff[Tl::kDma], voff[Tl::kDma];
 #pragma unroll
   for (int u = 0; u < Tl::kDma; ++u) {
     const int P = u * 256 + tid;
@@ -274,28 +278,13 @@ __global__ __launch_bounds__(256, 2) void fine_fwd_bf16_kernel(
     int it, ih, iw;
     dma_slot<D>(u, wave, lane, it, ih, iw);
     const uint32_t rowoff = static_cast<uint32_t>(slot_row<RASTER>(g, it, ih, iw) * D) * 2u;
-    kalt[u] = (c ^ Tl::ksw(r)) * 16;
-    valt[u] = (c ^ Tl::vsw(r)) * 16;
-    koff[u] = rowoff + kalt[u];
-    voff[u] = rowoff + valt[u];
+    koff[u] = rowoff + (c ^ Tl::ksw(r)) * 16;
+    voff[u] = rowoff + (c ^ Tl::vsw(r)) * 16;
   }
-  // stage K or V of a key cube (first row `row`, packed extent `ext`)
-  auto stage = [&](const __amdgpu_buffer_rsrc_t& rs, const uint32_t* off, const uint32_t* alt,
-                   int row, int ext, uint16_t* slot) {
-    const uint32_t row_bytes = static_cast<uint32_t>(row) * (D * 2);
-    if (RASTER && ext != kFullExt) {
-      const int nt = ext & 7, nh = (ext >> 3) & 7, nw = ext >> 6;
-      uint32_t eoff[Tl::kDma];
-#pragma unroll
-      for (int u = 0; u < Tl::kDma; ++u) {
-        int it, ih, iw;
-        dma_slot<D>(u, wave, lane, it, ih, iw);
-        eoff[u] = (it < nt && ih < nh && iw < nw) ? off[u] : alt[u];
-      }
-      dma_tile<D>(rs, row_bytes, eoff, slot, wave);
-    } else {
-      dma_tile<D>(rs, row_bytes, off, slot, wave);
-    }
+  // stage K or V of a key cube (first row `row`)
+  auto stage = [&](const __amdgpu_buffer_rsrc_t& rs, const uint32_t* off, int row,
+                   uint16_t* slot) {
+    dma_tile<D>(rs, static_cast<uint32_t>(row) * (D * 2), off, slot, wave);
   };
 
   // Q fragment: B operand of S^T, lane holds Q[slot 16w+li][32ks + 8lg .. +7]
@@ -339,9 +328,9 @@ __global__ __launch_bounds__(256, 2) void fine_fwd_bf16_kernel(
 
   // prologue: K(0), V(0), K(1) in flight together; S(0) and its row max
   const int ext0 = key_ext(0);
-  stage(krs, koff, kalt, key_row(0), ext0, kring);
-  stage(vrs, voff, valt, key_row(0), ext0, vring);
-  if (K > 1) stage(krs, koff, kalt, key_row(1), key_ext(1), kring + kT);
+  stage(krs, koff, key_row(0), kring);
+  stage(vrs, voff, key_row(0), vring);
+  if (K > 1) stage(krs, koff, key_row(1), kring + kT);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   // the masks follow the key cube's extent and are rebuilt only when it changes
@@ -376,10 +365,10 @@ __global__ __launch_bounds__(256, 2) void fine_fwd_bf16_kernel(
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     const int ext = key_ext(n + 1);
-    stage(vrs, voff, valt, key_row(n + 1), ext, vring + P1 * kT);
+    stage(vrs, voff, key_row(n + 1), vring + P1 * kT);
     if (n + 2 < K) {
       if (((n + 2) & 63) == 0) lane_keys<RASTER>(g, sel, n + 2, K, lane, ext_lanes, row_lanes);
-      stage(krs, koff, kalt, key_row(n + 2), key_ext(n + 2), kring + P0 * kT);
+      stage(krs, koff, key_row(n + 2), kring + P0 * kT);
     }
     if (!active) return;
     if ((ext >> 3) != hw_cur) {

@@ -34,8 +34,14 @@
  *     natural-log log-sum-exp.
  *   - The caller owns every buffer.  The library never allocates or frees
  *     device memory, keeps no pointer after returning and holds no mutable
- *     global state; calls are re-entrant.  Device pointers must point to
- *     memory of the current HIP device.
+ *     global state (vsa_forward_static's device array aside); calls are
+ *     re-entrant.  Device pointers must point to memory of the current HIP
+ *     device.
+ *   - Inputs (q, k, v, o_fine and the upstream gradients) must be finite.  A
+ *     pad slot of an edge cube is staged from its own raster address, which
+ *     holds a token of a neighbouring row or frame (or reads as zero past the
+ *     head's rows); its probability is exactly 0, so a finite value there
+ *     changes nothing, but a NaN or Inf would spread.
  *   - All work is enqueued asynchronously on `stream` (0 = null stream); the
  *     library never synchronises with the host.  Buffers must stay alive
  *     until the stream has executed the work.
@@ -44,7 +50,7 @@
  *     16-byte aligned (VSA_ERR_ALIGN).  Limits: B, H, T, Hh, Ww >= 1;
  *     cube = 4x4x4 (else VSA_ERR_UNSUPPORTED); d in {64, 128}
  *     (else VSA_ERR_UNSUPPORTED); 1 <= topk <= C (else VSA_ERR_SHAPE);
- *     C <= 4096 cubes, B*H <= 65535, B*H*Np*d < 2^58 and
+ *     C <= 4096 cubes, B*H <= 65535, B*H*C <= 2^29, B*H*Np*d < 2^58 and
  *     4*Hh*Ww*d < 2^31 (else VSA_ERR_UNSUPPORTED).
  *   - A kernel launch failure is reported as VSA_ERR_LAUNCH.
  *   - Offsets are 64-bit throughout.
