@@ -64,7 +64,10 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
 }
 
 __device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
-  const int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  // the first conversion fills bytes 0-1 and keeps bytes 2-3 of its third
+  // operand, which the second overwrites: any value serves there (a's bits
+  // cost no register initialisation)
+  const int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, __float_as_int(a), false);
   return static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true));
 }
 
@@ -320,6 +323,13 @@ __global__ __launch_bounds__(256, 2) void fine_fwd_fp8_kernel(
 #pragma unroll
   for (int b = 0; b < 8; ++b) tcur[b] = tcur[b] - mb;
   int vscale = s0.vscale;
+  // exp2 offsets of the 8 key blocks of a step: -mb, or -inf for blocks past
+  // their cube's t extent; rebuilt only when an extent changes, lowered with
+  // the running max
+  int nt_cur[2] = {s0.ext[0] & 7, s0.ext[1] & 7};
+  float moff[8];
+#pragma unroll
+  for (int b = 0; b < 8; ++b) moff[b] = (b & 3) < nt_cur[b >> 2] ? -mb : -INFINITY;
 
   auto step = [&](auto p0c, int n) {
     constexpr int P0 = decltype(p0c)::value, P1 = P0 ^ 1;
@@ -338,11 +348,17 @@ __global__ __launch_bounds__(256, 2) void fine_fwd_fp8_kernel(
       }
     }
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
+    for (int h = 0; h < 2; ++h) {
       if ((sn.ext[h] >> 3) != (ext_cur[h] >> 3)) {
         ext_cur[h] = sn.ext[h];
         bias[h] = hw_bias(sn.ext[h], lg);
       }
+      if ((sn.ext[h] & 7) != nt_cur[h]) {
+        nt_cur[h] = sn.ext[h] & 7;
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) moff[4 * h + kb] = kb < nt_cur[h] ? -mb : -INFINITY;
+      }
+    }
     // S(n+1) on the matrix cores while exp2 of step n runs on the VALU
     f32x4 tnext[8];
     scores(kring + P1 * kPair, kro, qf, bias, tnext);
@@ -350,12 +366,9 @@ __global__ __launch_bounds__(256, 2) void fine_fwd_fp8_kernel(
     pv(vring + P0 * kPair, vro, pf, ones, vscale, oacc, lacc);
     // S(n+1) into exp2 units (relative to the running max), pads to -inf
 #pragma unroll
-    for (int b = 0; b < 8; ++b) {
-      const int h = b >> 2;
-      const float off = (b & 3) < (sn.ext[h] & 7) ? -mb : -INFINITY;
+    for (int b = 0; b < 8; ++b)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) tnext[b][j] = fmaf(tnext[b][j], sn.c2[h], off);
-    }
+      for (int j = 0; j < 4; ++j) tnext[b][j] = fmaf(tnext[b][j], sn.c2[b >> 2], moff[b]);
     if (__ballot(lane_max(tnext) > kTau) != 0ull) {
       const float mt = row_max(tnext);
       const float delta = mt > kTau ? mt : 0.f;
@@ -365,7 +378,10 @@ __global__ __launch_bounds__(256, 2) void fine_fwd_fp8_kernel(
       lacc *= alpha;
       mb += delta;
 #pragma unroll
-      for (int b = 0; b < 8; ++b) tnext[b] = tnext[b] - delta;
+      for (int b = 0; b < 8; ++b) {
+        tnext[b] = tnext[b] - delta;
+        moff[b] -= delta;
+      }
     }
 #pragma unroll
     for (int b = 0; b < 8; ++b) tcur[b] = tnext[b];
