@@ -572,12 +572,14 @@ hipError_t launch_coarse_bwd(const Geo& g, const float* qm, const float* km, con
                              int32_t* order, hipStream_t s) {
   const ListArgs lists = {g.C <= kBitmapCubes ? idx : nullptr, offsets, list, order};
   // 16 cubes per workgroup while two 16 x C fp32 tiles fit the LDS, else 8,
-  // else 4
+  // else 4; small grids take 8 (more workgroups: at 112 cubes and 12 heads
+  // the backward is 1.5 us faster than with 16, the forward's coarse kernel
+  // is not)
   if (g.C > kCoarseBwd8Cubes)
     return g.D == 128
                ? launch_coarse_bwd_typed<128, 4>(g, qm, km, vm, docs, stats, dqc, dkc, dvc, lists, s)
                : launch_coarse_bwd_typed<64, 4>(g, qm, km, vm, docs, stats, dqc, dkc, dvc, lists, s);
-  if (g.C <= kCoarseBwd16Cubes)
+  if (g.C > kCoarseBwdSmallCubes && g.C <= kCoarseBwd16Cubes)
     return g.D == 128
                ? launch_coarse_bwd_typed<128, 16>(g, qm, km, vm, docs, stats, dqc, dkc, dvc, lists, s)
                : launch_coarse_bwd_typed<64, 16>(g, qm, km, vm, docs, stats, dqc, dkc, dvc, lists, s);

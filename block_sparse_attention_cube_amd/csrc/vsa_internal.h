@@ -13,10 +13,11 @@ constexpr int kCube = 4;     // cube edge along each of (t, y, x)
 constexpr int kSlots = 64;   // tokens per cube
 // The coarse stage keeps R x C fp32 score rows in LDS: the forward R = 16
 // query cubes per workgroup up to 2048 cubes, R = 8 above; the backward two
-// such tiles, R = 16 up to 1216 cubes, 8 up to 2048, 4 above.
+// such tiles, R = 8 up to 256 cubes, 16 up to 1216, 8 up to 2048, 4 above.
 constexpr int kMaxCubes = 4096;
 constexpr int kCoarseBwd16Cubes = 1216;
 constexpr int kCoarseBwd8Cubes = 2048;
+constexpr int kCoarseBwdSmallCubes = 256;   // up to here the backward takes 8 as well
 constexpr int kMaxCubesBackward = kMaxCubes;
 
 // Geometry of one problem, passed by value to every kernel.
