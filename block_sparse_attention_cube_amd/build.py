@@ -21,13 +21,20 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libvsa.so")
 
-SOURCES = ["vsa_api.cpp", "reorder.hip", "coarse.hip", "fine_fwd.hip", "fine_bwd.hip",
-           "quant_fp8.hip", "fine_fp8.hip"]
+SOURCES = ["vsa_api.cpp", "reorder.hip", "coarse.hip", "fine_fwd.hip", "dense_fwd.hip",
+           "fine_bwd.hip", "quant_fp8.hip", "fine_fp8.hip"]
 ARCH = "gfx950"
 FLAGS = ["-x", "hip", f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
          "-Wall", "-Wno-unused-function",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          f"-I{INCLUDE}", f"-I{CSRC}"]
+# Per-source extra flags.  The sparse fine forward is scheduled with LLVM's
+# memory-clause strategy: under its 168-VGPR budget (three workgroups per CU)
+# the default strategy feeds every K fragment through one register and waits
+# for each LDS read in turn; measured, the sparse kernel runs about 4% faster
+# this way on the Wan-1.3B shape (the dense kernel, in its own source, 2%
+# slower, so it keeps the default).
+EXTRA_FLAGS = {"fine_fwd.hip": ["-mllvm", "-amdgpu-sched-strategy=max-memory-clause"]}
 
 
 def _hipcc() -> str:
@@ -44,7 +51,7 @@ def _filter(stderr: str) -> str:
 
 def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [_hipcc(), *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [_hipcc(), *FLAGS, *EXTRA_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     msg = _filter(res.stderr)
     if res.returncode != 0:
