@@ -78,7 +78,11 @@ __device__ __forceinline__ void lane_keys(const Geo& g, const int32_t* __restric
 // wave whose row or slice lies past the cube's extent holds only pad slots
 // and computes nothing.  The launcher takes the mapping that idles more
 // waves on the grid at hand.
-template <int D, bool RASTER, bool HROWS>
+// EMPTY_HALVES: the grid's last cube layer is at most two time slices deep
+// (T % 4 in {1, 2}), so its key cubes have an empty second half, whose
+// staging and work are skipped; the launcher sets it from the grid, and
+// without it the step carries no test for the case.
+template <int D, bool RASTER, bool HROWS, bool EMPTY_HALVES>
 __global__ __launch_bounds__(256, 3) void fine_fwd_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const int32_t* __restrict__ idx,
@@ -176,12 +180,16 @@ __global__ __launch_bounds__(256, 3) void fine_fwd_bf16_kernel(
   auto key_ext = [&](int n) { return __builtin_amdgcn_readlane(ext_lanes, n & 63); };
   auto key_row = [&](int n) { return __builtin_amdgcn_readlane(row_lanes, n & 63); };
 
+  // A key cube whose t extent is at most 2 (the last cube layer of a grid
+  // with T % 4 in {1, 2}) has an empty second half: its K and V halves are
+  // not staged and its steps do only the other half's work.
+
   // prologue: both K halves and the first V half of key cube 0 in flight
   // together; S of the first half and its row max
   const int ext0 = key_ext(0), row0 = key_row(0);
   stage(krs, koff, row0, 0, kring);
   stage(vrs, voff, row0, 0, vring);
-  stage(krs, koff, row0, 1, kring + kH);
+  if (!EMPTY_HALVES || (ext0 & 7) > 2) stage(krs, koff, row0, 1, kring + kH);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   // the (ih, iw) mask follows the key cube's extent and is rebuilt only when
@@ -208,44 +216,20 @@ __global__ __launch_bounds__(256, 3) void fine_fwd_bf16_kernel(
   // j runs on the VALU, then PV of half j while S of half j+1 is scaled into
   // exp2 units.  Half j sits in ring slot H of both rings, so every LDS
   // address is a register plus an immediate offset.
-  auto step = [&](auto hc, int n) {
-    constexpr int H = decltype(hc)::value;
-    // the slots of K half j and V half j-1 are free for every wave
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    if (H == 0) {
-      // half j+1 is the second half of cube n; the next K half to stage is
-      // the first of cube n + 1
-      stage(vrs, voff, key_row(n), 1, vring + kH);
-      if (n + 1 < K) {
-        if (((n + 1) & 63) == 0) lane_keys<RASTER>(g, sel, n + 1, K, lane, ext_lanes, row_lanes);
-        stage(krs, koff, key_row(n + 1), 0, kring);
-      }
-    } else {
-      // half j+1 is the first half of cube n + 1 (present: the loop ends
-      // after the first half of the last cube)
-      const int row = key_row(n + 1);
-      stage(vrs, voff, row, 0, vring);
-      stage(krs, koff, row, 1, kring + kH);
-    }
-    if (!active) return;
-    if (H == 1) {
-      const int ext = key_ext(n + 1);
-      if ((ext >> 3) != hw_cur) {
-        hw_cur = ext >> 3;
-        bias = hw_bias(ext, lg);
-      }
-      nt_cur = ext & 7;
-    }
-    // exp2 offsets of the two key blocks of half j+1 (time slices 2(1-H)
-    // and 2(1-H)+1): -mb, or -inf past the cube's t extent
-    const float off0 = (H == 1 || nt_cur > 2) ? -mb : -INFINITY;
-    const float off1 = (H == 1 ? nt_cur > 1 : nt_cur > 3) ? -mb : -INFINITY;
+  // The work of a step: S of half j+1 from K slot ks (DO_S), exp2 and PV of
+  // half j from V slot vs (DO_PV); a step next to an empty half does one of
+  // the two, in code of its own so that the full step keeps its schedule.
+  auto work = [&](auto do_s, auto do_pv, const uint16_t* ks, const uint16_t* vs, float off0,
+                  float off1) {
+    constexpr bool DO_S = decltype(do_s)::value, DO_PV = decltype(do_pv)::value;
     f32x4 tnext[1][2];
-    score_half<D, 1>(kring + (1 - H) * kH, kro, qf, bias, tnext);
-    u32x4 pf[1];
-    probabilities_half<1>(tcur, pf);
-    pv_half<D, 1>(vring + H * kH, vtr, pf, oacc, lacc);
+    if (DO_S) score_half<D, 1>(ks, kro, qf, bias, tnext);
+    if (DO_PV) {
+      u32x4 pf[1];
+      probabilities_half<1>(tcur, pf);
+      pv_half<D, 1>(vs, vtr, pf, oacc, lacc);
+    }
+    if (!DO_S) return;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       tnext[0][0][r] = fmaf(tnext[0][0][r], c2, off0);
@@ -268,15 +252,62 @@ __global__ __launch_bounds__(256, 3) void fine_fwd_bf16_kernel(
     tcur[0][0] = tnext[0][0];
     tcur[0][1] = tnext[0][1];
   };
+  using T = std::true_type;
+  using F = std::false_type;
+  auto step = [&](auto hc, int n) {
+    constexpr int H = decltype(hc)::value;
+    // the slots of K half j and V half j-1 are free for every wave
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    // nt_cur: t extent of cube n (H = 0), of cube n + 1 (H = 1, below)
+    const bool full_n = !EMPTY_HALVES || nt_cur > 2;   // cube n has a second half (H = 0)
+    int ext = 0;
+    if (H == 0) {
+      // half j+1 is the second half of cube n; the next K half to stage is
+      // the first of cube n + 1
+      if (full_n) stage(vrs, voff, key_row(n), 1, vring + kH);
+      if (n + 1 < K) {
+        if (((n + 1) & 63) == 0) lane_keys<RASTER>(g, sel, n + 1, K, lane, ext_lanes, row_lanes);
+        stage(krs, koff, key_row(n + 1), 0, kring);
+      }
+    } else {
+      // half j+1 is the first half of cube n + 1 (present: the loop ends
+      // after the first half of the last cube)
+      const int row = key_row(n + 1);
+      ext = key_ext(n + 1);
+      stage(vrs, voff, row, 0, vring);
+      if (!EMPTY_HALVES || (ext & 7) > 2) stage(krs, koff, row, 1, kring + kH);
+    }
+    if (!active) {
+      if (H == 1) nt_cur = ext & 7;
+      return;
+    }
+    if (H == 0) {
+      // exp2 offsets of the two key blocks of the second half (time slices
+      // 2 and 3): -mb, or -inf past the cube's t extent
+      if (full_n) work(T{}, T{}, kring + kH, vring, -mb, nt_cur > 3 ? -mb : -INFINITY);
+      else work(F{}, T{}, kring + kH, vring, 0.f, 0.f);
+    } else {
+      if ((ext >> 3) != hw_cur) {
+        hw_cur = ext >> 3;
+        bias = hw_bias(ext, lg);
+      }
+      nt_cur = ext & 7;
+      // time slices 0 and 1 of cube n + 1: slice 0 always holds a valid key
+      const float off1 = nt_cur > 1 ? -mb : -INFINITY;
+      if (full_n) work(T{}, T{}, kring, vring + kH, -mb, off1);
+      else work(T{}, F{}, kring, vring + kH, -mb, off1);
+    }
+  };
   for (int n = 0;; ++n) {
     step(std::integral_constant<int, 0>{}, n);
     if (n + 1 >= K) break;
     step(std::integral_constant<int, 1>{}, n);
   }
-  // the second V half of the last cube has landed
+  // the second V half of the last cube has landed (if it has one)
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
-  if (active) {
+  if (active && (!EMPTY_HALVES || nt_cur > 2)) {
     u32x4 pf[1];
     probabilities_half<1>(tcur, pf);
     pv_half<D, 1>(vring + kH, vtr, pf, oacc, lacc);
@@ -466,8 +497,11 @@ hipError_t launch_typed(const Geo& g, int dtype, const void* q, const void* k, c
     // cube layer (4 - nt per cube) or h-rows past Hh in the last cube row
     const int64_t t_idle = int64_t(4 * g.Ct - g.T) * g.Ch * g.Cw;
     const int64_t h_idle = int64_t(4 * g.Ch - g.Hh) * g.Ct * g.Cw;
-    auto kern = h_idle > t_idle ? fine_fwd_bf16_kernel<D, RASTER, true>
-                                : fine_fwd_bf16_kernel<D, RASTER, false>;
+    const bool hrows = h_idle > t_idle, empty_halves = g.T % 4 == 1 || g.T % 4 == 2;
+    auto kern = hrows ? (empty_halves ? fine_fwd_bf16_kernel<D, RASTER, true, true>
+                                      : fine_fwd_bf16_kernel<D, RASTER, true, false>)
+                      : (empty_halves ? fine_fwd_bf16_kernel<D, RASTER, false, true>
+                                      : fine_fwd_bf16_kernel<D, RASTER, false, false>);
     return launch_kernel(kern, grid, block, 0, s,
                          static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                          static_cast<const uint16_t*>(v), idx, static_cast<uint16_t*>(o), lse,
