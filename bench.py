@@ -123,12 +123,6 @@ def settle_clock(fn, rotate, seconds=1.0):
             return round((time.perf_counter() - t0) * 1e3, 1)
 
 
-def t_extents(w):
-    """Valid time slices (1..4) of every cube of a workload's grid, cube order."""
-    ct, ch, cw = -(-w.T // 4), -(-w.Hh // 4), -(-w.Ww // 4)
-    return [min(4, w.T - 4 * t) for t in range(ct) for _ in range(ch) for _ in range(cw)]
-
-
 def valid_counts(w):
     """Valid slots n_c of every cube of a workload's grid, cube order."""
     ct, ch, cw = -(-w.T // 4), -(-w.Hh // 4), -(-w.Ww // 4)
@@ -197,7 +191,7 @@ def per_config(args, dev):
                "fine_useful_tflops": round(useful / (fine_ms * 1e-3) / 1e12, 2),
                "useful_over_computed": round(useful / fl, 4),
                "executed_over_computed": round(
-                   flops.executed_fine_flops(w.B, w.H, w.topk, w.d, t_extents(w)) / fl, 4)
+                   flops.executed_fine_flops(grid, w.d, idx.cpu().numpy()) / fl, 4)
                if w.dtype == "bf16" else 1.0,
                "timing": "hip graph replay"}
         del cube, obuf, plan      # the cube-order copies are not needed below

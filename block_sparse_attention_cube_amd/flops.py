@@ -45,14 +45,35 @@ def useful_fine_flops(B: int, H: int, d: int, n_valid: Sequence[int], idx) -> in
     return int(4 * d * (per_row * n[None, None, :]).sum())
 
 
-def executed_fine_flops(B: int, H: int, K: int, d: int, t_extent: Sequence[int]) -> int:
-    """FLOPs the bf16 fine kernel executes: each query cube's four 16-row
-    waves hold time slices 0..3, and a wave whose slice lies past the cube's
-    t extent (t_extent[c], 1..4) computes nothing, so a cube costs
-    min(t_extent, 4) / 4 of its 64x64-block FLOPs."""
+def query_wave_rows(T: int, Hh: int, Ww: int) -> str:
+    """Which 16-slot rows the bf16 fine kernel's four query waves hold on a
+    token grid: "h" (h-rows) where that idles more waves over the cube grid
+    than time slices do ("t"), as its launcher decides."""
+    ct, ch, cw = -(-T // 4), -(-Hh // 4), -(-Ww // 4)
+    t_idle = (4 * ct - T) * ch * cw
+    h_idle = (4 * ch - Hh) * ct * cw
+    return "h" if h_idle > t_idle else "t"
+
+
+def executed_fine_flops(grid: Sequence[int], d: int, idx) -> int:
+    """FLOPs the bf16 fine kernel executes on a token grid (T, Hh, Ww) with
+    block lists idx [B, H, C, K]: 4 * 64 * 64 * d per (query cube, selected
+    cube) pair, scaled by
+      * the query cube's active waves / 4: a wave whose 16 query slots (a
+        time slice, or an h-row, see query_wave_rows) lie past the cube's
+        extent computes nothing;
+      * 1/2 for a selected cube at most two time slices deep: its empty
+        second half is neither staged nor computed."""
     import numpy as np
-    nt = np.minimum(np.asarray(t_extent, dtype=np.int64), 4)
-    return int(4 * d * BLOCK * BLOCK * B * H * K * nt.sum() // 4)
+    T, Hh, Ww = grid
+    ct, ch, cw = -(-T // 4), -(-Hh // 4), -(-Ww // 4)
+    nt = np.array([min(4, T - 4 * t) for t in range(ct) for _ in range(ch) for _ in range(cw)])
+    nh = np.array([min(4, Hh - 4 * h) for _ in range(ct) for h in range(ch) for _ in range(cw)])
+    waves = nh if query_wave_rows(T, Hh, Ww) == "h" else nt           # active waves per query cube
+    halves = np.where(nt <= 2, 1, 2)                                    # key halves per key cube
+    sel = np.asarray(idx, dtype=np.int64)
+    per_query = halves[sel].sum(axis=-1)                                # [B, H, C]
+    return int(BLOCK * BLOCK * d * (per_query * waves[None, None, :]).sum() // 2)
 
 
 def reorder_bytes(B: int, H: int, N: int, Np: int, d: int, elem: int, tensors: int = 3) -> int:

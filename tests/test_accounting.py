@@ -96,20 +96,67 @@ def test_sample_plan_covers_the_corner_cube():
     assert 0 in qcubes and configs.WAN_14B.C - 1 in qcubes
 
 
-def test_executed_flops_skip_query_waves_past_the_t_extent():
-    # Wan-1.3B: T = 16, every cube four time slices deep -> all block FLOPs run
-    w = configs.WAN_1_3B
-    nt = [min(4, w.T - 4 * t) for t in range(-(-w.T // 4)) for _ in range(w.C // (-(-w.T // 4)))]
-    assert flops.executed_fine_flops(1, 12, 14, 128, nt) == flops.fine_forward_flops(1, 12, 112, 14, 128)
-    # Wan-14B: T = 21, the last of 6 cube layers holds one time slice -> 1 of 4 waves
-    w = configs.WAN_14B
-    layers = -(-w.T // 4)
-    per_layer = w.C // layers
-    nt = [min(4, w.T - 4 * t) for t in range(layers) for _ in range(per_layer)]
-    assert nt.count(1) == 240
-    got = flops.executed_fine_flops(1, 40, 144, 128, nt)
-    full = flops.fine_forward_flops(1, 40, 1440, 144, 128)
-    assert got * 8 == full * 7          # (1200 + 240/4) / 1440 = 7/8
-    # brute force over cubes and waves
-    brute = sum(4 * 128 * 16 * 64 * 144 * 40 for c in range(w.C) for wave in range(4) if wave < nt[c])
-    assert got == brute
+def _brute_executed(grid, d, idx):
+    """Executed FLOPs by enumeration: every query wave (16 slots: a time
+    slice or an h-row) with a valid slot, times every selected key half
+    (32 keys: time slices 0-1 or 2-3) with a valid slot, 2 x 16 x 32 x d
+    FLOPs each for S and PV."""
+    T, Hh, Ww = grid
+    ct, ch, cw = -(-T // 4), -(-Hh // 4), -(-Ww // 4)
+    cubes = [(t, h, x) for t in range(ct) for h in range(ch) for x in range(cw)]
+    rows = flops.query_wave_rows(T, Hh, Ww)
+    total = 0
+    B, H, C, K = idx.shape
+    for b in range(B):
+        for hd in range(H):
+            for i, (t, h, x) in enumerate(cubes):
+                if rows == "t":
+                    waves = sum(1 for w in range(4) if 4 * t + w < T)
+                else:
+                    waves = sum(1 for w in range(4) if 4 * h + w < Hh)
+                for k in range(K):
+                    tj = cubes[idx[b, hd, i, k]][0]
+                    halves = sum(1 for half in range(2) if 4 * tj + 2 * half < T)
+                    total += waves * halves * 2 * (2 * 16 * 32 * d)
+    return total
+
+
+def test_wave_rows_follow_the_idle_count():
+    # Wan-1.3B: T = 16 leaves no idle time slice, Hh = 14 idles half of the
+    # last cube row -> h-rows; Wan-14B: 3 idle time slices per cube column in
+    # the last layer (720) against 3 idle h-rows in the last cube row (360)
+    assert flops.query_wave_rows(16, 14, 26) == "h"
+    assert flops.query_wave_rows(21, 45, 80) == "t"
+    assert flops.query_wave_rows(16, 16, 16) == "t"
+
+
+@pytest.mark.parametrize("grid", [(16, 14, 26), (21, 45, 80), (5, 6, 7), (6, 5, 9), (9, 3, 10)])
+def test_executed_flops_match_enumeration(grid):
+    rng = np.random.default_rng(sum(grid))
+    T, Hh, Ww = grid
+    C = -(-T // 4) * -(-Hh // 4) * -(-Ww // 4)
+    K = min(C, 5)
+    idx = np.stack([rng.permutation(C)[:K] for _ in range(2 * C)]).reshape(1, 2, C, K)
+    if C > 200:   # enumeration on a subset of query cubes keeps the test fast
+        pick = rng.choice(C, 40, replace=False)
+        sub = np.zeros_like(idx)
+        sub[..., pick, :] = idx[..., pick, :]
+        idx = sub
+    assert flops.executed_fine_flops(grid, 64, idx) == _brute_executed(grid, 64, idx)
+
+
+def test_executed_flops_closed_forms():
+    # Wan-1.3B: every cube is four time slices deep (no empty key half); the
+    # last of 4 cube rows holds 2 h-rows, so 28 of 112 query cubes run 2 waves
+    idx = np.zeros((1, 12, 112, 14), dtype=np.int64)
+    got = flops.executed_fine_flops((16, 14, 26), 128, idx)
+    assert got * 8 == flops.fine_forward_flops(1, 12, 112, 14, 128) * 7      # (84 + 14) / 112
+    # Wan-14B: the last of 6 cube layers (240 of 1440 cubes) is one slice
+    # deep: those query cubes run 1 of 4 waves, and as selected cubes they
+    # run 1 of 2 halves.  With every selection in the first layer:
+    idx = np.zeros((1, 1, 1440, 144), dtype=np.int64)
+    full = flops.fine_forward_flops(1, 1, 1440, 144, 128)
+    assert flops.executed_fine_flops((21, 45, 80), 128, idx) * 8 == full * 7  # (1200 + 60) / 1440
+    # ... and every selection in the last layer: half of that
+    idx[:] = 1439
+    assert flops.executed_fine_flops((21, 45, 80), 128, idx) * 16 == full * 7
