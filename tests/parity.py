@@ -16,6 +16,10 @@ import numpy as np
 
 TOL = {"bf16": (3e-2, 3e-3), "f32": (1e-4, 1e-4)}
 
+# Largest errors measured in this session per (quantity, dtype): the test
+# session prints them at its end next to the tolerances.
+WORST: dict = {}
+
 
 def assert_close(gpu: np.ndarray, ref: np.ndarray, dtype: str, what: str, rows=None):
     """gpu/ref: (..., rows, d); rows: optional boolean mask over the row axis."""
@@ -31,6 +35,9 @@ def assert_close(gpu: np.ndarray, ref: np.ndarray, dtype: str, what: str, rows=N
         raise AssertionError(f"{what}: GPU output has non-finite values")
     mx, mean = float(err.max()) if err.size else 0.0, float(err.mean()) if err.size else 0.0
     tmax, tmean = TOL[dtype]
+    key = (what, dtype)
+    prev = WORST.get(key, (0.0, 0.0, 0))
+    WORST[key] = (max(prev[0], mx), max(prev[1], mean), prev[2] + 1)
     assert mx <= tmax and mean <= tmean, (
         f"{what}: max|err|={mx:.3e} (tol {tmax:g}), mean|err|={mean:.3e} (tol {tmean:g})")
     return mx, mean
