@@ -180,12 +180,12 @@ __global__ __launch_bounds__(256, 3) void fine_fwd_bf16_kernel(
   auto key_ext = [&](int n) { return __builtin_amdgcn_readlane(ext_lanes, n & 63); };
   auto key_row = [&](int n) { return __builtin_amdgcn_readlane(row_lanes, n & 63); };
 
-  // A key cube whose t extent is at most 2 (the last cube layer of a grid
-  // with T % 4 in {1, 2}) has an empty second half: its K and V halves are
-  // not staged and its steps do only the other half's work.
+  // With EMPTY_HALVES, a key cube whose t extent is at most 2 (the last
+  // cube layer) has an empty second half: its K and V halves are not staged
+  // and the steps next to it do only the other half's work.
 
-  // prologue: both K halves and the first V half of key cube 0 in flight
-  // together; S of the first half and its row max
+  // prologue: both K halves (the second unless empty) and the first V half
+  // of key cube 0 in flight together; S of the first half and its row max
   const int ext0 = key_ext(0), row0 = key_row(0);
   stage(krs, koff, row0, 0, kring);
   stage(vrs, voff, row0, 0, vring);
@@ -211,11 +211,6 @@ __global__ __launch_bounds__(256, 3) void fine_fwd_bf16_kernel(
   tcur[0][0] = tcur[0][0] - mb;
   tcur[0][1] = tcur[0][1] - mb;
 
-  // One step per half key cube, j = 2n + H: the K half j+1 and the V half j
-  // have landed.  S of half j+1 runs on the matrix cores while exp2 of half
-  // j runs on the VALU, then PV of half j while S of half j+1 is scaled into
-  // exp2 units.  Half j sits in ring slot H of both rings, so every LDS
-  // address is a register plus an immediate offset.
   // The work of a step: S of half j+1 from K slot ks (DO_S), exp2 and PV of
   // half j from V slot vs (DO_PV); a step next to an empty half does one of
   // the two, in code of its own so that the full step keeps its schedule.
@@ -254,6 +249,11 @@ __global__ __launch_bounds__(256, 3) void fine_fwd_bf16_kernel(
   };
   using T = std::true_type;
   using F = std::false_type;
+  // One step per half key cube, j = 2n + H: the K half j+1 and the V half j
+  // have landed.  S of half j+1 runs on the matrix cores while exp2 of half
+  // j runs on the VALU, then PV of half j while S of half j+1 is scaled into
+  // exp2 units.  Half j sits in ring slot H of both rings, so every LDS
+  // address is a register plus an immediate offset.
   auto step = [&](auto hc, int n) {
     constexpr int H = decltype(hc)::value;
     // the slots of K half j and V half j-1 are free for every wave
