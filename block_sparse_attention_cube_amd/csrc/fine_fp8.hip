@@ -4,8 +4,9 @@
 // library's own; the pages only note that sparse and low-bit attention stack
 // (TurboDiffusion write-up, section "主要技术").
 //
-// One workgroup = 4 waves = one query cube, wave w owns query slots
-// 16w..16w+15.  A step covers TWO selected key cubes (128 keys), the
+// One workgroup = 4 waves = one query cube, wave w owns the 16 query
+// slots of a time slice (or, where that idles more waves, an h-row) of the
+// cube, and a wave whose slots are all pads computes nothing.  A step covers TWO selected key cubes (128 keys), the
 // contraction length of gfx950's v_mfma_f32_16x16x128_f8f6f4:
 //   * S^T = K Q^T: one MFMA per 16 keys (d = 128 in a single instruction).
 //     Lane (li, lg) then holds, for query li, keys 16(b%4) + 4lg + j of
@@ -217,7 +218,11 @@ __device__ __forceinline__ void pv(const uint8_t* v_lds, int vro, const i32x8& p
 }
 
 // RASTER: o (and o_coarse) are raster [B,H,N,D]; otherwise o is cube order.
-template <bool RASTER>
+// HROWS: wave w owns the 16 query slots of the cube's h-row ih = w instead
+// of its time slice it = w; a wave whose row or slice lies past the cube's
+// extent holds only pad slots and computes nothing (the launcher takes the
+// mapping that idles more waves, as for the bf16 kernel).
+template <bool RASTER, bool HROWS>
 __global__ __launch_bounds__(256, 2) void fine_fwd_fp8_kernel(
     const uint8_t* __restrict__ q8, const uint8_t* __restrict__ k8,
     const uint8_t* __restrict__ vt8, const int32_t* __restrict__ exps,
@@ -271,10 +276,17 @@ __global__ __launch_bounds__(256, 2) void fine_fwd_fp8_kernel(
     dma_cube(rs, (cubes >> 16) * static_cast<uint32_t>(kTile), off, slot + kTile, wave);
   };
 
-  // Q fragment (B operand of S^T): Q8[slot 16w + li][32lg .. 32lg + 31]
+  // wave w holds time slice w (or h-row w) of the query cube: past the
+  // cube's extent its 16 slots are all pads and it computes nothing (it
+  // still stages its share of the tiles and meets every barrier).  Lane li
+  // serves query slot qslot.
+  const CubeExt eq = cube_extent(g, qc);
+  const bool active = wave < (HROWS ? eq.nh : eq.nt);
+  const int qslot = HROWS ? 16 * (li >> 2) + 4 * wave + (li & 3) : 16 * wave + li;
+  // Q fragment (B operand of S^T): Q8[qslot][32lg .. 32lg + 31]
   i32x8 qf;
   {
-    const uint8_t* qrow = q8 + head0 + (static_cast<int64_t>(qc) * 64 + wave * 16 + li) * kD + 32 * lg;
+    const uint8_t* qrow = q8 + head0 + (static_cast<int64_t>(qc) * 64 + qslot) * kD + 32 * lg;
     const u32x4 lo = *reinterpret_cast<const u32x4*>(qrow);
     const u32x4 hi = *reinterpret_cast<const u32x4*>(qrow + 16);
     qf = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
@@ -347,6 +359,7 @@ __global__ __launch_bounds__(256, 2) void fine_fwd_fp8_kernel(
         stage(krs, koff, rl(tab_c, n + 2), kring + P0 * kPair);
       }
     }
+    if (!active) return;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       if ((sn.ext[h] >> 3) != (ext_cur[h] >> 3)) {
@@ -395,27 +408,29 @@ __global__ __launch_bounds__(256, 2) void fine_fwd_fp8_kernel(
   {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    const i32x8 pf = probabilities(tcur);
-    if ((ns - 1) & 1) pv(vring + kPair, vro, pf, ones, vscale, oacc, lacc);
-    else pv(vring, vro, pf, ones, vscale, oacc, lacc);
+    if (active) {
+      const i32x8 pf = probabilities(tcur);
+      if ((ns - 1) & 1) pv(vring + kPair, vro, pf, ones, vscale, oacc, lacc);
+      else pv(vring, vro, pf, ones, vscale, oacc, lacc);
+    }
   }
   __syncthreads();   // every wave is done with the rings: reuse them for O
 
+  // a wave past the cube's extent writes zeros (pad rows)
   const float l = lacc[0];   // every row of lacc holds the row sum
-  const float inv = 1.f / l;
+  const float inv = active ? 1.f / l : 0.f;
   if (lse != nullptr && lg == 0)
-    lse[bh * g.Np + static_cast<int64_t>(qc) * 64 + wave * 16 + li] = (mb + log2f(l)) * kLn2;
+    lse[bh * g.Np + static_cast<int64_t>(qc) * 64 + qslot] = active ? (mb + log2f(l)) * kLn2 : 0.f;
 
   uint16_t* const o_lds = reinterpret_cast<uint16_t*>(smem);  // [64][kOS]
 #pragma unroll
   for (int e = 0; e < kD / 16; ++e) {
-    // lane holds O[q = 16w + li][d = 16e + 4lg + j], j = 0..3
+    // lane holds O[q = qslot][d = 16e + 4lg + j], j = 0..3
     const u32x2 w = {pack_bf16x2(oacc[e][0] * inv, oacc[e][1] * inv),
                      pack_bf16x2(oacc[e][2] * inv, oacc[e][3] * inv)};
-    *reinterpret_cast<u32x2*>(o_lds + (wave * 16 + li) * kOS + 16 * e + 4 * lg) = w;
+    *reinterpret_cast<u32x2*>(o_lds + qslot * kOS + 16 * e + 4 * lg) = w;
   }
   __syncthreads();
-  const CubeExt eq = cube_extent(g, qc);
 #pragma unroll
   for (int u = 0; u < kOutReg; ++u) {
     const int ch = tid + 256 * u, row = ch / kKC, c = ch % kKC;
@@ -442,12 +457,15 @@ hipError_t launch_fine_fp8(const Geo& g, const void* q8, const void* k8, const v
   if (g.D != kD) return hipErrorInvalidValue;
   const dim3 grid(g.B * g.H * g.C), block(256);
   auto u8 = [](const void* p) { return static_cast<const uint8_t*>(p); };
-  if (raster_out)
-    return launch_kernel(fine_fwd_fp8_kernel<true>, grid, block, 0, s, u8(q8), u8(k8), u8(vt8),
-                         exps, idx, static_cast<uint16_t*>(o), lse,
-                         static_cast<const uint16_t*>(oc), static_cast<uint16_t*>(o_coarse), g);
-  return launch_kernel(fine_fwd_fp8_kernel<false>, grid, block, 0, s, u8(q8), u8(k8), u8(vt8), exps,
-                       idx, static_cast<uint16_t*>(o), lse, static_cast<const uint16_t*>(oc),
+  // idle query waves over the cube grid: time slices past T in the last
+  // cube layer or h-rows past Hh in the last cube row
+  const int64_t t_idle = int64_t(4 * g.Ct - g.T) * g.Ch * g.Cw;
+  const int64_t h_idle = int64_t(4 * g.Ch - g.Hh) * g.Ct * g.Cw;
+  const bool hrows = h_idle > t_idle;
+  auto kern = raster_out ? (hrows ? fine_fwd_fp8_kernel<true, true> : fine_fwd_fp8_kernel<true, false>)
+                         : (hrows ? fine_fwd_fp8_kernel<false, true> : fine_fwd_fp8_kernel<false, false>);
+  return launch_kernel(kern, grid, block, 0, s, u8(q8), u8(k8), u8(vt8), exps, idx,
+                       static_cast<uint16_t*>(o), lse, static_cast<const uint16_t*>(oc),
                        static_cast<uint16_t*>(o_coarse), g);
 }
 
