@@ -375,14 +375,14 @@ __global__ __launch_bounds__(256) void idx_transpose_kernel(const int32_t* __res
 
 // ---------------------------------------------------------------------------
 // dQ: one workgroup per query cube, 4 waves x 16 query slots (wave w owns
-// row ih = w of the cube, as the forward).
+// h-row ih = w or time slice it = w of the cube, as the forward: HROWS).
 // Per selected key cube the K and V tiles go from cube order straight into
 // a 2-slot LDS ring by DMA; K^T comes from transposed reads of the K tile.
 // Pad key slots get P = 0 as in the forward: a -inf accumulator init for the
 // (ih, iw) part, a -inf exp2 offset for key tiles past the cube's t extent,
 // extents read per step from a per-lane table.
 // tile = bh * C + query cube; smem: 4 K/V tiles, [2 slots][K | V].
-template <int D, bool RASTER>
+template <int D, bool RASTER, bool HROWS>
 __device__ __forceinline__ void dq_tile(const BwdFineArgs& a, const Geo& g, int tile,
                                         uint16_t* smem) {
   using Tl = BwdTile<D>;
@@ -396,12 +396,13 @@ __device__ __forceinline__ void dq_tile(const BwdFineArgs& a, const Geo& g, int 
   const int K = g.K;
   const int32_t* __restrict__ sel = a.idx + static_cast<int64_t>(tile) * K;
   const float c2 = inv_sqrt_d<D>() * kLog2e;
-  // wave w owns the 16 query slots of row ih = w of the cube: slot
-  // qslot = 16 (li / 4) + 4 w + li % 4; a wave whose row lies past the grid
-  // has no valid query and only stages tiles and meets barriers
+  // wave w owns the 16 query slots of h-row ih = w of the cube (slot
+  // qslot = 16 (li / 4) + 4 w + li % 4) or of time slice it = w (slot
+  // 16 w + li); a wave whose row or slice lies past the grid has no valid
+  // query and only stages tiles and meets barriers
   const CubeExt eq = cube_extent(g, qc);
-  const int qslot = 16 * (li >> 2) + 4 * wave + (li & 3);
-  const bool active = wave < eq.nh;   // wave-uniform
+  const int qslot = HROWS ? 16 * (li >> 2) + 4 * wave + (li & 3) : 16 * wave + li;
+  const bool active = wave < (HROWS ? eq.nh : eq.nt);   // wave-uniform
   const int64_t qrow = bh * g.Np + static_cast<int64_t>(qc) * 64 + qslot;   // cube-order stats
   const int64_t head0 = bh * (RASTER ? g.N : g.Np) * D;   // q, k, v, dO rows of this head
 
@@ -430,7 +431,7 @@ __device__ __forceinline__ void dq_tile(const BwdFineArgs& a, const Geo& g, int 
 
   u32x4 qf[kKS], df[kKS];
   {
-    const int it = li >> 2, ih = wave, iw = li & 3;
+    const int it = qslot >> 4, ih = (qslot >> 2) & 3, iw = qslot & 3;
     const bool valid = it < eq.nt && ih < eq.nh && iw < eq.nw;   // pad rows: P = 0 via lse2
     const int64_t row = cube_row<RASTER>(g, eq, qc) + (valid ? slot_row<RASTER>(g, it, ih, iw) : 0);
 #pragma unroll
@@ -564,14 +565,16 @@ __device__ __forceinline__ void dq_tile(const BwdFineArgs& a, const Geo& g, int 
 }
 
 // ---------------------------------------------------------------------------
-// dK/dV: one workgroup per key cube, wave w owns keys 16w..16w+15 and loops
+// dK/dV: one workgroup per key cube, wave w owns the 16 keys of h-row
+// ih = w (HROWS) or of time slice it = w; a wave whose keys are all pads
+// only stages tiles and meets barriers.  The workgroup loops
 // over the query cubes that selected this key cube.  Per query cube the Q
 // and dO tiles and its 64 lse2 / delta values go straight into a 2-slot LDS
 // ring by DMA; Q^T and dO^T come from transposed reads.  Pad query slots
 // have lse2 = +inf (P = 0) and zero dO rows, so they add nothing.
 // tile = bh * C + rank of the key cube in the head's order (descending
 // selection counts); smem: [2 slots][Q | dO]; stat: [slot][lse2 | delta][q].
-template <int D, bool RASTER>
+template <int D, bool RASTER, bool HROWS>
 __device__ __forceinline__ void dkdv_tile(const BwdFineArgs& a, const Geo& g, int tile,
                                           uint16_t* smem, float (*stat)[2][64]) {
   using Tl = BwdTile<D>;
@@ -611,11 +614,15 @@ __device__ __forceinline__ void dkdv_tile(const BwdFineArgs& a, const Geo& g, in
 #pragma unroll
   for (int dt = 0; dt < kDT; ++dt) tro[dt] = tr_offset<D>(li, lg, dt);
 
-  // B operands of S = Q K^T and dP = dO V^T: lane holds (key = 16w + li, dims 32ks + 8lg ..)
+  // the wave's 16 keys: local key j is slot kslot(j)
+  auto kslot = [&](int j) { return HROWS ? 16 * (j >> 2) + 4 * wave + (j & 3) : 16 * wave + j; };
+  const CubeExt ek = cube_extent(g, kc);
+  const bool active = wave < (HROWS ? ek.nh : ek.nt);   // wave-uniform
+  // B operands of S = Q K^T and dP = dO V^T: lane holds (key kslot(li), dims 32ks + 8lg ..)
   u32x4 kf[kKS], vf[kKS];
   {
-    const CubeExt ek = cube_extent(g, kc);
-    const int it = wave, ih = li >> 2, iw = li & 3;
+    const int ks_ = kslot(li);
+    const int it = ks_ >> 4, ih = (ks_ >> 2) & 3, iw = ks_ & 3;
     const bool valid = it < ek.nt && ih < ek.nh && iw < ek.nw;   // pad key rows are not written
     const int64_t row = cube_row<RASTER>(g, ek, kc) + (valid ? slot_row<RASTER>(g, it, ih, iw) : 0);
 #pragma unroll
@@ -673,6 +680,7 @@ __device__ __forceinline__ void dkdv_tile(const BwdFineArgs& a, const Geo& g, in
       if (((i + 1) & 63) == 0) cubes(i + 1);
       stage(i + 1, slot ^ 1);
     }
+    if (!active) return;   // staging only
     const uint16_t* q_t = smem + slot * 2 * kT;
     const uint16_t* o_t = q_t + kT;
 
@@ -742,8 +750,8 @@ __device__ __forceinline__ void dkdv_tile(const BwdFineArgs& a, const Geo& g, in
   }
   __syncthreads();   // every wave is done with the ring
 
-  // epilogue: lane holds (key = 16w + 4lg + r, d = 16dt + li)
-  const CubeExt ek = cube_extent(g, kc);
+  // epilogue: lane holds (key kslot(4lg + r), d = 16dt + li); the rows of a
+  // skipped wave are pad slots, never written out
   const float inv_n = 1.f / static_cast<float>(ek.nt * ek.nh * ek.nw);
   const float* ck = a.dkc == nullptr ? nullptr : a.dkc + (bh * g.C + kc) * D;
   const float* cv = a.dvc == nullptr ? nullptr : a.dvc + (bh * g.C + kc) * D;
@@ -756,7 +764,7 @@ __device__ __forceinline__ void dkdv_tile(const BwdFineArgs& a, const Geo& g, in
     const float addv = cv ? cv[d] * inv_n : 0.f;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int key = wave * 16 + 4 * lg + r;
+      const int key = kslot(4 * lg + r);
       const float xk = dkacc[dt][r] * inv_sqrt_d<D>() + addk;
       const float xv = dvacc[dt][r] + addv;
       stage_k[key * kOS + d] = f32_to_bf16_rne(xk);
@@ -773,16 +781,16 @@ __device__ __forceinline__ void dkdv_tile(const BwdFineArgs& a, const Geo& g, in
 // dQ tiles take the slots that the short lists of a head leave free while its
 // long lists still run, and both kinds of tile of a head share one XCD's L2
 // (every head's q, k, v and dO rows are read by both).
-template <int D, bool RASTER>
+template <int D, bool RASTER, bool HROWS>
 __global__ __launch_bounds__(256, 2) void fine_bwd_kernel(BwdFineArgs a, Geo g) {
   __shared__ __attribute__((aligned(16))) uint16_t smem[4 * BwdTile<D>::kElems];
   __shared__ __attribute__((aligned(16))) float stat[2][2][64];
   const int t = xcd_remap(blockIdx.x, gridDim.x);
   const int bh = t / (2 * g.C), r = t - bh * (2 * g.C);
   if (r < g.C)
-    dkdv_tile<D, RASTER>(a, g, bh * g.C + r, smem, stat);
+    dkdv_tile<D, RASTER, HROWS>(a, g, bh * g.C + r, smem, stat);
   else
-    dq_tile<D, RASTER>(a, g, bh * g.C + (r - g.C), smem);
+    dq_tile<D, RASTER, HROWS>(a, g, bh * g.C + (r - g.C), smem);
 }
 
 }  // namespace
@@ -804,8 +812,15 @@ hipError_t launch_prep_layout(const Geo& g, const BwdPrepArgs& a, hipStream_t s)
 template <bool RASTER>
 hipError_t launch_fine_layout(const Geo& g, const BwdFineArgs& a, hipStream_t s) {
   const dim3 grid(2 * g.B * g.H * g.C), block(256);
-  return g.D == 128 ? launch_kernel(fine_bwd_kernel<128, RASTER>, grid, block, 0, s, a, g)
-                    : launch_kernel(fine_bwd_kernel<64, RASTER>, grid, block, 0, s, a, g);
+  // the waves' 16-slot rows: h-rows where they idle more waves over the cube
+  // grid than time slices do (edge cubes in h against edge cubes in t)
+  const int64_t t_idle = int64_t(4 * g.Ct - g.T) * g.Ch * g.Cw;
+  const int64_t h_idle = int64_t(4 * g.Ch - g.Hh) * g.Ct * g.Cw;
+  if (h_idle > t_idle)
+    return g.D == 128 ? launch_kernel(fine_bwd_kernel<128, RASTER, true>, grid, block, 0, s, a, g)
+                      : launch_kernel(fine_bwd_kernel<64, RASTER, true>, grid, block, 0, s, a, g);
+  return g.D == 128 ? launch_kernel(fine_bwd_kernel<128, RASTER, false>, grid, block, 0, s, a, g)
+                    : launch_kernel(fine_bwd_kernel<64, RASTER, false>, grid, block, 0, s, a, g);
 }
 }  // namespace
 
