@@ -812,11 +812,7 @@ hipError_t launch_prep_layout(const Geo& g, const BwdPrepArgs& a, hipStream_t s)
 template <bool RASTER>
 hipError_t launch_fine_layout(const Geo& g, const BwdFineArgs& a, hipStream_t s) {
   const dim3 grid(2 * g.B * g.H * g.C), block(256);
-  // the waves' 16-slot rows: h-rows where they idle more waves over the cube
-  // grid than time slices do (edge cubes in h against edge cubes in t)
-  const int64_t t_idle = int64_t(4 * g.Ct - g.T) * g.Ch * g.Cw;
-  const int64_t h_idle = int64_t(4 * g.Ch - g.Hh) * g.Ct * g.Cw;
-  if (h_idle > t_idle)
+  if (waves_hold_h_rows(g))
     return g.D == 128 ? launch_kernel(fine_bwd_kernel<128, RASTER, true>, grid, block, 0, s, a, g)
                       : launch_kernel(fine_bwd_kernel<64, RASTER, true>, grid, block, 0, s, a, g);
   return g.D == 128 ? launch_kernel(fine_bwd_kernel<128, RASTER, false>, grid, block, 0, s, a, g)

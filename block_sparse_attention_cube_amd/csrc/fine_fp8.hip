@@ -457,11 +457,7 @@ hipError_t launch_fine_fp8(const Geo& g, const void* q8, const void* k8, const v
   if (g.D != kD) return hipErrorInvalidValue;
   const dim3 grid(g.B * g.H * g.C), block(256);
   auto u8 = [](const void* p) { return static_cast<const uint8_t*>(p); };
-  // idle query waves over the cube grid: time slices past T in the last
-  // cube layer or h-rows past Hh in the last cube row
-  const int64_t t_idle = int64_t(4 * g.Ct - g.T) * g.Ch * g.Cw;
-  const int64_t h_idle = int64_t(4 * g.Ch - g.Hh) * g.Ct * g.Cw;
-  const bool hrows = h_idle > t_idle;
+  const bool hrows = waves_hold_h_rows(g);
   auto kern = raster_out ? (hrows ? fine_fwd_fp8_kernel<true, true> : fine_fwd_fp8_kernel<true, false>)
                          : (hrows ? fine_fwd_fp8_kernel<false, true> : fine_fwd_fp8_kernel<false, false>);
   return launch_kernel(kern, grid, block, 0, s, u8(q8), u8(k8), u8(vt8), exps, idx,

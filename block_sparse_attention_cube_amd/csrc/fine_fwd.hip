@@ -493,11 +493,7 @@ hipError_t launch_typed(const Geo& g, int dtype, const void* q, const void* k, c
                         void* o_coarse, hipStream_t s) {
   const dim3 grid(g.B * g.H * g.C), block(256);
   if (dtype == 1) {
-    // idle query waves over the cube grid: time slices past T in the last
-    // cube layer (4 - nt per cube) or h-rows past Hh in the last cube row
-    const int64_t t_idle = int64_t(4 * g.Ct - g.T) * g.Ch * g.Cw;
-    const int64_t h_idle = int64_t(4 * g.Ch - g.Hh) * g.Ct * g.Cw;
-    const bool hrows = h_idle > t_idle, empty_halves = g.T % 4 == 1 || g.T % 4 == 2;
+    const bool hrows = waves_hold_h_rows(g), empty_halves = g.T % 4 == 1 || g.T % 4 == 2;
     auto kern = hrows ? (empty_halves ? fine_fwd_bf16_kernel<D, RASTER, true, true>
                                       : fine_fwd_bf16_kernel<D, RASTER, true, false>)
                       : (empty_halves ? fine_fwd_bf16_kernel<D, RASTER, false, true>

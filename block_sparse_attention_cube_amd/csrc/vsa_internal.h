@@ -83,6 +83,18 @@ __device__ inline uint16_t f32_to_bf16_rne(float f) {
   return static_cast<uint16_t>(u >> 16);
 }
 
+// The rows of a query (or key) cube that the attention kernels give their
+// four 16-slot waves: h-rows (slots 16 it + 4 w + iw) when they leave more
+// waves idle over the cube grid than time slices (slots 16 w + ..) do, so
+// that more waves hold only pad slots and skip their work; time slices
+// otherwise.  Idle waves: 4 Ct - T time slices per cube column of the last
+// cube layer, 4 Ch - Hh h-rows per cube of the last cube row.
+inline bool waves_hold_h_rows(const Geo& g) {
+  const int64_t t_idle = int64_t(4 * g.Ct - g.T) * g.Ch * g.Cw;
+  const int64_t h_idle = int64_t(4 * g.Ch - g.Hh) * g.Ct * g.Cw;
+  return h_idle > t_idle;
+}
+
 // Workgroups are dealt to the 8 XCDs round-robin (hardware id w runs on XCD
 // w % 8).  Remap so that each XCD receives one contiguous range of logical
 // tiles: tiles of one head then share that XCD's L2.
