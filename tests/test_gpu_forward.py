@@ -44,6 +44,11 @@ EDGE = [
     # and the top-K 64 keys per lane
     Workload("cubes2304-ragged", B=1, H=1, T=4, Hh=190, Ww=189, d=64, dtype="bf16", topk=3,
              structure="offset", alpha=0.5),
+    # one-frame last cube layer (its key cubes' empty second halves skipped)
+    # with more than 64 selected cubes per query cube (the per-lane key
+    # table reloads mid-walk)
+    Workload("t13-k70", B=1, H=1, T=13, Hh=16, Ww=24, d=64, dtype="bf16", topk=70,
+             structure="field", alpha=0.5),
 ]
 SMALL = [configs.TINY_F32, configs.DIT_410M, configs.WAN_1_3B]
 CASES = SMALL + EDGE
