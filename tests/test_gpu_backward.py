@@ -41,6 +41,11 @@ EDGE = [
     # 2304 cubes: the coarse backward takes 4 cubes per workgroup
     Workload("bwd-2304-cubes", B=1, H=1, T=4, Hh=190, Ww=189, d=64, dtype="bf16", topk=2,
              structure="offset", alpha=0.5, backward=True),
+    # top-K above 64: the dQ tiles reload their per-lane key table mid-walk and
+    # dK/dV block lists run past 64 entries; one-frame last cube layer (its
+    # waves hold time slices, three of four idle on that layer)
+    Workload("bwd-t13-k70", B=1, H=1, T=13, Hh=16, Ww=24, d=64, dtype="bf16", topk=70,
+             structure="field", alpha=0.5, backward=True),
 ]
 CASES = list(configs.SWEEP) + EDGE
 ids = [w.name for w in CASES]
